@@ -1,0 +1,303 @@
+"""Benchmark of the FSDP2 mixed-dtype hot path on one MI355X.
+
+One step = the fused reduce-scatter pack of every bucket + the all-gather
+copy-in of rank 0 + the all-gather copy-out of the gathered buffer, on the
+chosen workload (default: the 50.3M-element mixed bf16/fp32 transformer
+layout, W=8, the layout of the pages' isolated packing test).  Inputs are
+seeded synthetic tensors already resident in HBM; R independent buffer sets
+are rotated so that no step finds its data in the 256 MB last-level cache.
+
+Prints ONE JSON line (rank 0):
+  value        whole-step algorithmic bytes / step time  (GB/s)
+  ms_per_step  wall time per step over the K timed steps
+  roofline     the pack kernel: algorithmic bytes per launch / mean launch
+               time vs 8 TB/s HBM peak.  Launch times come from HIP events
+               that the kernel dispatch itself stamps at the kernel's start
+               and end (hipExtLaunchKernelGGL on the launch stream);
+               traffic from the committed rocprofv3 counter summary when it
+               was taken on the current kernel source, else null
+  cpu_baseline the CPU oracle's pack, single thread, on a bounded sample
+plus per-kernel times, the pre-cast-then-pack comparator and a plain-copy
+ceiling measured in the same run.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ms per fused mixed-dtype pack + achieved HBM GB/s (% of MI355X peak)"
+HBM_PEAK_GBPS = 8000.0
+PAGES_H100_FUSED_MS = 0.1888      # isolated H100 test, 50.3M-element layout (context only)
+PAGES_H100_PRECAST_MS = 0.3582
+KERNEL_SOURCE = os.path.join(ROOT, "fsdp2_mixed_dtype_amd", "csrc", "fsdppack_kernels.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "pack_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mixed50m")
+    ap.add_argument("--rotate-bytes", type=float, default=2.0, help="GiB of buffers rotated across steps")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="bound on the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pack-only", action="store_true",
+                    help="run only pack launches (for counter collection under rocprofv3)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run plain 256 MiB device copies (known size) to calibrate byte counters")
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only (W is a layout parameter, no collectives); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fsdp2_mixed_dtype_amd as fp
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = wl.get(args.workload)
+    W = w.world
+    t_plan = time.perf_counter()
+    plan = fp.plan_buckets(w.descs(), W)
+    plan_us = (time.perf_counter() - t_plan) * 1e6
+
+    # ---- algorithmic bytes (read + write) per launch
+    def esz(dt):
+        return fp.ELEM_SIZE[dt]
+    pack_bytes = []
+    for b in plan.buckets:
+        rd = sum(plan.numel[i] * esz(w.tensors[i].grad_dtype) for i in b.members)
+        pack_bytes.append(rd + W * b.S * esz(b.dtype))
+    copy_in_bytes = sum(P * (esz(t.storage_dtype) + esz(t.param_dtype)) for P, t in zip(plan.P, w.tensors))
+    copy_out_bytes = sum(2 * t.numel * esz(t.param_dtype) for t in w.tensors)
+    step_bytes = sum(pack_bytes) + copy_in_bytes + copy_out_bytes
+
+    # ---- inputs: seeded host draws, uploaded once per rotation set
+    grads_h = wl.make_grads(w)
+
+    def to_dev(a, dt):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        if dt == fp.BF16:
+            t = t.view(torch.bfloat16)
+        return t.to(dev)
+
+    set_bytes = step_bytes
+    R = max(2, math.ceil(args.rotate_bytes * 2**30 / set_bytes))
+    sets = []
+    for r in range(R):
+        g = [to_dev(a, t.grad_dtype) for a, t in zip(grads_h, w.tensors)]
+        outs = [torch.empty(W * b.S, dtype=fp.TORCH_DTYPE[b.dtype], device=dev) for b in plan.buckets]
+        shards = [torch.randn(P, device=dev).to(fp.TORCH_DTYPE[t.storage_dtype]) for P, t in zip(plan.P, w.tensors)]
+        ag = torch.randint(0, 255, (W * plan.B,), dtype=torch.uint8, device=dev)
+        params = [torch.empty(t.numel, dtype=fp.TORCH_DTYPE[t.param_dtype], device=dev) for t in w.tensors]
+        sets.append((g, outs, shards, ag, params))
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    nb = len(plan.buckets)
+
+    def timed(pair):
+        # the library stamps these events at the kernel's own start and end
+        if pair is not None:
+            fp.time_next_launch(*pair)
+
+    def step(s, ev=None):
+        g, outs, shards, ag, params = s
+        for bi in range(nb):
+            timed(None if ev is None else ev[bi])
+            fp.pack_reduce_scatter_input(plan, bi, g, outs[bi], stream)
+        if args.pack_only:
+            return
+        timed(None if ev is None else ev[nb])
+        fp.all_gather_copy_in(plan, 0, shards, ag, stream)
+        timed(None if ev is None else ev[nb + 1])
+        fp.all_gather_copy_out(plan, ag, params, stream)
+
+    def new_event():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)          # creates the underlying HIP event
+        return e
+
+    for i in range(args.warmup):
+        step(sets[i % R])
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[(new_event(), new_event()) for _ in range(nb + 2)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(sets[i % R], evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / K
+
+    def mean_ms(j):
+        return sum(e[j][0].elapsed_time(e[j][1]) for e in evs) / K
+
+    pack_ms = [mean_ms(bi) for bi in range(nb)]
+    copy_in_ms = None if args.pack_only else mean_ms(nb)
+    copy_out_ms = None if args.pack_only else mean_ms(nb + 1)
+    pack_total_ms = sum(pack_ms)
+    pack_gbps = sum(pack_bytes) / (pack_total_ms * 1e-3) / 1e9
+    step_gbps = (sum(pack_bytes) if args.pack_only else step_bytes) / (ms_per_step * 1e-3) / 1e9
+
+    extra = {}
+    if not args.pack_only:
+        # ---- pre-cast then homogeneous pack (the pages' comparator), our kernels, 2 launches
+        bf_idx = [i for i, t in enumerate(w.tensors) if t.grad_dtype == fp.BF16]
+        if bf_idx and nb == 1 and plan.buckets[0].dtype == fp.FP32:
+            cast_plan = fp.plan_buckets([(w.tensors[i].numel, 1, fp.BF16, fp.FP32, fp.FP32, fp.FP32)
+                                         for i in bf_idx], 1)
+            homo = fp.plan_buckets([(t.dim0, t.inner, fp.FP32, fp.FP32, fp.FP32, fp.FP32) for t in w.tensors], W)
+            temp_elems = cast_plan.buckets[0].S
+            cast_offsets = cast_plan.buckets[0].O
+            csets = []
+            for r in range(R):
+                tmp = torch.empty(temp_elems, dtype=torch.float32, device=dev)
+                views = list(sets[r][0])
+                for k, i in enumerate(bf_idx):
+                    views[i] = tmp[cast_offsets[k]: cast_offsets[k] + w.tensors[i].numel]
+                csets.append((tmp, views, sets[r][1][0]))
+            e_c = [(new_event(), new_event(), new_event(), new_event()) for _ in range(K)]
+            for i in range(args.warmup + K):
+                tmp, views, out = csets[i % R]
+                e = e_c[i - args.warmup] if i >= args.warmup else None
+                timed(None if e is None else e[0:2])
+                fp.pack_reduce_scatter_input(cast_plan, 0, [sets[i % R][0][j] for j in bf_idx], tmp, stream)
+                timed(None if e is None else e[2:4])
+                fp.pack_reduce_scatter_input(homo, 0, views, out, stream)
+            torch.cuda.synchronize()
+            precast_ms = sum(a.elapsed_time(b) + c.elapsed_time(d) for a, b, c, d in e_c) / K
+            extra.update(precast_then_pack_ms=round(precast_ms, 5), precast_vs_fused=round(precast_ms / pack_total_ms, 3),
+                         precast_temporaries_MiB=round(temp_elems * 4 / 2**20, 2))
+            cast_plan.destroy()
+            homo.destroy()
+
+        # ---- plain-copy ceiling: device-to-device copy moving the pack's byte count
+        nbytes = sum(pack_bytes) // 2
+        src = [torch.empty(nbytes // 4, dtype=torch.float32, device=dev) for _ in range(R)]
+        dst = [torch.empty_like(x) for x in src]
+        for i in range(args.warmup):
+            dst[i % R].copy_(src[i % R])
+        c0, c1 = new_event(), new_event()
+        torch.cuda.synchronize()
+        c0.record(stream)
+        for i in range(K):
+            dst[i % R].copy_(src[i % R])
+        c1.record(stream)
+        torch.cuda.synchronize()
+        copy_ms = c0.elapsed_time(c1) / K      # back-to-back copies, events around the batch
+        extra["copy_ceiling_GBps"] = round(2 * (nbytes // 4) * 4 / (copy_ms * 1e-3) / 1e9, 1)
+        del src, dst
+
+    if args.calib_copy:
+        # plain device-to-device copies of a known size: what a byte counter
+        # reads for them calibrates the counter against real traffic
+        n = 256 * 2**20 // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        extra["calib_copy_bytes_each_way"] = n * 4
+        del a, b
+
+    # ---- roofline of the dominant kernel (the pack of the largest bucket)
+    dom = max(range(nb), key=lambda i: pack_bytes[i])
+    achieved = pack_bytes[dom] / (pack_ms[dom] * 1e-3) / 1e9
+    traffic = None
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            summ = json.load(f)
+        if summ.get("kernel_source_sha256_16") == kernel_source_hash() and summ.get("workload") == args.workload:
+            traffic = summ.get("traffic_bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "kernel": "segments_kernel (pack)", "bytes_per_launch": pack_bytes[dom]}
+
+    # ---- CPU baseline: the oracle, as it stands, on a bounded sample of the same pack
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        ref = oracle.plan(w.descs(), W)
+        reps, t_cpu = 0, 0.0
+        t_start = time.perf_counter()
+        while reps == 0 or (time.perf_counter() - t_start) < args.cpu_seconds:
+            ta = time.perf_counter()
+            for bi in range(nb):
+                oracle.pack(ref, bi, grads_h)
+            t_cpu += time.perf_counter() - ta
+            reps += 1
+        cpu_gbps = reps * sum(pack_bytes) / t_cpu / 1e9
+        cpu = {"value": round(cpu_gbps, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"oracle pack of every bucket of {args.workload}, full size, repeated {reps}x "
+                         f"({t_cpu:.1f} s, single thread); GB/s under the same byte model",
+               "ms_per_pack": round(t_cpu / reps * 1e3, 2)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(step_gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16,fp32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "world": W, "tensors": len(w.tensors),
+                   "elements": sum(t.numel for t in w.tensors), "buckets": nb,
+                   "step": "pack(all buckets)" + ("" if args.pack_only else " + copy_in(rank 0) + copy_out"),
+                   "rotated_sets": R},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "pack_ms": round(pack_total_ms, 5),
+        "pack_GBps": round(pack_gbps, 1),
+        "pack_frac_of_peak": round(pack_gbps / HBM_PEAK_GBPS, 4),
+        "pack_bytes": sum(pack_bytes),
+        "copy_in_ms": None if copy_in_ms is None else round(copy_in_ms, 5),
+        "copy_in_GBps": None if copy_in_ms is None else round(copy_in_bytes / (copy_in_ms * 1e-3) / 1e9, 1),
+        "copy_out_ms": None if copy_out_ms is None else round(copy_out_ms, 5),
+        "copy_out_GBps": None if copy_out_ms is None else round(copy_out_bytes / (copy_out_ms * 1e-3) / 1e9, 1),
+        "step_bytes": step_bytes,
+        "plan_us": round(plan_us, 1),
+        "pages_h100_fused_pack_ms": PAGES_H100_FUSED_MS if args.workload == "mixed50m" else None,
+        "pages_h100_precast_ms": PAGES_H100_PRECAST_MS if args.workload == "mixed50m" else None,
+        "kernel_source_sha256_16": kernel_source_hash(),
+    }
+    out.update(extra)
+    print(json.dumps(out), flush=True)
+    plan.destroy()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,233 @@
+"""Python binding of libfsdppack: FSDP2's mixed-dtype gradient pack for
+reduce-scatter and its all-gather copy-in / copy-out on MI355X (gfx950).
+
+This module only marshals arguments (torch tensors -> device pointers, the
+current HIP stream) and calls the C ABI declared in ``include/fsdppack.h``;
+every step of the work runs in the library's HIP kernels.  There is no CPU
+fallback: if ``libfsdppack.so`` is missing, loading fails loudly.
+
+Functions (same names as the C ABI without the ``fsdppack_`` prefix):
+  plan_buckets(params, world)                  -> Plan
+  pack_reduce_scatter_input(plan, bucket, grads, out, stream=None)
+  all_gather_copy_in(plan, rank, shards, ag_out, stream=None)
+  all_gather_copy_out(plan, ag, params, stream=None)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch  # device memory and streams; loaded first so libfsdppack binds to torch's HIP runtime
+
+BF16 = 1
+FP32 = 2
+DTYPE_NONE = 0
+TORCH_DTYPE = {BF16: torch.bfloat16, FP32: torch.float32}
+ELEM_SIZE = {BF16: 2, FP32: 4}
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfsdppack.so")
+
+STATUS = {0: "OK", -1: "EINVAL", -2: "EDTYPE", -3: "ENOMEM", -4: "EHIP", -5: "ESTATE"}
+
+
+class FsdpPackError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{STATUS.get(code, code)}: {message}")
+        self.code = code
+
+
+class ParamDesc(ctypes.Structure):
+    _fields_ = [("dim0", ctypes.c_int64), ("inner", ctypes.c_int64),
+                ("grad_dtype", ctypes.c_int32), ("reduce_dtype", ctypes.c_int32),
+                ("storage_dtype", ctypes.c_int32), ("param_dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libfsdppack (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run fsdp2_mixed_dtype_amd.build.build() "
+                              "(hipcc --offload-arch=gfx950) first")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        P_i32, P_i64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+        PP_i32, PP_i64 = ctypes.POINTER(P_i32), ctypes.POINTER(P_i64)
+        L.fsdppack_plan_buckets.argtypes = [ctypes.POINTER(ParamDesc), i32, i32, ctypes.POINTER(vp)]
+        L.fsdppack_plan_info.argtypes = [vp, P_i32, P_i32, P_i32]
+        L.fsdppack_plan_bucket.argtypes = [vp, i32, P_i32, P_i64, P_i32, PP_i32, PP_i64, PP_i64]
+        L.fsdppack_plan_all_gather_layout.argtypes = [vp, P_i64, PP_i64, PP_i64]
+        L.fsdppack_pack_reduce_scatter_input.argtypes = [vp, i32, vp, vp, vp]
+        L.fsdppack_all_gather_copy_in.argtypes = [vp, i32, vp, vp, vp]
+        L.fsdppack_all_gather_copy_out.argtypes = [vp, vp, vp, vp]
+        L.fsdppack_plan_destroy.argtypes = [vp]
+        L.fsdppack_plan_destroy.restype = None
+        L.fsdppack_last_error.argtypes = []
+        L.fsdppack_last_error.restype = ctypes.c_char_p
+        L.fsdppack_counters.argtypes = [P_i64, i32]
+        L.fsdppack_time_next_launch.argtypes = [vp, vp]
+        for f in (L.fsdppack_plan_buckets, L.fsdppack_plan_info, L.fsdppack_plan_bucket,
+                  L.fsdppack_plan_all_gather_layout, L.fsdppack_pack_reduce_scatter_input,
+                  L.fsdppack_all_gather_copy_in, L.fsdppack_all_gather_copy_out, L.fsdppack_counters,
+                  L.fsdppack_time_next_launch):
+            f.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise FsdpPackError(rc, lib().fsdppack_last_error().decode())
+
+
+@dataclass(frozen=True)
+class Bucket:
+    dtype: int          # effective reduction dtype
+    S: int              # row length of the [W, S] reduce-scatter input
+    members: tuple      # parameter indices (unit order)
+    P: tuple            # padded rank-chunk size of each member
+    O: tuple            # column offset of each member
+
+
+class Plan:
+    """A planned fully_shard unit (owns the library handle)."""
+
+    def __init__(self, handle: int, descs):
+        self._h = ctypes.c_void_p(handle)
+        self.descs = tuple(descs)
+        L = lib()
+        nb, n, w = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(L.fsdppack_plan_info(self._h, ctypes.byref(nb), ctypes.byref(n), ctypes.byref(w)))
+        self.world, self.n = w.value, n.value
+        buckets = []
+        for b in range(nb.value):
+            dt, S, m = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int32()
+            mem = ctypes.POINTER(ctypes.c_int32)()
+            P, O = ctypes.POINTER(ctypes.c_int64)(), ctypes.POINTER(ctypes.c_int64)()
+            _check(L.fsdppack_plan_bucket(self._h, b, ctypes.byref(dt), ctypes.byref(S), ctypes.byref(m),
+                                          ctypes.byref(mem), ctypes.byref(P), ctypes.byref(O)))
+            k = m.value
+            buckets.append(Bucket(dt.value, S.value, tuple(mem[i] for i in range(k)),
+                                  tuple(P[i] for i in range(k)), tuple(O[i] for i in range(k))))
+        self.buckets = tuple(buckets)
+        B = ctypes.c_int64()
+        P, A = ctypes.POINTER(ctypes.c_int64)(), ctypes.POINTER(ctypes.c_int64)()
+        _check(L.fsdppack_plan_all_gather_layout(self._h, ctypes.byref(B), ctypes.byref(P), ctypes.byref(A)))
+        self.B = B.value
+        self.P = tuple(P[i] for i in range(self.n))
+        self.A = tuple(A[i] for i in range(self.n))
+        self.numel = tuple(d.dim0 * d.inner for d in self.descs)
+
+    @property
+    def handle(self):
+        if not self._h:
+            raise FsdpPackError(-5, "plan already destroyed")
+        return self._h
+
+    def destroy(self):
+        if self._h:
+            lib().fsdppack_plan_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def plan_buckets(params, world: int) -> Plan:
+    """Plan one unit.  params: sequence of (dim0, inner, grad_dtype,
+    reduce_dtype, storage_dtype, param_dtype) tuples (or ParamDesc)."""
+    descs = [p if isinstance(p, ParamDesc) else ParamDesc(*[int(x) for x in p]) for p in params]
+    arr = (ParamDesc * max(1, len(descs)))(*descs)
+    h = ctypes.c_void_p()
+    _check(lib().fsdppack_plan_buckets(arr, len(descs), int(world), ctypes.byref(h)))
+    return Plan(h.value, descs)
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t, dtype: int | None, numel: int | None, what: str):
+    if t is None:
+        return 0
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what}: tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: tensor must be contiguous")
+    if dtype is not None and t.dtype != TORCH_DTYPE[dtype]:
+        raise TypeError(f"{what}: expected {TORCH_DTYPE[dtype]}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{what}: expected {numel} elements, got {t.numel()}")
+    return t.data_ptr()
+
+
+def _ptr_array(ptrs):
+    return (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
+
+
+def pack_reduce_scatter_input(plan: Plan, bucket: int, grads, out, stream=None):
+    """Fill `out` ([W, S] of the bucket's reduction dtype) with every member's
+    gradient chunked along dim 0, cast and zero-padded.  `grads` is indexed by
+    parameter (unit order); entries of non-members may be None."""
+    b = plan.buckets[bucket]
+    members = set(b.members)
+    ptrs = [_ptr(g, plan.descs[i].grad_dtype, plan.numel[i], f"grads[{i}]") if i in members else 0
+            for i, g in enumerate(grads)]
+    if len(ptrs) != plan.n:
+        raise ValueError(f"grads: expected {plan.n} entries, got {len(ptrs)}")
+    optr = _ptr(out, b.dtype, plan.world * b.S, "out")
+    _check(lib().fsdppack_pack_reduce_scatter_input(plan.handle, bucket, _ptr_array(ptrs), optr, _stream(stream)))
+    return out
+
+
+def _bytes_ptr(t, nbytes: int, what: str):
+    p = _ptr(t, None, None, what)
+    if t.numel() * t.element_size() != nbytes:
+        raise ValueError(f"{what}: expected {nbytes} bytes, got {t.numel() * t.element_size()}")
+    return p
+
+
+def all_gather_copy_in(plan: Plan, rank: int, shards, ag_out, stream=None):
+    """Write row `rank` of the [W, B]-byte all-gather buffer from the rank's
+    padded shards (P elements each, storage dtype)."""
+    if len(shards) != plan.n:
+        raise ValueError(f"shards: expected {plan.n} entries, got {len(shards)}")
+    ptrs = [_ptr(s, plan.descs[i].storage_dtype, plan.P[i], f"shards[{i}]") for i, s in enumerate(shards)]
+    aptr = _bytes_ptr(ag_out, plan.world * plan.B, "ag_out")
+    _check(lib().fsdppack_all_gather_copy_in(plan.handle, int(rank), _ptr_array(ptrs), aptr, _stream(stream)))
+    return ag_out
+
+
+def all_gather_copy_out(plan: Plan, ag, params, stream=None):
+    """Rebuild every full parameter (param dtype) from the gathered buffer."""
+    if len(params) != plan.n:
+        raise ValueError(f"params: expected {plan.n} entries, got {len(params)}")
+    ptrs = [_ptr(p, plan.descs[i].param_dtype, plan.numel[i], f"params[{i}]") for i, p in enumerate(params)]
+    aptr = _bytes_ptr(ag, plan.world * plan.B, "ag")
+    _check(lib().fsdppack_all_gather_copy_out(plan.handle, aptr, _ptr_array(ptrs), _stream(stream)))
+    return params
+
+
+def time_next_launch(start, stop):
+    """Have the next compute call on this thread stamp two timing events
+    (torch.cuda.Event(enable_timing=True), already recorded once so that they
+    exist) at its kernel's start and end."""
+    _check(lib().fsdppack_time_next_launch(start.cuda_event, stop.cuda_event))
+
+
+def counters():
+    """(kernel launches, pointer-table uploads, pointer-table reuses, plan uploads)."""
+    c = (ctypes.c_int64 * 4)()
+    _check(lib().fsdppack_counters(c, 4))
+    return tuple(c)

@@ -1,0 +1,367 @@
+// fsdppack_abi.cpp -- the C ABI of libfsdppack (declared in include/fsdppack.h).
+//
+// Argument checks are synchronous and on the host; every compute call then
+// enqueues one launch of the grouped segment kernel on the caller's stream.
+// Per-call device pointers (grads, shards, params) reach the kernel through a
+// small device table cached by content (see PtrCache in fsdppack_plan.h), so
+// a training loop that passes the same buffers each step pays no upload.
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "fsdppack_plan.h"
+
+using namespace fsdppack;
+
+namespace {
+
+thread_local std::string g_error;
+thread_local void *g_next_start = nullptr;   // events for the next launch on this thread
+thread_local void *g_next_stop = nullptr;
+std::atomic<int64_t> g_counters[4];   // launches, table uploads, table reuses, plan uploads
+
+int fail(int code, const std::string &msg)
+{
+    g_error = msg;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char *what)
+{
+    return fail(FSDPPACK_EHIP, std::string(what) + ": " + hipGetErrorName(e) + " (" + hipGetErrorString(e) + ")");
+}
+
+bool trace_on()
+{
+    static const bool on = [] {
+        const char *v = std::getenv("FSDPPACK_TRACE");
+        return v != nullptr && v[0] != '\0' && v[0] != '0';
+    }();
+    return on;
+}
+
+int64_t default_item_bytes()
+{
+    const char *v = std::getenv("FSDPPACK_ITEM_BYTES");
+    if (v != nullptr) {
+        const long long x = std::atoll(v);
+        if (x >= 256 && x % 16 == 0) return x;
+    }
+    return kItemBytes;
+}
+
+bool plan_ok(const fsdppack_plan *p) { return p != nullptr && p->magic == kPlanMagic; }
+
+bool aligned(const void *p, int64_t bytes) { return (reinterpret_cast<uintptr_t>(p) % bytes) == 0; }
+
+int upload_list(WorkList &wl)
+{
+    const size_t sb = wl.segs.size() * sizeof(Seg), ib = wl.items.size() * sizeof(Item);
+    hipError_t e;
+    if (sb) {
+        if ((e = hipMalloc(reinterpret_cast<void **>(&wl.d_segs), sb)) != hipSuccess) return hip_fail(e, "hipMalloc(segments)");
+        if ((e = hipMemcpy(wl.d_segs, wl.segs.data(), sb, hipMemcpyHostToDevice)) != hipSuccess) return hip_fail(e, "hipMemcpy(segments)");
+    }
+    if ((e = hipMalloc(reinterpret_cast<void **>(&wl.d_items), ib)) != hipSuccess) return hip_fail(e, "hipMalloc(items)");
+    if ((e = hipMemcpy(wl.d_items, wl.items.data(), ib, hipMemcpyHostToDevice)) != hipSuccess) return hip_fail(e, "hipMemcpy(items)");
+    return FSDPPACK_OK;
+}
+
+// Upload the plan's work lists once, on the current device; afterwards the
+// plan is bound to that device.  Caller holds plan->mu.
+int ensure_device(fsdppack_plan *p)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (p->uploaded) {
+        if (dev != p->device)
+            return fail(FSDPPACK_ESTATE, "plan was prepared on device " + std::to_string(p->device) +
+                                             " but the current device is " + std::to_string(dev));
+        return FSDPPACK_OK;
+    }
+    for (BucketPlan &b : p->buckets)
+        if (int rc = upload_list(b.pack)) return rc;
+    if (int rc = upload_list(p->copy_in)) return rc;
+    if (int rc = upload_list(p->copy_out)) return rc;
+    p->caches.resize(p->buckets.size() + 2);
+    p->device = dev;
+    p->uploaded = true;
+    g_counters[3]++;
+    return FSDPPACK_OK;
+}
+
+// Find or stage the device pointer table for `key` in cache `c`, ordered
+// before work enqueued next on `stream`.  Caller holds plan->mu.
+int acquire_table(PtrCache &c, const std::vector<uint64_t> &key, hipStream_t stream, PtrSlot **out)
+{
+    hipError_t e;
+    for (PtrSlot &s : c.slots) {
+        if (s.live && s.key == key) {
+            if (s.stream != stream) {
+                // another stream used this table last: order after that use
+                if ((e = hipStreamWaitEvent(stream, static_cast<hipEvent_t>(s.used), 0)) != hipSuccess)
+                    return hip_fail(e, "hipStreamWaitEvent");
+                s.stream = stream;
+            }
+            s.last_use = ++c.clock;
+            g_counters[2]++;
+            *out = &s;
+            return FSDPPACK_OK;
+        }
+    }
+    PtrSlot *victim = nullptr;
+    for (PtrSlot &s : c.slots)
+        if (!s.live) { victim = &s; break; }
+    if (victim == nullptr) {
+        victim = &c.slots[0];
+        for (PtrSlot &s : c.slots)
+            if (s.last_use < victim->last_use) victim = &s;
+        // the kernels that read this table (and its upload) must be done
+        if ((e = hipEventSynchronize(static_cast<hipEvent_t>(victim->used))) != hipSuccess)
+            return hip_fail(e, "hipEventSynchronize");
+    }
+    const size_t bytes = key.size() * sizeof(uint64_t);
+    if (victim->d_table == nullptr) {
+        if ((e = hipMalloc(reinterpret_cast<void **>(&victim->d_table), bytes)) != hipSuccess) return hip_fail(e, "hipMalloc(pointer table)");
+        if ((e = hipHostMalloc(reinterpret_cast<void **>(&victim->h_stage), bytes, hipHostMallocDefault)) != hipSuccess) return hip_fail(e, "hipHostMalloc(pointer table)");
+        hipEvent_t ev;
+        if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+        victim->ready = ev;
+        if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+        victim->used = ev;
+    }
+    std::memcpy(victim->h_stage, key.data(), bytes);
+    if ((e = hipMemcpyAsync(victim->d_table, victim->h_stage, bytes, hipMemcpyHostToDevice, stream)) != hipSuccess)
+        return hip_fail(e, "hipMemcpyAsync(pointer table)");
+    if ((e = hipEventRecord(static_cast<hipEvent_t>(victim->ready), stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    victim->key = key;
+    victim->stream = stream;
+    victim->live = true;
+    victim->last_use = ++c.clock;
+    g_counters[1]++;
+    *out = victim;
+    return FSDPPACK_OK;
+}
+
+// Run one work list: table lookup, one kernel launch, mark the table used.
+int run_list(fsdppack_plan *p, WorkList &wl, size_t cache_index, const std::vector<uint64_t> &key, char *base,
+             void *stream, const char *what)
+{
+    if (wl.n_items() <= 0) return FSDPPACK_OK;
+    std::lock_guard<std::mutex> lock(p->mu);
+    if (int rc = ensure_device(p)) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    PtrSlot *slot = nullptr;
+    if (int rc = acquire_table(p->caches[cache_index], key, s, &slot)) return rc;
+    LaunchArgs args{};
+    args.segs = wl.d_segs;
+    args.items = wl.d_items;
+    args.table = slot->d_table;
+    args.base = base;
+    args.n_items = wl.n_items();
+    void *ev0 = g_next_start, *ev1 = g_next_stop;
+    g_next_start = g_next_stop = nullptr;
+    const int le = launch_segments(args, stream, ev0, ev1);
+    if (le != 0) return hip_fail(static_cast<hipError_t>(le), what);
+    hipError_t e = hipEventRecord(static_cast<hipEvent_t>(slot->used), s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    g_counters[0]++;
+    if (trace_on())
+        std::fprintf(stderr, "fsdppack: %s: %d workgroups, %lld bytes read, %lld bytes written\n", what,
+                     args.n_items, static_cast<long long>(wl.src_bytes), static_cast<long long>(wl.dst_bytes));
+    return FSDPPACK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fsdppack_plan_buckets(const fsdppack_param_desc *params, int32_t n, int32_t world,
+                          fsdppack_plan **out_plan)
+{
+    if (out_plan == nullptr) return fail(FSDPPACK_EINVAL, "plan_buckets: out_plan is NULL");
+    *out_plan = nullptr;
+    fsdppack_plan *p = new (std::nothrow) fsdppack_plan();
+    if (p == nullptr) return fail(FSDPPACK_ENOMEM, "plan_buckets: out of host memory");
+    std::string err;
+    int rc;
+    try {
+        rc = build_plan(params, n, world, default_item_bytes(), p, err);
+    } catch (const std::bad_alloc &) {
+        rc = FSDPPACK_ENOMEM;
+        err = "plan_buckets: out of host memory";
+    }
+    if (rc != FSDPPACK_OK) {
+        delete p;
+        return fail(rc, err);
+    }
+    *out_plan = p;
+    return FSDPPACK_OK;
+}
+
+int fsdppack_plan_info(const fsdppack_plan *plan, int32_t *num_buckets, int32_t *num_params, int32_t *world)
+{
+    if (!plan_ok(plan)) return fail(FSDPPACK_ESTATE, "plan_info: invalid plan handle");
+    if (num_buckets) *num_buckets = static_cast<int32_t>(plan->buckets.size());
+    if (num_params) *num_params = plan->n;
+    if (world) *world = plan->W;
+    return FSDPPACK_OK;
+}
+
+int fsdppack_plan_bucket(const fsdppack_plan *plan, int32_t bucket, int32_t *reduce_dtype, int64_t *S,
+                         int32_t *nmembers, const int32_t **members, const int64_t **P, const int64_t **O)
+{
+    if (!plan_ok(plan)) return fail(FSDPPACK_ESTATE, "plan_bucket: invalid plan handle");
+    if (bucket < 0 || bucket >= static_cast<int32_t>(plan->buckets.size()))
+        return fail(FSDPPACK_EINVAL, "plan_bucket: bucket index out of range");
+    const BucketPlan &b = plan->buckets[bucket];
+    if (reduce_dtype) *reduce_dtype = b.dtype;
+    if (S) *S = b.S;
+    if (nmembers) *nmembers = static_cast<int32_t>(b.members.size());
+    if (members) *members = b.members.data();
+    if (P) *P = b.P.data();
+    if (O) *O = b.O.data();
+    return FSDPPACK_OK;
+}
+
+int fsdppack_plan_all_gather_layout(const fsdppack_plan *plan, int64_t *B, const int64_t **P, const int64_t **A)
+{
+    if (!plan_ok(plan)) return fail(FSDPPACK_ESTATE, "plan_all_gather_layout: invalid plan handle");
+    if (B) *B = plan->B;
+    if (P) *P = plan->P.data();
+    if (A) *A = plan->A.data();
+    return FSDPPACK_OK;
+}
+
+int fsdppack_pack_reduce_scatter_input(const fsdppack_plan *cplan, int32_t bucket, const void *const *grads,
+                                       void *out, void *stream)
+{
+    fsdppack_plan *plan = const_cast<fsdppack_plan *>(cplan);
+    if (!plan_ok(plan)) return fail(FSDPPACK_ESTATE, "pack_reduce_scatter_input: invalid plan handle");
+    if (bucket < 0 || bucket >= static_cast<int32_t>(plan->buckets.size()))
+        return fail(FSDPPACK_EINVAL, "pack_reduce_scatter_input: bucket index out of range");
+    if (grads == nullptr) return fail(FSDPPACK_EINVAL, "pack_reduce_scatter_input: grads is NULL");
+    BucketPlan &b = plan->buckets[bucket];
+    const int64_t dsz = dtype_bytes(b.dtype);
+    if (b.S > 0 && (out == nullptr || !aligned(out, dsz)))
+        return fail(FSDPPACK_EINVAL, "pack_reduce_scatter_input: out is NULL or not aligned to its element size");
+    std::vector<uint64_t> key(plan->n, 0);
+    for (int32_t t : b.members) {
+        if (plan->numel[t] == 0) continue;
+        const void *g = grads[t];
+        if (g == nullptr || !aligned(g, dtype_bytes(plan->params[t].grad_dtype)))
+            return fail(FSDPPACK_EINVAL, "pack_reduce_scatter_input: grads[" + std::to_string(t) +
+                                             "] is NULL or not aligned to its element size");
+        key[t] = reinterpret_cast<uint64_t>(g);
+    }
+    try {
+        return run_list(plan, b.pack, static_cast<size_t>(bucket), key, static_cast<char *>(out), stream,
+                        "pack_reduce_scatter_input");
+    } catch (const std::bad_alloc &) {
+        return fail(FSDPPACK_ENOMEM, "pack_reduce_scatter_input: out of host memory");
+    }
+}
+
+int fsdppack_all_gather_copy_in(const fsdppack_plan *cplan, int32_t rank, const void *const *shards, void *ag_out,
+                                void *stream)
+{
+    fsdppack_plan *plan = const_cast<fsdppack_plan *>(cplan);
+    if (!plan_ok(plan)) return fail(FSDPPACK_ESTATE, "all_gather_copy_in: invalid plan handle");
+    if (rank < 0 || rank >= plan->W) return fail(FSDPPACK_EINVAL, "all_gather_copy_in: rank out of range");
+    if (shards == nullptr) return fail(FSDPPACK_EINVAL, "all_gather_copy_in: shards is NULL");
+    if (plan->B > 0 && (ag_out == nullptr || !aligned(ag_out, 4)))
+        return fail(FSDPPACK_EINVAL, "all_gather_copy_in: ag_out is NULL or not 4-byte aligned");
+    std::vector<uint64_t> key(plan->n, 0);
+    for (int32_t t = 0; t < plan->n; ++t) {
+        if (plan->P[t] == 0) continue;
+        const void *s = shards[t];
+        if (s == nullptr || !aligned(s, dtype_bytes(plan->params[t].storage_dtype)))
+            return fail(FSDPPACK_EINVAL, "all_gather_copy_in: shards[" + std::to_string(t) +
+                                             "] is NULL or not aligned to its element size");
+        key[t] = reinterpret_cast<uint64_t>(s);
+    }
+    char *row = static_cast<char *>(ag_out) + static_cast<int64_t>(rank) * plan->B;
+    try {
+        return run_list(plan, plan->copy_in, plan->buckets.size(), key, row, stream, "all_gather_copy_in");
+    } catch (const std::bad_alloc &) {
+        return fail(FSDPPACK_ENOMEM, "all_gather_copy_in: out of host memory");
+    }
+}
+
+int fsdppack_all_gather_copy_out(const fsdppack_plan *cplan, const void *ag, void *const *params, void *stream)
+{
+    fsdppack_plan *plan = const_cast<fsdppack_plan *>(cplan);
+    if (!plan_ok(plan)) return fail(FSDPPACK_ESTATE, "all_gather_copy_out: invalid plan handle");
+    if (params == nullptr) return fail(FSDPPACK_EINVAL, "all_gather_copy_out: params is NULL");
+    if (plan->B > 0 && (ag == nullptr || !aligned(ag, 4)))
+        return fail(FSDPPACK_EINVAL, "all_gather_copy_out: ag is NULL or not 4-byte aligned");
+    std::vector<uint64_t> key(plan->n, 0);
+    for (int32_t t = 0; t < plan->n; ++t) {
+        if (plan->numel[t] == 0) continue;
+        void *d = params[t];
+        if (d == nullptr || !aligned(d, dtype_bytes(plan->params[t].param_dtype)))
+            return fail(FSDPPACK_EINVAL, "all_gather_copy_out: params[" + std::to_string(t) +
+                                             "] is NULL or not aligned to its element size");
+        key[t] = reinterpret_cast<uint64_t>(d);
+    }
+    try {
+        return run_list(plan, plan->copy_out, plan->buckets.size() + 1, key,
+                        const_cast<char *>(static_cast<const char *>(ag)), stream, "all_gather_copy_out");
+    } catch (const std::bad_alloc &) {
+        return fail(FSDPPACK_ENOMEM, "all_gather_copy_out: out of host memory");
+    }
+}
+
+void fsdppack_plan_destroy(fsdppack_plan *plan)
+{
+    if (!plan_ok(plan)) return;
+    {
+        std::lock_guard<std::mutex> lock(plan->mu);
+        for (PtrCache &c : plan->caches) {
+            for (PtrSlot &s : c.slots) {
+                if (s.used) {
+                    (void)hipEventSynchronize(static_cast<hipEvent_t>(s.used));
+                    (void)hipEventDestroy(static_cast<hipEvent_t>(s.used));
+                }
+                if (s.ready) (void)hipEventDestroy(static_cast<hipEvent_t>(s.ready));
+                if (s.d_table) (void)hipFree(s.d_table);
+                if (s.h_stage) (void)hipHostFree(s.h_stage);
+            }
+        }
+        auto free_list = [](WorkList &wl) {
+            if (wl.d_segs) (void)hipFree(wl.d_segs);
+            if (wl.d_items) (void)hipFree(wl.d_items);
+            wl.d_segs = nullptr;
+            wl.d_items = nullptr;
+        };
+        for (BucketPlan &b : plan->buckets) free_list(b.pack);
+        free_list(plan->copy_in);
+        free_list(plan->copy_out);
+        plan->magic = 0;
+    }
+    delete plan;
+}
+
+const char *fsdppack_last_error(void) { return g_error.c_str(); }
+
+int fsdppack_time_next_launch(void *start_event, void *stop_event)
+{
+    g_next_start = start_event;
+    g_next_stop = stop_event;
+    return FSDPPACK_OK;
+}
+
+int fsdppack_counters(int64_t *counters, int32_t n)
+{
+    if (counters == nullptr || n < 0) return fail(FSDPPACK_EINVAL, "counters: bad arguments");
+    for (int32_t i = 0; i < n && i < 4; ++i) counters[i] = g_counters[i].load();
+    return FSDPPACK_OK;
+}
+
+}  // extern "C"

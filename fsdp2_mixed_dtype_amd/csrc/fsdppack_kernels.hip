@@ -1,0 +1,305 @@
+// fsdppack_kernels.hip -- the grouped multi-tensor segment kernel of
+// libfsdppack for gfx950 (MI355X).
+//
+// One launch moves a whole work list: the reduce-scatter pack of a bucket
+// (every (rank, tensor) chunk, cast to the reduction dtype and zero-padded:
+// "PyTorch adds per-parameter mixed precision to FSDP2", paragraph 2), the
+// all-gather copy-in of one rank (every shard cast to its compute dtype,
+// paragraph 1) or the all-gather copy-out (every gathered segment back into
+// its full parameter, padding dropped).
+//
+// The work is pure data movement with a handful of integer operations per
+// element, so the design aims at HBM bandwidth, not at the matrix cores:
+//  * each workgroup (one wave64) owns one item of the host-built prefix map
+//    (4 KiB of destination) and walks the segments it overlaps;
+//  * every destination byte is written by a 16-byte vector store from its
+//    16-byte aligned address (scalar stores only at a range's unaligned head
+//    and tail), 64-lane wavefronts covering 1 KiB per store instruction;
+//  * source vectors come from 8- or 16-byte loads that need only dword
+//    alignment; a bf16 source sitting 2 bytes past a dword boundary loads
+//    one extra dword and shifts adjacent dwords by 16 bits, so no load ever
+//    touches a dword that holds no byte of the source;
+//  * bf16 -> fp32 widening and fp32 -> bf16 round-to-nearest-even happen in
+//    registers with integer operations (bit exact, independent of the
+//    floating-point mode registers);
+//  * padding is produced by stores of zero vectors, never by reads.
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include "fsdppack_internal.h"
+
+namespace fsdppack {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// One wavefront per workgroup, each lane holding four destination vectors
+// in flight: an item of kBlock * kUnroll * 16 = 4 KiB of destination is one
+// unrolled pass (all loads issued, then all stores), and a launch has many
+// thousands of short workgroups, which kept more bytes in flight than
+// longer-lived or persistent workgroups in measurements on MI355X.
+constexpr int kBlock = 64;    // threads per workgroup (one wave64)
+constexpr int kUnroll = 4;    // destination vectors in flight per thread
+static_assert(kBlock * kUnroll * 16 == kItemBytes, "one item is one unrolled pass of the workgroup");
+
+template <int DT> struct ElemT;
+template <> struct ElemT<kBF16> { using T = uint16_t; };
+template <> struct ElemT<kFP32> { using T = uint32_t; };
+
+// binary32 bits -> bfloat16 bits.  Adding 0x7FFF plus the lowest kept bit
+// and dropping the low half rounds to nearest with ties to even (a carry
+// runs into the exponent, reaching infinity past the largest finite value).
+// NaNs are selected separately: quiet bit set, sign and top payload kept.
+__device__ __forceinline__ uint32_t f32_to_bf16(uint32_t u)
+{
+    const uint32_t rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    const bool is_nan = (u & 0x7FFFFFFFu) > 0x7F800000u;
+    return is_nan ? ((u >> 16) | 0x0040u) : rounded;
+}
+
+template <int S, int D>
+__device__ __forceinline__ uint32_t convert1(uint32_t bits)
+{
+    if constexpr (S == kBF16 && D == kFP32) return bits << 16;
+    else if constexpr (S == kFP32 && D == kBF16) return f32_to_bf16(bits);
+    else return bits;
+}
+
+template <int S, int D>
+struct Path {
+    using ST = typename ElemT<S>::T;
+    using DT = typename ElemT<D>::T;
+    static constexpr int V = 16 / (int)sizeof(DT);             // elements per 16 B store
+    static constexpr int NSRC = V * (int)sizeof(ST) / 4;        // source dwords per vector
+};
+
+// ---------------------------------------------------------------- loads
+//
+// Caller tensors arrive through the pointer table as plain addresses; they
+// are global memory, so every access is made through address-space-1
+// pointers (global_load / global_store rather than flat instructions).
+// (C-style casts: C++ casts may not change the address space.)  Multi-dword
+// loads need only dword alignment; the vector types below say so.
+
+#define FSDPPACK_GLOBAL __attribute__((address_space(1)))
+typedef u32x4 u32x4_a4 __attribute__((aligned(4)));
+typedef u32x2 u32x2_a4 __attribute__((aligned(4)));
+
+template <typename T>
+__device__ __forceinline__ const FSDPPACK_GLOBAL T *gin(const char *p) { return (const FSDPPACK_GLOBAL T *)p; }
+template <typename T>
+__device__ __forceinline__ FSDPPACK_GLOBAL T *gout(char *p) { return (FSDPPACK_GLOBAL T *)p; }
+
+// N consecutive dwords from a 4-byte aligned global address.
+template <int N>
+__device__ __forceinline__ void load_dwords(const char *p, uint32_t *w)
+{
+    const FSDPPACK_GLOBAL uint32_t *g = gin<uint32_t>(p);
+    int i = 0;
+#pragma unroll
+    for (; i + 4 <= N; i += 4) {
+        const u32x4 v = *(const FSDPPACK_GLOBAL u32x4_a4 *)(g + i);
+        w[i] = v.x; w[i + 1] = v.y; w[i + 2] = v.z; w[i + 3] = v.w;
+    }
+    if constexpr (N % 4 >= 2) {
+        const u32x2 v = *(const FSDPPACK_GLOBAL u32x2_a4 *)(g + (N / 4) * 4);
+        w[(N / 4) * 4] = v.x; w[(N / 4) * 4 + 1] = v.y;
+    }
+    if constexpr (N % 2 == 1) w[N - 1] = g[N - 1];
+}
+
+// Source vector of NSRC dwords starting 2 bytes past a dword boundary (a
+// bf16 source whose element offset is odd): load NSRC + 1 dwords from the
+// boundary below and shift every adjacent pair down by 16 bits.  The first
+// and last dword each still hold a byte of the vector, so no load touches a
+// dword the source does not own part of.
+template <int NSRC>
+__device__ __forceinline__ void load_half_shifted(const char *p_minus_2, uint32_t (&o)[NSRC])
+{
+    uint32_t w[NSRC + 1];
+    load_dwords<NSRC + 1>(p_minus_2, w);
+#pragma unroll
+    for (int k = 0; k < NSRC; ++k) o[k] = (w[k] >> 16) | (w[k + 1] << 16);
+}
+
+// ---------------------------------------------------------------- convert + store
+
+template <int S, int D>
+__device__ __forceinline__ u32x4 convert_vec(const uint32_t (&w)[Path<S, D>::NSRC])
+{
+    u32x4 r;
+    if constexpr (S == kBF16 && D == kFP32) {          // 4 bf16 -> 4 fp32
+        r.x = w[0] << 16; r.y = w[0] & 0xFFFF0000u;
+        r.z = w[1] << 16; r.w = w[1] & 0xFFFF0000u;
+    } else if constexpr (S == kFP32 && D == kBF16) {   // 8 fp32 -> 8 bf16
+        r.x = f32_to_bf16(w[0]) | (f32_to_bf16(w[1]) << 16);
+        r.y = f32_to_bf16(w[2]) | (f32_to_bf16(w[3]) << 16);
+        r.z = f32_to_bf16(w[4]) | (f32_to_bf16(w[5]) << 16);
+        r.w = f32_to_bf16(w[6]) | (f32_to_bf16(w[7]) << 16);
+    } else {                                           // same dtype: bit copy
+        r.x = w[0]; r.y = w[1]; r.z = w[2]; r.w = w[3];
+    }
+    return r;
+}
+
+// Non-temporal: the packed buffer is consumed by the collective, not by
+// this kernel, so it should stream past the caches (measured faster).
+__device__ __forceinline__ void store16(char *p, u32x4 v)
+{
+    __builtin_nontemporal_store(v, gout<u32x4>(p));
+}
+
+// One element: dst[i] = i < valid ? cast(src[i]) : +0.
+template <int S, int D>
+__device__ __forceinline__ void copy_one(const char *src, char *dst, int64_t i, int64_t valid)
+{
+    using P = Path<S, D>;
+    uint32_t v = 0;
+    if (i < valid) v = convert1<S, D>(gin<typename P::ST>(src)[i]);
+    gout<typename P::DT>(dst)[i] = static_cast<typename P::DT>(v);
+}
+
+// A destination vector that straddles the end of the valid prefix (at most
+// one per segment): element-wise loads of the valid part only.
+template <int S, int D>
+__device__ __forceinline__ void copy_straddle(const char *src, char *dst, int64_t i0, int64_t valid)
+{
+    using P = Path<S, D>;
+    typename P::DT e[P::V];
+#pragma unroll
+    for (int k = 0; k < P::V; ++k) {
+        uint32_t v = 0;
+        if (i0 + k < valid) v = convert1<S, D>(gin<typename P::ST>(src)[i0 + k]);
+        e[k] = static_cast<typename P::DT>(v);
+    }
+    u32x4 r;
+    __builtin_memcpy(&r, e, 16);
+    store16(dst + i0 * (int64_t)sizeof(typename P::DT), r);
+}
+
+// Elements [lo, hi) of one segment: dst[i] = i < valid ? cast(src[i]) : +0,
+// where src / dst address element 0 of the segment.  All threads of the
+// workgroup take part; no two threads write the same byte.
+template <int S, int D>
+__device__ void copy_range(const char *__restrict__ src, char *__restrict__ dst, int64_t lo,
+                           int64_t hi, int64_t valid)
+{
+    using P = Path<S, D>;
+    constexpr int64_t SB = sizeof(typename P::ST), DB = sizeof(typename P::DT);
+    const int tid = threadIdx.x;
+
+    // head: elements before the first 16-byte aligned destination address
+    const uint32_t dmis = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst + lo * DB) & 15u);
+    int64_t head = static_cast<int64_t>(((16u - dmis) & 15u) / DB);
+    if (head > hi - lo) head = hi - lo;
+    if (tid < head) copy_one<S, D>(src, dst, lo + tid, valid);
+
+    const int64_t v0 = lo + head;                 // first aligned vector
+    const int64_t nvec = (hi - v0) / P::V;
+    int64_t nfull = valid > v0 ? (valid - v0) / P::V : 0;
+    if (nfull > nvec) nfull = nvec;
+
+    if (nfull > 0) {
+        const char *s0 = src + v0 * SB;
+        char *d0 = dst + v0 * DB;
+        constexpr int64_t SV = P::V * SB;       // source bytes per vector
+        // element alignment makes the source 4-byte aligned, or 2 bytes past
+        // a dword boundary for a bf16 source at an odd element offset
+        if ((reinterpret_cast<uintptr_t>(s0) & 3u) == 0) {
+            for (int64_t q = tid; q < nfull; q += kBlock * kUnroll) {
+                uint32_t w[kUnroll][P::NSRC];
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    const int64_t qq = q + u * kBlock;
+                    if (qq < nfull) load_dwords<P::NSRC>(s0 + qq * SV, w[u]);
+                }
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    const int64_t qq = q + u * kBlock;
+                    if (qq < nfull) store16(d0 + qq * 16, convert_vec<S, D>(w[u]));
+                }
+            }
+        } else if constexpr (S == kBF16) {
+            const char *a0 = s0 - 2;
+            for (int64_t q = tid; q < nfull; q += kBlock * kUnroll) {
+                uint32_t w[kUnroll][P::NSRC];
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    const int64_t qq = q + u * kBlock;
+                    if (qq < nfull) load_half_shifted<P::NSRC>(a0 + qq * SV, w[u]);
+                }
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    const int64_t qq = q + u * kBlock;
+                    if (qq < nfull) store16(d0 + qq * 16, convert_vec<S, D>(w[u]));
+                }
+            }
+        }
+    }
+
+    // the straddling vector (if any) and the all-padding vectors
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    for (int64_t q = nfull + tid; q < nvec; q += kBlock) {
+        const int64_t i0 = v0 + q * P::V;
+        if (i0 >= valid) store16(dst + i0 * DB, zero);
+        else copy_straddle<S, D>(src, dst, i0, valid);
+    }
+
+    // tail: elements after the last whole vector
+    const int64_t t0 = v0 + nvec * P::V;
+    if (tid < hi - t0) copy_one<S, D>(src, dst, t0 + tid, valid);
+}
+
+__device__ __forceinline__ void run_segment(const Seg &g, int64_t lo, int64_t hi,
+                                            const uint64_t *table, char *base)
+{
+    char *tp = reinterpret_cast<char *>(table[g.slot]);
+    const char *src;
+    char *dst;
+    if (g.table_side == kTableIsSource) { src = tp + g.src_off; dst = base + g.dst_off; }
+    else { src = base + g.src_off; dst = tp + g.dst_off; }
+    switch (g.src_dt * 4 + g.dst_dt) {
+    case kBF16 * 4 + kFP32: copy_range<kBF16, kFP32>(src, dst, lo, hi, g.valid); break;
+    case kFP32 * 4 + kFP32: copy_range<kFP32, kFP32>(src, dst, lo, hi, g.valid); break;
+    case kFP32 * 4 + kBF16: copy_range<kFP32, kBF16>(src, dst, lo, hi, g.valid); break;
+    case kBF16 * 4 + kBF16: copy_range<kBF16, kBF16>(src, dst, lo, hi, g.valid); break;
+    default: break;   // the planner only emits the four pairs above
+    }
+}
+
+// One workgroup per item.  Item k covers everything from items[k] up to (not
+// including) items[k+1]; the host guarantees items[n_items] = {n_segs, 0},
+// so the loop never reads past the segment array.
+__device__ __forceinline__ void run_item(const LaunchArgs &a, int32_t k)
+{
+    const Item first = a.items[k];
+    const Item last = a.items[k + 1];
+    for (int32_t s = first.seg; s < last.seg || (s == last.seg && last.off > 0); ++s) {
+        const Seg g = a.segs[s];
+        const int64_t lo = (s == first.seg) ? first.off : 0;
+        const int64_t hi = (s == last.seg) ? last.off : g.len;
+        if (hi > lo) run_segment(g, lo, hi, a.table, a.base);
+    }
+}
+
+__global__ void __launch_bounds__(kBlock) segments_kernel(LaunchArgs a)
+{
+    run_item(a, static_cast<int32_t>(blockIdx.x));
+}
+
+}  // namespace
+
+int launch_segments(const LaunchArgs &args, void *stream, void *start_event, void *stop_event)
+{
+    if (args.n_items <= 0) return static_cast<int>(hipSuccess);
+    const uint32_t grid = static_cast<uint32_t>(args.n_items);
+    // hipExtLaunchKernelGGL: when events are given they are stamped by the
+    // dispatch itself, so they bracket exactly this kernel's execution
+    hipExtLaunchKernelGGL(segments_kernel, dim3(grid), dim3(kBlock), 0,
+                          static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(start_event),
+                          static_cast<hipEvent_t>(stop_event), 0, args);
+    return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace fsdppack

@@ -1,0 +1,180 @@
+/*
+ * fsdppack.h -- C ABI of libfsdppack: FSDP2's mixed-dtype gradient pack for
+ * reduce-scatter and its all-gather copy-in / copy-out, on AMD MI355X (gfx950).
+ *
+ * What the calls compute (web pages on FSDP2 per-parameter mixed precision):
+ *  - "PyTorch adds per-parameter mixed precision to FSDP2" (ainewsletter.today),
+ *    paragraph 2: gradients of one fully_shard unit arrive in mixed compute
+ *    dtypes (BF16, FP32); they are chunked and padded and cast straight into a
+ *    single buffer of the reduction dtype, one bucket (and one reduce-scatter)
+ *    per effective reduction dtype.  Paragraph 1: the all-gather copy-in
+ *    groups staging copies by (source, target) dtype and keeps one all-gather
+ *    per unit.
+ *  - "The unit you wrapped" (kernels.rudrite.com), shard and padding
+ *    paragraphs: a rank's piece is a contiguous row-major slice, and
+ *    right-hand padding gives every rank the same size.
+ *  - "Mixed-Precision Training" (NeMo AutoModel docs), table "Storage Dtype
+ *    Compared to Compute Dtype": param_dtype is the compute dtype the
+ *    all-gather delivers, reduce_dtype the dtype of the gradient reduction,
+ *    the storage dtype that of the resident sharded parameter.
+ *
+ * Layout (W = world size, a layout parameter only; no collective is issued):
+ *  - Parameter t is viewed as [dim0, inner].  Rank r's chunk is rows
+ *    [r*c, (r+1)*c) with c = ceil(dim0 / W), i.e. flat elements
+ *    [r*P, r*P + P) with P = c * inner; elements past numel = dim0 * inner
+ *    are padding (+0).
+ *  - Reduce-scatter input of a bucket: a row-major [W, S] array of the bucket's
+ *    reduction dtype, S = sum of the members' P; member t occupies columns
+ *    [O_t, O_t + P_t) of every row, O_t the exclusive prefix sum of P in
+ *    unit order.
+ *  - All-gather buffer: a row-major [W, B]-byte array; parameter t's P_t
+ *    elements in its param dtype start at byte A_t of each row (A_0 = 0, every
+ *    A_t and B a multiple of 16, parameters in unit order, gap bytes zero).
+ *
+ * Conventions:
+ *  - dtype codes: FSDPPACK_BF16 (bfloat16), FSDPPACK_FP32 (IEEE binary32).
+ *    bf16 -> fp32 is exact; fp32 -> bf16 rounds to nearest, ties to even,
+ *    keeps subnormals, overflows to infinity, and turns a NaN into a quiet
+ *    NaN with the same sign and top payload bits.
+ *  - Data pointers are device pointers owned by the caller; each must be
+ *    aligned to its element size.  Pointer arrays (grads, shards, params) are
+ *    host arrays with one entry per parameter, indexed by parameter (unit
+ *    order); they are read during the call only.  An entry may be NULL only
+ *    where it is never dereferenced (a parameter with zero elements, or one
+ *    outside the bucket being packed).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every compute
+ *    call enqueues exactly one kernel launch on it and returns without
+ *    waiting; argument errors are reported synchronously and enqueue nothing.
+ *  - Every call returns FSDPPACK_OK (0) or a negative error code, and on
+ *    error leaves a message for fsdppack_last_error() (per thread).  No
+ *    exception crosses the ABI.
+ *  - A plan is immutable after creation and may be shared by threads and
+ *    streams; its device tables are uploaded on the first compute call that
+ *    needs them (a synchronous copy) on the device current at that time, and
+ *    the plan may only be used on that device afterwards.
+ */
+#ifndef FSDPPACK_H
+#define FSDPPACK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fsdppack_dtype {
+    FSDPPACK_DTYPE_NONE = 0,   /* reduce_dtype only: "unset", use the grad dtype */
+    FSDPPACK_BF16 = 1,
+    FSDPPACK_FP32 = 2
+};
+
+enum fsdppack_status {
+    FSDPPACK_OK = 0,
+    FSDPPACK_EINVAL = -1,  /* bad argument: NULL, out-of-range index, misaligned pointer, bad size */
+    FSDPPACK_EDTYPE = -2,  /* unsupported dtype code */
+    FSDPPACK_ENOMEM = -3,  /* host or device allocation failed */
+    FSDPPACK_EHIP = -4,    /* a HIP runtime call failed (the message names it) */
+    FSDPPACK_ESTATE = -5   /* plan destroyed or corrupt, or used on another device */
+};
+
+/* One parameter of a fully_shard unit.  dim0 >= 0, inner >= 1 when dim0 > 0
+ * (a 0-d tensor is dim0 = 1, inner = 1).  grad_dtype: the dtype its gradient
+ * arrives in.  reduce_dtype: the policy's reduction dtype, or
+ * FSDPPACK_DTYPE_NONE for "same as the gradient".  storage_dtype: dtype of
+ * the resident sharded parameter (copy-in source).  param_dtype: compute
+ * dtype delivered by the all-gather (copy-in target, copy-out dtype). */
+typedef struct fsdppack_param_desc {
+    int64_t dim0;
+    int64_t inner;
+    int32_t grad_dtype;
+    int32_t reduce_dtype;
+    int32_t storage_dtype;
+    int32_t param_dtype;
+} fsdppack_param_desc;
+
+typedef struct fsdppack_plan fsdppack_plan;   /* opaque, library-owned */
+
+/* Plan one unit: bucket the n parameters by effective reduction dtype
+ * (reduce_dtype if set, else grad_dtype; buckets in order of first
+ * appearance, members in unit order) and compute P, O, S per bucket and the
+ * all-gather offsets A and row size B.  Host work only (no HIP call).
+ * params: n descriptors (host).  world: W >= 1.  *out_plan receives a new
+ * plan owned by the caller until fsdppack_plan_destroy.
+ * Errors: EINVAL (NULL, n < 0, W < 1, negative sizes, sizes whose byte
+ * counts overflow int64), EDTYPE (unknown dtype code), ENOMEM. */
+int fsdppack_plan_buckets(const fsdppack_param_desc *params, int32_t n, int32_t world,
+                          fsdppack_plan **out_plan);
+
+/* Number of buckets and parameters of a plan. */
+int fsdppack_plan_info(const fsdppack_plan *plan, int32_t *num_buckets, int32_t *num_params,
+                       int32_t *world);
+
+/* Describe bucket `bucket`: its reduction dtype, row length S, and its
+ * nmembers parameter indices with their P and O (arrays owned by the plan,
+ * valid until it is destroyed).  Any output pointer may be NULL. */
+int fsdppack_plan_bucket(const fsdppack_plan *plan, int32_t bucket, int32_t *reduce_dtype,
+                         int64_t *S, int32_t *nmembers, const int32_t **members,
+                         const int64_t **P, const int64_t **O);
+
+/* All-gather layout: row bytes B, and per parameter (unit order) P and the
+ * byte offset A within a row (arrays owned by the plan).  Any output pointer
+ * may be NULL. */
+int fsdppack_plan_all_gather_layout(const fsdppack_plan *plan, int64_t *B, const int64_t **P,
+                                    const int64_t **A);
+
+/* Fused reduce-scatter pack of one bucket (the _chunk_cat.out-style op):
+ *   out[r*S + O_t + j] = cast(grads[t][r*P_t + j])  if r*P_t + j < numel_t,
+ *                      = +0                          otherwise,
+ * for every member t, rank r < W and j < P_t, cast = the member's grad dtype
+ * to the bucket's reduction dtype.  grads: n host entries (by parameter
+ * index) of device pointers to contiguous gradients of numel_t elements;
+ * only the bucket's members are read.  out: device buffer of W*S elements of
+ * the reduction dtype, fully overwritten.  One kernel launch on `stream`.
+ * Errors: EINVAL (bucket out of range, NULL or misaligned pointer), ESTATE,
+ * EHIP, ENOMEM. */
+int fsdppack_pack_reduce_scatter_input(const fsdppack_plan *plan, int32_t bucket,
+                                       const void *const *grads, void *out, void *stream);
+
+/* All-gather copy-in for rank `rank` (0 <= rank < W): row `rank` of ag_out
+ * (a device [W, B]-byte buffer) receives each parameter's padded local shard
+ * cast from its storage dtype to its param dtype at byte A_t; the row's gap
+ * bytes are written as zero, the other rows are not touched.  shards: n host
+ * entries of device pointers to P_t elements each (storage dtype).  The
+ * copies are grouped by (storage, param) dtype pair inside one launch.
+ * Errors: EINVAL, ESTATE, EHIP, ENOMEM. */
+int fsdppack_all_gather_copy_in(const fsdppack_plan *plan, int32_t rank, const void *const *shards,
+                                void *ag_out, void *stream);
+
+/* All-gather copy-out: rebuild every full parameter from the gathered
+ * [W, B]-byte buffer ag, dropping padding:
+ *   params[t][r*P_t + j] = element j of parameter t's segment in row r,
+ *   for j < min(P_t, numel_t - r*P_t).
+ * params: n host entries of device pointers to numel_t elements each
+ * (param dtype), fully overwritten.  Errors: EINVAL, ESTATE, EHIP, ENOMEM. */
+int fsdppack_all_gather_copy_out(const fsdppack_plan *plan, const void *ag, void *const *params,
+                                 void *stream);
+
+/* Free a plan and its device tables (waits for work still using them).
+ * NULL is a no-op. */
+void fsdppack_plan_destroy(fsdppack_plan *plan);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *fsdppack_last_error(void);
+
+/* Kernel timing: the next compute call made on this thread that launches a
+ * kernel stamps `start_event` and `stop_event` (hipEvent_t, created by the
+ * caller with timing enabled; either may be NULL) at that kernel's start and
+ * end, so hipEventElapsedTime gives its exact execution time.  Applies to one
+ * launch, then clears.  For benchmarks and profilers. */
+int fsdppack_time_next_launch(void *start_event, void *stop_event);
+
+/* Library-wide counters since load (for tests and tracing): counters[0] =
+ * kernel launches, [1] = pointer-table uploads, [2] = pointer-table reuses,
+ * [3] = plan device-table uploads.  n <= 4 entries are written. */
+int fsdppack_counters(int64_t *counters, int32_t n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FSDPPACK_H */

@@ -1,0 +1,326 @@
+"""GPU parity: libfsdppack's HIP kernels (through the C ABI) against the CPU
+oracle, byte for byte (0 ULP), on the same seeded inputs.
+
+Covered: the reduce-scatter pack of every bucket of the five workloads at
+full size (the launch configuration the benchmark times), the same with
+special values injected, random layouts with misaligned sources and outputs,
+the all-gather copy-in and copy-out, the copy-in -> all-gather -> copy-out
+round trip, every float32 bit pattern through the fp32 -> bf16 cast, edge
+cases (empty, W = 1, dim0 < W, zero-size tensors), determinism, one launch per
+call, and pointer-table reuse / eviction.  Destination buffers are poisoned
+with 0xAB and surrounded by guard bytes that must stay untouched.
+"""
+import random
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+import fsdp2_mixed_dtype_amd as fp  # noqa: E402
+
+BF16, FP32 = 1, 2
+DEV = torch.device("cuda:0")
+GUARD = 256          # guard bytes on each side of every destination
+POISON = 0xAB
+
+
+def to_dev(a, dt, elem_offset=0):
+    """Copy a host array (bf16 as uint16 bits, or float32) to the GPU,
+    optionally as a view starting `elem_offset` elements into a larger
+    allocation (to test misaligned sources)."""
+    a = np.ascontiguousarray(a).reshape(-1)
+    base = torch.empty(a.size + elem_offset, dtype=fp.TORCH_DTYPE[dt], device=DEV)
+    t = base[elem_offset:]
+    host = torch.from_numpy(a.copy())
+    if dt == BF16:
+        host = host.view(torch.bfloat16)
+    t.copy_(host)
+    return t
+
+
+def host_bytes(t):
+    return t.detach().contiguous().view(torch.uint8).cpu().numpy()
+
+
+class Guarded:
+    """A poisoned destination of `numel` elements at `elem_offset` elements
+    past a 256-byte aligned start, with guard bytes on both sides."""
+
+    def __init__(self, numel, dt, elem_offset=0):
+        # dt: BF16 / FP32, or None for a plain byte buffer
+        esz = fp.ELEM_SIZE[dt] if dt else 1
+        self.front = GUARD + elem_offset * esz
+        self.nbytes = numel * esz
+        self.raw = torch.full((self.front + self.nbytes + GUARD,), POISON, dtype=torch.uint8, device=DEV)
+        self.t = self.raw[self.front:self.front + self.nbytes]
+        if dt:
+            self.t = self.t.view(fp.TORCH_DTYPE[dt])
+
+    def result(self):
+        h = host_bytes(self.raw)
+        assert np.all(h[:self.front] == POISON), "write before the destination"
+        assert np.all(h[self.front + self.nbytes:] == POISON), "write past the destination"
+        return h[self.front:self.front + self.nbytes]
+
+
+def gpu_pack(plan, bucket, g_dev, out_offset=0):
+    b = plan.buckets[bucket]
+    out = Guarded(plan.world * b.S, b.dtype, out_offset)
+    fp.pack_reduce_scatter_input(plan, bucket, g_dev, out.t)
+    torch.cuda.synchronize()
+    return out.result()
+
+
+def check_pack(w, grads, src_offsets=None, out_offset=0):
+    ref = oracle.plan(w.descs(), w.world)
+    plan = fp.plan_buckets(w.descs(), w.world)
+    src_offsets = src_offsets or [0] * len(grads)
+    g_dev = [to_dev(g, t.grad_dtype, o) for g, t, o in zip(grads, w.tensors, src_offsets)]
+    for bi in range(len(ref.buckets)):
+        got = gpu_pack(plan, bi, g_dev, out_offset)
+        want = oracle.pack(ref, bi, grads).view(np.uint8).reshape(-1)
+        if not np.array_equal(got, want):
+            bad = np.flatnonzero(got != want)
+            pytest.fail(f"{w.name} bucket {bi}: {bad.size} bytes differ, first at byte {bad[0]}")
+    plan.destroy()
+
+
+_grad_cache = {}
+
+
+def grads_of(name):
+    if name not in _grad_cache:
+        _grad_cache.clear()
+        _grad_cache[name] = wl.make_grads(wl.get(name))
+    return _grad_cache[name]
+
+
+# --------------------------------------------------------------------------- pack
+
+@pytest.mark.parametrize("name", ["tiny", "mixed50m", "layout500", "kda_block", "hetero500"])
+def test_pack_full_size_matches_oracle(name):
+    print(f"[pack parity] workload={name}", flush=True)
+    w = wl.get(name)
+    check_pack(w, grads_of(name))
+
+
+def test_pack_special_values_heterogeneous():
+    print("[pack parity] hetero500 + specials", flush=True)
+    w = wl.hetero500()
+    grads = [g.copy() for g in grads_of("hetero500")]
+    wl.inject_specials(grads, [t.grad_dtype for t in w.tensors], seed=5)
+    check_pack(w, grads)
+
+
+def _random_workload(rng, seed):
+    W = rng.choice([1, 2, 3, 4, 5, 8, 16, 33, 128])
+    n = rng.randint(1, 9)
+    shapes, gdt, rdt = [], [], []
+    for _ in range(n):
+        dim0 = rng.choice([0, 1, 2, W - 1, W, W + 1, rng.randint(1, 9 * W + 5), rng.randint(1, 3000)])
+        inner = rng.choice([1, 2, 3, 7, 8, 64, 33, 129])
+        shapes.append((max(dim0, 0), inner))
+        gdt.append(rng.choice([BF16, FP32]))
+        rdt.append(rng.choice([0, BF16, FP32]))
+    return wl.custom(shapes, gdt, rdt, W, seed, storage_dtypes=[rng.choice([BF16, FP32]) for _ in range(n)])
+
+
+def test_pack_random_layouts_misaligned():
+    rng = random.Random(2024)
+    for case in range(60):
+        w = _random_workload(rng, case)
+        grads = wl.make_grads(w)
+        wl.inject_specials(grads, [t.grad_dtype for t in w.tensors], seed=case)
+        offsets = [rng.choice([0, 0, 1, 2, 3, 5, 7]) for _ in grads]
+        out_off = rng.choice([0, 0, 1, 2, 3, 6])
+        print(f"[pack random] case={case} W={w.world} n={len(w.tensors)} src_off={offsets} out_off={out_off}",
+              flush=True)
+        check_pack(w, grads, offsets, out_off)
+
+
+def test_pack_every_f32_pattern_to_bf16():
+    """All 2**32 float32 bit patterns through the fp32 -> bf16 pack (W=1)."""
+    chunk = 1 << 28
+    plan = fp.plan_buckets([(chunk, 1, FP32, BF16, FP32, FP32)], 1)
+    out = torch.empty(chunk, dtype=torch.bfloat16, device=DEV)
+    for start in range(0, 1 << 32, chunk):
+        print(f"[exhaustive fp32->bf16] chunk start={start:#x}", flush=True)
+        x = torch.arange(start, start + chunk, dtype=torch.int64, device=DEV)
+        x = torch.where(x >= 2**31, x - 2**32, x).to(torch.int32).view(torch.float32)
+        fp.pack_reduce_scatter_input(plan, 0, [x], out)
+        got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+        del x
+        u = np.arange(start, start + chunk, dtype=np.uint64).astype(np.uint32)
+        want = oracle.convert(u.view(np.float32), FP32, BF16)
+        assert np.array_equal(got, want), f"mismatch in chunk {start:#x}"
+    plan.destroy()
+
+
+def test_pack_every_bf16_pattern_to_fp32():
+    h = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    w = wl.custom([(1 << 16,)], [BF16], [FP32], 1)
+    check_pack(w, [h])
+    w4 = wl.custom([(1 << 16,)], [BF16], [FP32], 3)       # ragged, W=3
+    check_pack(w4, [h], [1])
+
+
+def test_pack_edge_cases():
+    cases = [
+        wl.custom([(0, 4), (0, 1)], [FP32, BF16], [FP32, FP32], 4),          # nothing to do
+        wl.custom([(1,)], [BF16], [FP32], 8),                                  # one element, W > dim0
+        wl.custom([(5, 3)], [FP32], [BF16], 1),                                # W = 1
+        wl.custom([(3, 1), (2, 5), (7, 2)], [BF16, FP32, BF16], [FP32, FP32, FP32], 1000),  # large W
+        wl.custom([(0, 3), (4, 4), (0, 9)], [FP32, FP32, BF16], [0, 0, 0], 3),  # empty members
+        wl.custom([(8, 0), (2, 2)], [BF16, BF16], [0, 0], 2),                  # inner 0
+    ]
+    for i, w in enumerate(cases):
+        print(f"[pack edge] case={i}", flush=True)
+        check_pack(w, wl.make_grads(w))
+
+
+def test_pack_non_members_may_be_none():
+    w = wl.custom([(6, 6), (5, 1), (9, 2)], [BF16, FP32, BF16], [BF16, FP32, 0], 4)
+    grads = wl.make_grads(w)
+    ref = oracle.plan(w.descs(), w.world)
+    plan = fp.plan_buckets(w.descs(), w.world)
+    g_dev = [to_dev(g, t.grad_dtype) for g, t in zip(grads, w.tensors)]
+    for bi, b in enumerate(plan.buckets):
+        only = [g if i in b.members else None for i, g in enumerate(g_dev)]
+        got = gpu_pack(plan, bi, only)
+        assert np.array_equal(got, oracle.pack(ref, bi, grads).view(np.uint8).reshape(-1))
+
+
+def test_deterministic_one_launch_and_table_reuse():
+    w = wl.mixed50m()
+    grads = grads_of("mixed50m")
+    plan = fp.plan_buckets(w.descs(), w.world)
+    g_dev = [to_dev(g, t.grad_dtype) for g, t in zip(grads, w.tensors)]
+    out1 = torch.empty(w.world * plan.buckets[0].S, dtype=torch.float32, device=DEV)
+    out2 = torch.full_like(out1, 7.0)
+    c0 = fp.counters()
+    fp.pack_reduce_scatter_input(plan, 0, g_dev, out1)
+    c1 = fp.counters()
+    fp.pack_reduce_scatter_input(plan, 0, g_dev, out2)
+    c2 = fp.counters()
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int32), out2.view(torch.int32))
+    assert c1[0] - c0[0] == 1 and c2[0] - c1[0] == 1          # one launch per call
+    assert c1[1] - c0[1] == 1 and c2[1] - c1[1] == 0          # first call uploads the pointer table
+    assert c2[2] - c1[2] == 1                                  # second call reuses it
+    plan.destroy()
+
+
+def test_pointer_table_eviction_keeps_results_correct():
+    w = wl.custom([(37, 3), (5,), (64, 2)], [BF16, FP32, BF16], [FP32, FP32, FP32], 4)
+    ref = oracle.plan(w.descs(), w.world)
+    plan = fp.plan_buckets(w.descs(), w.world)
+    outs, wants = [], []
+    for k in range(40):     # more distinct pointer sets than the cache holds
+        grads = wl.make_grads(w, seed=100 + k)
+        g_dev = [to_dev(g, t.grad_dtype, k % 3) for g, t in zip(grads, w.tensors)]
+        out = torch.empty(w.world * plan.buckets[0].S, dtype=torch.float32, device=DEV)
+        fp.pack_reduce_scatter_input(plan, 0, g_dev, out)
+        outs.append((out, g_dev))
+        wants.append(oracle.pack(ref, 0, grads))
+    torch.cuda.synchronize()
+    for (out, _), want in zip(outs, wants):
+        assert np.array_equal(host_bytes(out), want.view(np.uint8).reshape(-1))
+    plan.destroy()
+
+
+def test_pack_on_side_stream():
+    w = wl.tiny()
+    grads = wl.make_grads(w)
+    ref = oracle.plan(w.descs(), w.world)
+    plan = fp.plan_buckets(w.descs(), w.world)
+    g_dev = [to_dev(g, t.grad_dtype) for g, t in zip(grads, w.tensors)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    out = torch.empty(w.world * plan.buckets[0].S, dtype=torch.float32, device=DEV)
+    with torch.cuda.stream(s):
+        fp.pack_reduce_scatter_input(plan, 0, g_dev, out)
+    fp.pack_reduce_scatter_input(plan, 0, g_dev, out, stream=s)      # same table, explicit stream
+    s.synchronize()
+    assert np.array_equal(host_bytes(out), oracle.pack(ref, 0, grads).view(np.uint8).reshape(-1))
+    plan.destroy()
+
+
+# --------------------------------------------------------------------------- all-gather staging
+
+def _shards_random(w, ref, rank):
+    return [wl.random_array(P, t.storage_dtype, seed=1000 * rank + i) for i, (t, P) in
+            enumerate(zip(w.tensors, ref.P))]
+
+
+@pytest.mark.parametrize("name", ["tiny", "layout500", "mixed50m", "kda_block", "hetero500"])
+def test_copy_in_matches_oracle(name):
+    print(f"[copy-in parity] workload={name}", flush=True)
+    w = wl.get(name)
+    ref = oracle.plan(w.descs(), w.world)
+    plan = fp.plan_buckets(w.descs(), w.world)
+    ranks = range(w.world) if w.world <= 4 else [0, 1, w.world - 1]
+    ag = Guarded(w.world * plan.B, None)
+    ag_u8 = ag.t
+    ag_ref = np.full((w.world, ref.B), POISON, np.uint8)
+    for r in ranks:
+        shards = _shards_random(w, ref, r)
+        offs = [(i + r) % 3 for i in range(len(shards))]
+        fp.all_gather_copy_in(plan, r, [to_dev(s, t.storage_dtype, o) for s, t, o in
+                                        zip(shards, w.tensors, offs)], ag_u8)
+        oracle.copy_in(ref, r, shards, ag_ref)
+    torch.cuda.synchronize()
+    got = ag.result().reshape(w.world, -1)
+    assert np.array_equal(got, ag_ref), "copy-in rows differ (untouched rows must keep the poison)"
+    plan.destroy()
+
+
+@pytest.mark.parametrize("name", ["tiny", "layout500", "kda_block", "hetero500"])
+def test_copy_out_matches_oracle(name):
+    print(f"[copy-out parity] workload={name}", flush=True)
+    w = wl.get(name)
+    ref = oracle.plan(w.descs(), w.world)
+    plan = fp.plan_buckets(w.descs(), w.world)
+    gathered = np.random.default_rng(7).integers(0, 256, size=w.world * ref.B, dtype=np.uint8)
+    ag = torch.from_numpy(gathered.copy()).to(DEV)
+    outs = [Guarded(t.numel, t.param_dtype, i % 3) for i, t in enumerate(w.tensors)]
+    fp.all_gather_copy_out(plan, ag, [o.t for o in outs])
+    torch.cuda.synchronize()
+    wants = oracle.copy_out(ref, gathered)
+    for i, (o, want) in enumerate(zip(outs, wants)):
+        assert np.array_equal(o.result(), want.view(np.uint8)), f"param {i} differs"
+    plan.destroy()
+
+
+@pytest.mark.parametrize("name", ["tiny", "mixed50m", "hetero500"])
+def test_copy_in_all_gather_copy_out_round_trip(name):
+    """copy-out(all-gather(copy-in(shards of X))) == cast(X), storage -> param dtype."""
+    print(f"[round trip] workload={name}", flush=True)
+    w = wl.get(name)
+    ref = oracle.plan(w.descs(), w.world)
+    plan = fp.plan_buckets(w.descs(), w.world)
+    params = wl.make_params(w)
+    ag = torch.empty(w.world * plan.B, dtype=torch.uint8, device=DEV)
+    x_dev = [to_dev(x, t.storage_dtype) for x, t in zip(params, w.tensors)]
+    for r in range(w.world):
+        shards = []
+        for i, (x, t) in enumerate(zip(x_dev, w.tensors)):
+            P = ref.P[i]
+            s = torch.zeros(P, dtype=x.dtype, device=DEV)
+            v = max(0, min(P, t.numel - r * P))
+            s[:v] = x[r * P: r * P + v]
+            shards.append(s)
+        fp.all_gather_copy_in(plan, r, shards, ag)
+    outs = [torch.empty(t.numel, dtype=fp.TORCH_DTYPE[t.param_dtype], device=DEV) for t in w.tensors]
+    fp.all_gather_copy_out(plan, ag, outs)
+    torch.cuda.synchronize()
+    for i, (o, x, t) in enumerate(zip(outs, params, w.tensors)):
+        want = oracle.convert(x, t.storage_dtype, t.param_dtype)
+        assert np.array_equal(host_bytes(o), want.view(np.uint8)), f"param {i} differs after the round trip"
+    plan.destroy()

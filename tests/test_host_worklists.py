@@ -1,0 +1,135 @@
+"""Host checks of the library's planner and work lists (no GPU needed).
+
+* The planner behind the C ABI (fsdppack_plan.cpp) agrees with the oracle's
+  planner on every layout: buckets, members, P, O, S, A and B.
+* A sanitizer build of the same planner (tests/native/worklist_check.cpp)
+  verifies the bounds invariants the HIP kernel relies on -- every segment
+  reads and writes inside its buffers and the items cover every destination
+  byte exactly once -- for the five workloads and for random layouts, at
+  several work-item sizes.
+* Argument errors are reported synchronously with the documented codes.
+"""
+import os
+import random
+import subprocess
+
+import pytest
+
+import oracle
+import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+fp = pytest.importorskip("fsdp2_mixed_dtype_amd")
+BF16, FP32 = 1, 2
+
+
+@pytest.fixture(scope="module")
+def checker(tmp_path_factory):
+    exe = str(tmp_path_factory.mktemp("wlc") / "worklist_check")
+    subprocess.check_call(["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+                           "-fno-omit-frame-pointer", "-I", os.path.join(ROOT, "include"),
+                           os.path.join(ROOT, "tests", "native", "worklist_check.cpp"),
+                           os.path.join(ROOT, "fsdp2_mixed_dtype_amd", "csrc", "fsdppack_plan.cpp"),
+                           "-o", exe])
+    return exe
+
+
+def _run(exe, descs, W, item_bytes):
+    text = f"{W} {item_bytes} {len(descs)}\n" + "".join(" ".join(str(int(x)) for x in d) + "\n" for d in descs)
+    res = subprocess.run([exe], input=text, capture_output=True, text=True, timeout=600)
+    assert res.returncode == 0 and res.stdout.startswith("OK"), res.stdout + res.stderr[-3000:]
+
+
+def _random_layout(rng):
+    W = rng.choice([1, 2, 3, 4, 7, 8, 16, 128, 300])
+    n = rng.randint(0, 12)
+    descs = []
+    for _ in range(n):
+        dim0 = rng.choice([0, 1, 2, 3, W - 1, W, W + 1, rng.randint(1, 5 * W + 3)])
+        inner = rng.choice([0, 1, 2, 3, 5, 8, 64, 33]) if dim0 else rng.randint(0, 4)
+        descs.append((max(dim0, 0), inner, rng.choice([BF16, FP32]), rng.choice([0, BF16, FP32]),
+                      rng.choice([BF16, FP32]), rng.choice([BF16, FP32])))
+    return descs, W
+
+
+@pytest.mark.parametrize("name", list(wl.WORKLOADS))
+def test_worklists_in_bounds_workloads(checker, name):
+    w = wl.get(name)
+    for item_bytes in (65536, 4096 + 16):
+        _run(checker, w.descs(), w.world, item_bytes)
+
+
+def test_worklists_in_bounds_random(checker):
+    rng = random.Random(1234)
+    for _ in range(150):
+        descs, W = _random_layout(rng)
+        _run(checker, descs, W, rng.choice([256, 272, 1024, 65536]))
+
+
+def _oracle_matches(descs, W):
+    p = fp.plan_buckets(descs, W)
+    o = oracle.plan(descs, W)
+    assert [(b.dtype, list(b.members), list(b.P), list(b.O), b.S) for b in p.buckets] == \
+           [(b.dtype, b.members, b.P, b.O, b.S) for b in o.buckets]
+    assert (p.B, list(p.A), list(p.P)) == (o.B, o.A, o.P)
+    p.destroy()
+
+
+@pytest.mark.parametrize("name", list(wl.WORKLOADS))
+def test_abi_planner_matches_oracle_workloads(name):
+    w = wl.get(name)
+    _oracle_matches(w.descs(), w.world)
+
+
+def test_abi_planner_matches_oracle_random():
+    rng = random.Random(99)
+    for _ in range(300):
+        descs, W = _random_layout(rng)
+        _oracle_matches(descs, W)
+
+
+def test_planner_errors():
+    with pytest.raises(fp.FsdpPackError) as e:
+        fp.plan_buckets([(4, 4, FP32, 0, FP32, FP32)], 0)
+    assert e.value.code == -1
+    with pytest.raises(fp.FsdpPackError) as e:
+        fp.plan_buckets([(4, 4, 3, 0, FP32, FP32)], 2)
+    assert e.value.code == -2
+    with pytest.raises(fp.FsdpPackError) as e:
+        fp.plan_buckets([(4, 4, FP32, 7, FP32, FP32)], 2)
+    assert e.value.code == -2
+    with pytest.raises(fp.FsdpPackError) as e:
+        fp.plan_buckets([(-1, 4, FP32, 0, FP32, FP32)], 2)
+    assert e.value.code == -1
+    with pytest.raises(fp.FsdpPackError) as e:
+        fp.plan_buckets([(1 << 40, 1 << 30, FP32, 0, FP32, FP32)], 2)
+    assert e.value.code == -1
+    empty = fp.plan_buckets([], 3)
+    assert empty.buckets == () and empty.B == 0
+    empty.destroy()
+
+
+def test_compute_call_argument_errors_before_any_gpu_work():
+    # all of these are rejected on the host, so they run without a GPU
+    import ctypes
+    L = fp.lib()
+    p = fp.plan_buckets([(4, 4, FP32, 0, FP32, BF16), (3, 1, BF16, 0, FP32, BF16)], 2)
+    ptrs = (ctypes.c_void_p * 2)(0x1000, 0x2002)
+    assert L.fsdppack_pack_reduce_scatter_input(p.handle, 5, ptrs, 0x4000, None) == -1
+    assert L.fsdppack_pack_reduce_scatter_input(p.handle, 0, None, 0x4000, None) == -1
+    assert "grads is NULL" in L.fsdppack_last_error().decode()
+    assert L.fsdppack_pack_reduce_scatter_input(p.handle, 0, ptrs, 0x4002, None) == -1       # misaligned out
+    bad = (ctypes.c_void_p * 2)(0x1001, 0x2002)
+    assert L.fsdppack_pack_reduce_scatter_input(p.handle, 0, bad, 0x4000, None) == -1         # misaligned grad
+    assert "grads[0]" in L.fsdppack_last_error().decode()
+    nul = (ctypes.c_void_p * 2)(0, 0x2002)
+    assert L.fsdppack_pack_reduce_scatter_input(p.handle, 0, nul, 0x4000, None) == -1         # NULL member
+    assert L.fsdppack_all_gather_copy_in(p.handle, 2, ptrs, 0x4000, None) == -1               # rank out of range
+    assert L.fsdppack_all_gather_copy_in(p.handle, -1, ptrs, 0x4000, None) == -1
+    assert L.fsdppack_all_gather_copy_in(p.handle, 0, ptrs, 0x4002, None) == -1               # misaligned row
+    assert L.fsdppack_all_gather_copy_out(p.handle, 0x4000, None, None) == -1
+    assert L.fsdppack_plan_bucket(p.handle, 3, None, None, None, None, None, None) == -1
+    assert L.fsdppack_plan_bucket(None, 0, None, None, None, None, None, None) == -5
+    assert L.fsdppack_pack_reduce_scatter_input(None, 0, ptrs, 0x4000, None) == -5
+    p.destroy()
+    assert fp.counters()[0] == 0           # nothing was launched

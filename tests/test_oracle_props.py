@@ -79,7 +79,7 @@ def test_size_and_roundtrip_identities(layout):
             assert np.array_equal(g.view(np.uint8), want.view(np.uint8))
     # copy-out(all-gather(copy-in(shards))) == cast(full params), storage -> param dtype
     params = wl.make_params(w)
-    ag = np.zeros((W, pl.B), np.uint8)
+    ag = np.full((W, pl.B), 0xAB, np.uint8)        # poisoned: copy-in must write every byte
     for r in range(W):
         oracle.copy_in(pl, r, [oracle.shard(pl, i, params[i], r) for i in range(len(params))], ag)
     full = oracle.copy_out(pl, ag)
