@@ -11,6 +11,10 @@ Functions (same names as the C ABI without the ``fsdppack_`` prefix):
   pack_reduce_scatter_input(plan, bucket, grads, out, stream=None)
   all_gather_copy_in(plan, rank, shards, ag_out, stream=None)
   all_gather_copy_out(plan, ag, params, stream=None)
+
+The tensor lists may also be given as a PointerArray from prepare_grads /
+prepare_shards / prepare_params: validated once and reused across calls, the
+way a training loop reuses its gradient and shard buffers every step.
 """
 from __future__ import annotations
 
@@ -176,18 +180,66 @@ def _ptr_array(ptrs):
     return (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
 
 
+class PointerArray:
+    """Device pointers of a plan's gradients, shards or parameters, validated
+    once (dtype, size, contiguity, device) and reusable across calls.  Keeps
+    the tensors alive."""
+
+    def __init__(self, plan: Plan, kind: str, tensors, ptrs):
+        self.plan_handle = plan.handle.value
+        self.kind = kind
+        self.tensors = list(tensors)
+        self.array = _ptr_array(ptrs)
+
+
+def prepare_grads(plan: Plan, grads) -> PointerArray:
+    """Gradients by parameter index (grad dtype, numel elements); None allowed
+    for parameters that are never packed."""
+    if len(grads) != plan.n:
+        raise ValueError(f"grads: expected {plan.n} entries, got {len(grads)}")
+    ptrs = [_ptr(g, plan.descs[i].grad_dtype, plan.numel[i], f"grads[{i}]") for i, g in enumerate(grads)]
+    return PointerArray(plan, "grads", grads, ptrs)
+
+
+def prepare_shards(plan: Plan, shards) -> PointerArray:
+    """Padded local shards by parameter index (storage dtype, P elements)."""
+    if len(shards) != plan.n:
+        raise ValueError(f"shards: expected {plan.n} entries, got {len(shards)}")
+    ptrs = [_ptr(s, plan.descs[i].storage_dtype, plan.P[i], f"shards[{i}]") for i, s in enumerate(shards)]
+    return PointerArray(plan, "shards", shards, ptrs)
+
+
+def prepare_params(plan: Plan, params) -> PointerArray:
+    """Full parameters by index (param dtype, numel elements)."""
+    if len(params) != plan.n:
+        raise ValueError(f"params: expected {plan.n} entries, got {len(params)}")
+    ptrs = [_ptr(p, plan.descs[i].param_dtype, plan.numel[i], f"params[{i}]") for i, p in enumerate(params)]
+    return PointerArray(plan, "params", params, ptrs)
+
+
+def _prepared(plan: Plan, arr, kind: str, make):
+    if isinstance(arr, PointerArray):
+        if arr.kind != kind or arr.plan_handle != plan.handle.value:
+            raise ValueError(f"pointer array was prepared for {arr.kind} of another plan")
+        return arr.array
+    return make(plan, arr).array
+
+
 def pack_reduce_scatter_input(plan: Plan, bucket: int, grads, out, stream=None):
     """Fill `out` ([W, S] of the bucket's reduction dtype) with every member's
     gradient chunked along dim 0, cast and zero-padded.  `grads` is indexed by
     parameter (unit order); entries of non-members may be None."""
     b = plan.buckets[bucket]
-    members = set(b.members)
-    ptrs = [_ptr(g, plan.descs[i].grad_dtype, plan.numel[i], f"grads[{i}]") if i in members else 0
-            for i, g in enumerate(grads)]
-    if len(ptrs) != plan.n:
-        raise ValueError(f"grads: expected {plan.n} entries, got {len(ptrs)}")
+    if isinstance(grads, PointerArray):
+        arr = _prepared(plan, grads, "grads", prepare_grads)
+    else:
+        members = set(b.members)
+        if len(grads) != plan.n:
+            raise ValueError(f"grads: expected {plan.n} entries, got {len(grads)}")
+        arr = _ptr_array([_ptr(g, plan.descs[i].grad_dtype, plan.numel[i], f"grads[{i}]") if i in members else 0
+                          for i, g in enumerate(grads)])
     optr = _ptr(out, b.dtype, plan.world * b.S, "out")
-    _check(lib().fsdppack_pack_reduce_scatter_input(plan.handle, bucket, _ptr_array(ptrs), optr, _stream(stream)))
+    _check(lib().fsdppack_pack_reduce_scatter_input(plan.handle, bucket, arr, optr, _stream(stream)))
     return out
 
 
@@ -201,21 +253,17 @@ def _bytes_ptr(t, nbytes: int, what: str):
 def all_gather_copy_in(plan: Plan, rank: int, shards, ag_out, stream=None):
     """Write row `rank` of the [W, B]-byte all-gather buffer from the rank's
     padded shards (P elements each, storage dtype)."""
-    if len(shards) != plan.n:
-        raise ValueError(f"shards: expected {plan.n} entries, got {len(shards)}")
-    ptrs = [_ptr(s, plan.descs[i].storage_dtype, plan.P[i], f"shards[{i}]") for i, s in enumerate(shards)]
+    arr = _prepared(plan, shards, "shards", prepare_shards)
     aptr = _bytes_ptr(ag_out, plan.world * plan.B, "ag_out")
-    _check(lib().fsdppack_all_gather_copy_in(plan.handle, int(rank), _ptr_array(ptrs), aptr, _stream(stream)))
+    _check(lib().fsdppack_all_gather_copy_in(plan.handle, int(rank), arr, aptr, _stream(stream)))
     return ag_out
 
 
 def all_gather_copy_out(plan: Plan, ag, params, stream=None):
     """Rebuild every full parameter (param dtype) from the gathered buffer."""
-    if len(params) != plan.n:
-        raise ValueError(f"params: expected {plan.n} entries, got {len(params)}")
-    ptrs = [_ptr(p, plan.descs[i].param_dtype, plan.numel[i], f"params[{i}]") for i, p in enumerate(params)]
+    arr = _prepared(plan, params, "params", prepare_params)
     aptr = _bytes_ptr(ag, plan.world * plan.B, "ag")
-    _check(lib().fsdppack_all_gather_copy_out(plan.handle, aptr, _ptr_array(ptrs), _stream(stream)))
+    _check(lib().fsdppack_all_gather_copy_out(plan.handle, aptr, arr, _stream(stream)))
     return params
 
 

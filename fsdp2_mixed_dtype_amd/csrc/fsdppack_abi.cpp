@@ -67,8 +67,10 @@ int upload_list(WorkList &wl)
         if ((e = hipMalloc(reinterpret_cast<void **>(&wl.d_segs), sb)) != hipSuccess) return hip_fail(e, "hipMalloc(segments)");
         if ((e = hipMemcpy(wl.d_segs, wl.segs.data(), sb, hipMemcpyHostToDevice)) != hipSuccess) return hip_fail(e, "hipMemcpy(segments)");
     }
-    if ((e = hipMalloc(reinterpret_cast<void **>(&wl.d_items), ib)) != hipSuccess) return hip_fail(e, "hipMalloc(items)");
-    if ((e = hipMemcpy(wl.d_items, wl.items.data(), ib, hipMemcpyHostToDevice)) != hipSuccess) return hip_fail(e, "hipMemcpy(items)");
+    if (ib) {
+        if ((e = hipMalloc(reinterpret_cast<void **>(&wl.d_items), ib)) != hipSuccess) return hip_fail(e, "hipMalloc(items)");
+        if ((e = hipMemcpy(wl.d_items, wl.items.data(), ib, hipMemcpyHostToDevice)) != hipSuccess) return hip_fail(e, "hipMemcpy(items)");
+    }
     return FSDPPACK_OK;
 }
 
@@ -103,11 +105,13 @@ int acquire_table(PtrCache &c, const std::vector<uint64_t> &key, hipStream_t str
     hipError_t e;
     for (PtrSlot &s : c.slots) {
         if (s.live && s.key == key) {
-            if (s.stream != stream) {
-                // another stream used this table last: order after that use
-                if ((e = hipStreamWaitEvent(stream, static_cast<hipEvent_t>(s.used), 0)) != hipSuccess)
+            bool ordered = false;
+            for (void *st : s.streams) ordered |= (st == stream);
+            if (!ordered) {
+                // first use on this stream: wait once for the upload
+                if ((e = hipStreamWaitEvent(stream, static_cast<hipEvent_t>(s.ready), 0)) != hipSuccess)
                     return hip_fail(e, "hipStreamWaitEvent");
-                s.stream = stream;
+                s.streams.push_back(stream);
             }
             s.last_use = ++c.clock;
             g_counters[2]++;
@@ -122,9 +126,9 @@ int acquire_table(PtrCache &c, const std::vector<uint64_t> &key, hipStream_t str
         victim = &c.slots[0];
         for (PtrSlot &s : c.slots)
             if (s.last_use < victim->last_use) victim = &s;
-        // the kernels that read this table (and its upload) must be done
-        if ((e = hipEventSynchronize(static_cast<hipEvent_t>(victim->used))) != hipSuccess)
-            return hip_fail(e, "hipEventSynchronize");
+        // kernels still reading the evicted table (on any stream) and its
+        // staging upload must be done before either is overwritten
+        if ((e = hipDeviceSynchronize()) != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
     }
     const size_t bytes = key.size() * sizeof(uint64_t);
     if (victim->d_table == nullptr) {
@@ -133,15 +137,13 @@ int acquire_table(PtrCache &c, const std::vector<uint64_t> &key, hipStream_t str
         hipEvent_t ev;
         if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) return hip_fail(e, "hipEventCreate");
         victim->ready = ev;
-        if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) return hip_fail(e, "hipEventCreate");
-        victim->used = ev;
     }
     std::memcpy(victim->h_stage, key.data(), bytes);
     if ((e = hipMemcpyAsync(victim->d_table, victim->h_stage, bytes, hipMemcpyHostToDevice, stream)) != hipSuccess)
         return hip_fail(e, "hipMemcpyAsync(pointer table)");
     if ((e = hipEventRecord(static_cast<hipEvent_t>(victim->ready), stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     victim->key = key;
-    victim->stream = stream;
+    victim->streams.assign(1, stream);
     victim->live = true;
     victim->last_use = ++c.clock;
     g_counters[1]++;
@@ -149,7 +151,7 @@ int acquire_table(PtrCache &c, const std::vector<uint64_t> &key, hipStream_t str
     return FSDPPACK_OK;
 }
 
-// Run one work list: table lookup, one kernel launch, mark the table used.
+// Run one work list: table lookup, then one kernel launch.
 int run_list(fsdppack_plan *p, WorkList &wl, size_t cache_index, const std::vector<uint64_t> &key, char *base,
              void *stream, const char *what)
 {
@@ -169,8 +171,6 @@ int run_list(fsdppack_plan *p, WorkList &wl, size_t cache_index, const std::vect
     g_next_start = g_next_stop = nullptr;
     const int le = launch_segments(args, stream, ev0, ev1);
     if (le != 0) return hip_fail(static_cast<hipError_t>(le), what);
-    hipError_t e = hipEventRecord(static_cast<hipEvent_t>(slot->used), s);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
     g_counters[0]++;
     if (trace_on())
         std::fprintf(stderr, "fsdppack: %s: %d workgroups, %lld bytes read, %lld bytes written\n", what,
@@ -323,12 +323,9 @@ void fsdppack_plan_destroy(fsdppack_plan *plan)
     if (!plan_ok(plan)) return;
     {
         std::lock_guard<std::mutex> lock(plan->mu);
+        if (plan->uploaded) (void)hipDeviceSynchronize();   // no kernel may still read the tables
         for (PtrCache &c : plan->caches) {
             for (PtrSlot &s : c.slots) {
-                if (s.used) {
-                    (void)hipEventSynchronize(static_cast<hipEvent_t>(s.used));
-                    (void)hipEventDestroy(static_cast<hipEvent_t>(s.used));
-                }
                 if (s.ready) (void)hipEventDestroy(static_cast<hipEvent_t>(s.ready));
                 if (s.d_table) (void)hipFree(s.d_table);
                 if (s.h_stage) (void)hipHostFree(s.h_stage);

@@ -10,10 +10,10 @@
 // reached through a per-call pointer table; the other side is an offset into
 // the call's single packed buffer.
 //
-// Work is split into *items*, one per workgroup: item k starts at
-// (segment, element offset) items[k] and ends where items[k+1] starts, so a
-// workgroup may cover part of one large segment or many small ones.  This
-// array is the prefix map from workgroup to (tensor, rank chunk).
+// Work is split into *items*, one per workgroup: item k covers everything
+// from one (segment, element offset) to the next, so a workgroup may cover
+// part of one large segment or many small ones.  This array is the prefix
+// map from workgroup to (tensor, rank chunk).
 #pragma once
 
 #include <cstdint>
@@ -47,17 +47,38 @@ struct Seg {
 };
 static_assert(sizeof(Seg) == 40, "Seg layout is shared with the device");
 
+// One work item: the elements from (seg_a, off_a) up to, not including,
+// (seg_b, off_b) of the segment list, where (seg_b, off_b) may be
+// (n_segs, 0), the end of the list.
 struct Item {
-    int32_t seg;       // first segment of the item
-    int32_t pad_;
-    int64_t off;       // element offset inside that segment
+    int32_t seg_a;
+    int32_t seg_b;
+    int64_t off_a;
+    int64_t off_b;
+    int64_t pad_;
 };
-static_assert(sizeof(Item) == 16, "Item layout is shared with the device");
+static_assert(sizeof(Item) == 32, "Item layout is shared with the device");
+
+// Workgroups are dealt to the GPU's XCDs round-robin (workgroup b runs on XCD
+// b % kXcds), and each XCD has its own L2.  Item b is therefore stored at
+// item_slot(b): the workgroups of one XCD read consecutive records, so one
+// 128-byte line serves four workgroups of the same XCD instead of being
+// fetched by several XCDs.  A bijection on [0, n); only locality depends on
+// the XCD count being right.
+constexpr int32_t kXcds = 8;
+#if defined(__HIP__)
+__attribute__((host, device))   // shared by the host planner and the kernel
+#endif
+inline int32_t item_slot(int32_t b, int32_t n)
+{
+    const int32_t per = n / kXcds;
+    return b < per * kXcds ? (b % kXcds) * per + b / kXcds : b;
+}
 
 // Arguments of one launch of the grouped segment kernel.
 struct LaunchArgs {
     const Seg *segs;
-    const Item *items;       // n_items + 1 entries (the last is a sentinel)
+    const Item *items;       // n_items records, item b at item_slot(b, n_items)
     const uint64_t *table;   // device pointer table, indexed by Seg::slot
     char *base;              // the call's packed buffer (destination or source)
     int32_t n_items;

@@ -268,17 +268,16 @@ __device__ __forceinline__ void run_segment(const Seg &g, int64_t lo, int64_t hi
     }
 }
 
-// One workgroup per item.  Item k covers everything from items[k] up to (not
-// including) items[k+1]; the host guarantees items[n_items] = {n_segs, 0},
-// so the loop never reads past the segment array.
+// One workgroup per item.  An item's end is either inside a segment
+// (off_b > 0) or the start of segment seg_b (off_b == 0, possibly the end of
+// the list), so the loop never reads past the segment array.
 __device__ __forceinline__ void run_item(const LaunchArgs &a, int32_t k)
 {
-    const Item first = a.items[k];
-    const Item last = a.items[k + 1];
-    for (int32_t s = first.seg; s < last.seg || (s == last.seg && last.off > 0); ++s) {
+    const Item it = a.items[item_slot(k, a.n_items)];
+    for (int32_t s = it.seg_a; s < it.seg_b || (s == it.seg_b && it.off_b > 0); ++s) {
         const Seg g = a.segs[s];
-        const int64_t lo = (s == first.seg) ? first.off : 0;
-        const int64_t hi = (s == last.seg) ? last.off : g.len;
+        const int64_t lo = (s == it.seg_a) ? it.off_a : 0;
+        const int64_t hi = (s == it.seg_b) ? it.off_b : g.len;
         if (hi > lo) run_segment(g, lo, hi, a.table, a.base);
     }
 }

@@ -36,7 +36,10 @@ constexpr int64_t kMaxBytes = INT64_MAX / 4;
 void build_items(const std::vector<Seg> &segs, const std::vector<int64_t> &vpos, int64_t item_bytes,
                  std::vector<Item> &items)
 {
-    items.clear();
+    // item starts in list order: a new item wherever the virtual position
+    // crosses a multiple of item_bytes
+    struct Start { int32_t seg; int64_t off; };
+    std::vector<Start> starts;
     int64_t current = -1;   // virtual window of the item being filled
     for (size_t i = 0; i < segs.size(); ++i) {
         const Seg &g = segs[i];
@@ -47,11 +50,20 @@ void build_items(const std::vector<Seg> &segs, const std::vector<int64_t> &vpos,
         for (int64_t k = k0; k <= k1; ++k) {
             if (k == current) continue;   // the open item runs on into this segment
             const int64_t off = (k == k0) ? 0 : (k * item_bytes - a) / esz;
-            items.push_back(Item{static_cast<int32_t>(i), 0, off});
+            starts.push_back(Start{static_cast<int32_t>(i), off});
             current = k;
         }
     }
-    items.push_back(Item{static_cast<int32_t>(segs.size()), 0, 0});
+    const int32_t n = static_cast<int32_t>(starts.size());
+    items.assign(n, Item{});
+    for (int32_t b = 0; b < n; ++b) {
+        Item it{};
+        it.seg_a = starts[b].seg;
+        it.off_a = starts[b].off;
+        if (b + 1 < n) { it.seg_b = starts[b + 1].seg; it.off_b = starts[b + 1].off; }
+        else { it.seg_b = static_cast<int32_t>(segs.size()); it.off_b = 0; }
+        items[item_slot(b, n)] = it;
+    }
 }
 
 int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, int64_t item_bytes,

@@ -20,13 +20,13 @@ namespace fsdppack {
 // A work list and, once uploaded, its device copy.
 struct WorkList {
     std::vector<Seg> segs;
-    std::vector<Item> items;          // n_items + 1 entries
+    std::vector<Item> items;          // n_items records, stored by item_slot()
     int64_t dst_bytes = 0;            // bytes the list writes
     int64_t src_bytes = 0;            // bytes the list reads
     // device side (owned by the plan)
     Seg *d_segs = nullptr;
     Item *d_items = nullptr;
-    int32_t n_items() const { return static_cast<int32_t>(items.size()) - 1; }
+    int32_t n_items() const { return static_cast<int32_t>(items.size()); }
 };
 
 struct BucketPlan {
@@ -40,14 +40,16 @@ struct BucketPlan {
 // Per-call pointer tables, cached on the device by content: the same grads /
 // shards / params pointers (the usual case from step to step) reuse an
 // uploaded table; a new set is staged through pinned host memory and copied
-// on the caller's stream.
+// on the caller's stream.  A steady-state call records no event: a slot is
+// only rewritten after a device-wide synchronisation (eviction is rare), and
+// a stream that first uses a slot uploaded on another stream waits once for
+// the upload.
 struct PtrSlot {
     std::vector<uint64_t> key;
     uint64_t *d_table = nullptr;
     uint64_t *h_stage = nullptr;      // pinned host staging of this slot
     void *ready = nullptr;            // hipEvent_t: upload finished
-    void *used = nullptr;             // hipEvent_t: last kernel reading it finished
-    void *stream = nullptr;           // stream the upload was enqueued on
+    std::vector<void *> streams;      // streams ordered after the upload
     uint64_t last_use = 0;
     bool live = false;
 };

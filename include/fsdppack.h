@@ -43,8 +43,9 @@
  *    where it is never dereferenced (a parameter with zero elements, or one
  *    outside the bucket being packed).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every compute
- *    call enqueues exactly one kernel launch on it and returns without
- *    waiting; argument errors are reported synchronously and enqueue nothing.
+ *    call enqueues one kernel launch on it (none when there is nothing to
+ *    write) and returns without waiting; argument errors are reported
+ *    synchronously and enqueue nothing.
  *  - Every call returns FSDPPACK_OK (0) or a negative error code, and on
  *    error leaves a message for fsdppack_last_error() (per thread).  No
  *    exception crosses the ABI.
@@ -52,6 +53,12 @@
  *    streams; its device tables are uploaded on the first compute call that
  *    needs them (a synchronous copy) on the device current at that time, and
  *    the plan may only be used on that device afterwards.
+ *  - Per-call pointers reach the kernel through device tables cached by
+ *    content, 16 per operation (per bucket for the pack).  A call with a new
+ *    set of pointers uploads one asynchronously on `stream`; a 17th distinct
+ *    set evicts the least recently used table after a device-wide
+ *    synchronisation.  Calls with a known set record no event and upload
+ *    nothing.
  */
 #ifndef FSDPPACK_H
 #define FSDPPACK_H
@@ -154,8 +161,9 @@ int fsdppack_all_gather_copy_in(const fsdppack_plan *plan, int32_t rank, const v
 int fsdppack_all_gather_copy_out(const fsdppack_plan *plan, const void *ag, void *const *params,
                                  void *stream);
 
-/* Free a plan and its device tables (waits for work still using them).
- * NULL is a no-op. */
+/* Free a plan and its device tables.  Synchronises the device first if the
+ * plan was ever used there (no kernel may still read its tables).  NULL is a
+ * no-op. */
 void fsdppack_plan_destroy(fsdppack_plan *plan);
 
 /* Message of the last failed call on this thread ("" if none). */

@@ -4,8 +4,9 @@
 // into this program with the address and undefined-behaviour sanitizers) and
 // checks, for every work list the kernels would run, the invariants the
 // grouped segment kernel relies on:
-//  * the item array is a sentinel-terminated, strictly increasing list of
-//    (segment, offset) starts inside the segment array;
+//  * the item records are stored by a bijective slot map, each covers a
+//    non-empty range inside the segment array, and consecutive items meet
+//    exactly (the last one ends the list);
 //  * every segment's destination range lies inside its destination buffer,
 //    its source range (the `valid` prefix) inside its source buffer, its
 //    pointer-table slot inside the table, and its dtypes are supported;
@@ -40,23 +41,38 @@ static std::string g_fail;
 // dst_size(seg): bytes of the buffer the segment writes into;
 // src_size(seg): bytes of the buffer it reads from.
 template <typename DstSize, typename SrcSize>
-static bool check_list(const char *name, const WorkList &wl, int32_t n, DstSize dst_size, SrcSize src_size,
+static bool check_list(const char *name, const WorkList &wl, int32_t nparams, DstSize dst_size, SrcSize src_size,
                        std::vector<std::vector<std::pair<int64_t, int64_t>>> &written)
 {
     const int64_t nseg = static_cast<int64_t>(wl.segs.size());
-    CHECK(!wl.items.empty(), "%s: empty item array", name);
-    const Item &sent = wl.items.back();
-    CHECK(sent.seg == nseg && sent.off == 0, "%s: bad sentinel (%d,%lld)", name, sent.seg, (long long)sent.off);
-    for (size_t k = 0; k + 1 < wl.items.size(); ++k) {
-        const Item &a = wl.items[k], &b = wl.items[k + 1];
-        CHECK(a.seg >= 0 && a.seg < nseg, "%s: item %zu segment %d out of range", name, k, a.seg);
-        CHECK(a.off >= 0 && a.off < wl.segs[a.seg].len, "%s: item %zu offset out of range", name, k);
-        CHECK(a.seg < b.seg || (a.seg == b.seg && a.off < b.off), "%s: items %zu,%zu not increasing", name, k, k + 1);
+    const int32_t n = static_cast<int32_t>(wl.items.size());
+    // item_slot must be a bijection on [0, n)
+    std::vector<uint8_t> hit(n, 0);
+    for (int32_t b = 0; b < n; ++b) {
+        const int32_t slot = item_slot(b, n);
+        CHECK(slot >= 0 && slot < n && !hit[slot], "%s: item_slot not a bijection at %d", name, b);
+        hit[slot] = 1;
+    }
+    for (int32_t b = 0; b < n; ++b) {
+        const Item &it = wl.items[item_slot(b, n)];
+        CHECK(it.seg_a >= 0 && it.seg_a < nseg, "%s: item %d start segment %d out of range", name, b, it.seg_a);
+        CHECK(it.off_a >= 0 && it.off_a < wl.segs[it.seg_a].len, "%s: item %d start offset out of range", name, b);
+        CHECK(it.seg_b >= 0 && it.seg_b <= nseg, "%s: item %d end segment out of range", name, b);
+        CHECK(it.seg_b < nseg ? (it.off_b >= 0 && it.off_b < wl.segs[it.seg_b].len) : it.off_b == 0,
+              "%s: item %d end offset out of range", name, b);
+        CHECK(it.seg_a < it.seg_b || (it.seg_a == it.seg_b && it.off_a < it.off_b), "%s: item %d empty or reversed",
+              name, b);
+        if (b + 1 < n) {
+            const Item &nx = wl.items[item_slot(b + 1, n)];
+            CHECK(nx.seg_a == it.seg_b && nx.off_a == it.off_b, "%s: item %d does not end where %d starts", name, b, b + 1);
+        } else {
+            CHECK(it.seg_b == nseg && it.off_b == 0, "%s: last item does not end the list", name);
+        }
     }
     for (int64_t i = 0; i < nseg; ++i) {
         const Seg &g = wl.segs[i];
         CHECK(dtype_ok(g.src_dt) && dtype_ok(g.dst_dt), "%s: segment %lld bad dtype", name, (long long)i);
-        CHECK(g.slot >= 0 && g.slot < n, "%s: segment %lld slot %d out of range", name, (long long)i, g.slot);
+        CHECK(g.slot >= 0 && g.slot < nparams, "%s: segment %lld slot %d out of range", name, (long long)i, g.slot);
         CHECK(g.len >= 0 && g.valid >= 0 && g.valid <= g.len, "%s: segment %lld bad len/valid", name, (long long)i);
         const int64_t dend = g.dst_off + g.len * dtype_bytes(g.dst_dt);
         CHECK(g.dst_off >= 0 && dend <= dst_size(g), "%s: segment %lld writes [%lld,%lld) past %lld", name,
@@ -68,14 +84,14 @@ static bool check_list(const char *name, const WorkList &wl, int32_t n, DstSize 
                   (long long)i, (long long)g.src_off, (long long)send, (long long)src_size(g));
         }
     }
-    // walk items the way the kernel does and mark written bytes
-    for (size_t k = 0; k + 1 < wl.items.size(); ++k) {
-        const Item first = wl.items[k], last = wl.items[k + 1];
-        for (int32_t s = first.seg; s < last.seg || (s == last.seg && last.off > 0); ++s) {
+    // walk items the way the kernel does and record written byte ranges
+    for (int32_t b = 0; b < n; ++b) {
+        const Item it = wl.items[item_slot(b, n)];
+        for (int32_t s = it.seg_a; s < it.seg_b || (s == it.seg_b && it.off_b > 0); ++s) {
             CHECK(s < nseg, "%s: item walk reads segment %d of %lld", name, s, (long long)nseg);
             const Seg &g = wl.segs[s];
-            const int64_t lo = (s == first.seg) ? first.off : 0;
-            const int64_t hi = (s == last.seg) ? last.off : g.len;
+            const int64_t lo = (s == it.seg_a) ? it.off_a : 0;
+            const int64_t hi = (s == it.seg_b) ? it.off_b : g.len;
             if (hi <= lo) continue;
             CHECK(hi <= g.len, "%s: range past segment end", name);
             const int64_t esz = dtype_bytes(g.dst_dt);

@@ -217,6 +217,25 @@ def test_deterministic_one_launch_and_table_reuse():
     plan.destroy()
 
 
+def test_prepared_pointer_arrays_match_tensor_lists():
+    w = wl.hetero500()
+    grads = grads_of("hetero500")
+    ref = oracle.plan(w.descs(), w.world)
+    plan = fp.plan_buckets(w.descs(), w.world)
+    g_dev = [to_dev(g, t.grad_dtype) for g, t in zip(grads, w.tensors)]
+    prepared = fp.prepare_grads(plan, g_dev)
+    for bi, b in enumerate(plan.buckets):
+        out = Guarded(w.world * b.S, b.dtype)
+        fp.pack_reduce_scatter_input(plan, bi, prepared, out.t)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.result(), oracle.pack(ref, bi, grads).view(np.uint8).reshape(-1))
+    other = fp.plan_buckets(w.descs(), w.world)
+    with pytest.raises(ValueError):
+        fp.pack_reduce_scatter_input(other, 0, prepared, out.t)      # prepared for another plan
+    other.destroy()
+    plan.destroy()
+
+
 def test_pointer_table_eviction_keeps_results_correct():
     w = wl.custom([(37, 3), (5,), (64, 2)], [BF16, FP32, BF16], [FP32, FP32, FP32], 4)
     ref = oracle.plan(w.descs(), w.world)
