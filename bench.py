@@ -264,7 +264,7 @@ def main():
         pass
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": "segments_kernel (pack)", "bytes_per_launch": pack_bytes[dom]}
+                "kernel": "window_kernel<pack>", "bytes_per_launch": pack_bytes[dom]}
 
     # ---- CPU baseline: the oracle, as it stands, on a bounded sample of the same pack
     cpu = None

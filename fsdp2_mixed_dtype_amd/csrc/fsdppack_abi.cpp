@@ -1,7 +1,7 @@
 // fsdppack_abi.cpp -- the C ABI of libfsdppack (declared in include/fsdppack.h).
 //
 // Argument checks are synchronous and on the host; every compute call then
-// enqueues one launch of the grouped segment kernel on the caller's stream.
+// enqueues one launch of a window kernel on the caller's stream.
 // Per-call device pointers (grads, shards, params) reach the kernel through a
 // small device table cached by content (see PtrCache in fsdppack_plan.h), so
 // a training loop that passes the same buffers each step pays no upload.
@@ -45,37 +45,30 @@ bool trace_on()
     return on;
 }
 
-int64_t default_item_bytes()
-{
-    const char *v = std::getenv("FSDPPACK_ITEM_BYTES");
-    if (v != nullptr) {
-        const long long x = std::atoll(v);
-        if (x >= 256 && x % 16 == 0) return x;
-    }
-    return kItemBytes;
-}
-
 bool plan_ok(const fsdppack_plan *p) { return p != nullptr && p->magic == kPlanMagic; }
 
 bool aligned(const void *p, int64_t bytes) { return (reinterpret_cast<uintptr_t>(p) % bytes) == 0; }
 
-int upload_list(WorkList &wl)
+int upload_table(OpTable &op)
 {
-    const size_t sb = wl.segs.size() * sizeof(Seg), ib = wl.items.size() * sizeof(Item);
     hipError_t e;
-    if (sb) {
-        if ((e = hipMalloc(reinterpret_cast<void **>(&wl.d_segs), sb)) != hipSuccess) return hip_fail(e, "hipMalloc(segments)");
-        if ((e = hipMemcpy(wl.d_segs, wl.segs.data(), sb, hipMemcpyHostToDevice)) != hipSuccess) return hip_fail(e, "hipMemcpy(segments)");
+    const size_t bytes = op.members.size();
+    if (bytes) {
+        if ((e = hipMalloc(&op.d_members, bytes)) != hipSuccess) return hip_fail(e, "hipMalloc(member table)");
+        if ((e = hipMemcpy(op.d_members, op.members.data(), bytes, hipMemcpyHostToDevice)) != hipSuccess)
+            return hip_fail(e, "hipMemcpy(member table)");
     }
-    if (ib) {
-        if ((e = hipMalloc(reinterpret_cast<void **>(&wl.d_items), ib)) != hipSuccess) return hip_fail(e, "hipMalloc(items)");
-        if ((e = hipMemcpy(wl.d_items, wl.items.data(), ib, hipMemcpyHostToDevice)) != hipSuccess) return hip_fail(e, "hipMemcpy(items)");
+    const size_t cbytes = op.columns.size() * sizeof(ColumnWindow);
+    if (cbytes) {
+        if ((e = hipMalloc(&op.d_columns, cbytes)) != hipSuccess) return hip_fail(e, "hipMalloc(column map)");
+        if ((e = hipMemcpy(op.d_columns, op.columns.data(), cbytes, hipMemcpyHostToDevice)) != hipSuccess)
+            return hip_fail(e, "hipMemcpy(column map)");
     }
     return FSDPPACK_OK;
 }
 
-// Upload the plan's work lists once, on the current device; afterwards the
-// plan is bound to that device.  Caller holds plan->mu.
+// Upload the plan's member tables once, on the current device; afterwards
+// the plan is bound to that device.  Caller holds plan->mu.
 int ensure_device(fsdppack_plan *p)
 {
     int dev = -1;
@@ -88,9 +81,9 @@ int ensure_device(fsdppack_plan *p)
         return FSDPPACK_OK;
     }
     for (BucketPlan &b : p->buckets)
-        if (int rc = upload_list(b.pack)) return rc;
-    if (int rc = upload_list(p->copy_in)) return rc;
-    if (int rc = upload_list(p->copy_out)) return rc;
+        if (int rc = upload_table(b.pack)) return rc;
+    if (int rc = upload_table(p->copy_in)) return rc;
+    if (int rc = upload_table(p->copy_out)) return rc;
     p->caches.resize(p->buckets.size() + 2);
     p->device = dev;
     p->uploaded = true;
@@ -151,30 +144,28 @@ int acquire_table(PtrCache &c, const std::vector<uint64_t> &key, hipStream_t str
     return FSDPPACK_OK;
 }
 
-// Run one work list: table lookup, then one kernel launch.
-int run_list(fsdppack_plan *p, WorkList &wl, size_t cache_index, const std::vector<uint64_t> &key, char *base,
-             void *stream, const char *what)
+// Run one operation: pointer-table lookup, then one kernel launch.
+int run_op(fsdppack_plan *p, const OpTable &op, size_t cache_index, const std::vector<uint64_t> &key, char *base,
+           void *stream, const char *what)
 {
-    if (wl.n_items() <= 0) return FSDPPACK_OK;
+    if (op.n_windows <= 0) return FSDPPACK_OK;
     std::lock_guard<std::mutex> lock(p->mu);
     if (int rc = ensure_device(p)) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     PtrSlot *slot = nullptr;
     if (int rc = acquire_table(p->caches[cache_index], key, s, &slot)) return rc;
-    LaunchArgs args{};
-    args.segs = wl.d_segs;
-    args.items = wl.d_items;
+    WindowArgs args = op.args(true);
+    args.W = p->W;
     args.table = slot->d_table;
     args.base = base;
-    args.n_items = wl.n_items();
     void *ev0 = g_next_start, *ev1 = g_next_stop;
     g_next_start = g_next_stop = nullptr;
-    const int le = launch_segments(args, stream, ev0, ev1);
+    const int le = launch_windows(args, stream, ev0, ev1);
     if (le != 0) return hip_fail(static_cast<hipError_t>(le), what);
     g_counters[0]++;
     if (trace_on())
         std::fprintf(stderr, "fsdppack: %s: %d workgroups, %lld bytes read, %lld bytes written\n", what,
-                     args.n_items, static_cast<long long>(wl.src_bytes), static_cast<long long>(wl.dst_bytes));
+                     args.n_windows, static_cast<long long>(op.src_bytes), static_cast<long long>(op.dst_bytes));
     return FSDPPACK_OK;
 }
 
@@ -192,7 +183,7 @@ int fsdppack_plan_buckets(const fsdppack_param_desc *params, int32_t n, int32_t 
     std::string err;
     int rc;
     try {
-        rc = build_plan(params, n, world, default_item_bytes(), p, err);
+        rc = build_plan(params, n, world, p, err);
     } catch (const std::bad_alloc &) {
         rc = FSDPPACK_ENOMEM;
         err = "plan_buckets: out of host memory";
@@ -251,17 +242,18 @@ int fsdppack_pack_reduce_scatter_input(const fsdppack_plan *cplan, int32_t bucke
     const int64_t dsz = dtype_bytes(b.dtype);
     if (b.S > 0 && (out == nullptr || !aligned(out, dsz)))
         return fail(FSDPPACK_EINVAL, "pack_reduce_scatter_input: out is NULL or not aligned to its element size");
-    std::vector<uint64_t> key(plan->n, 0);
     for (int32_t t : b.members) {
         if (plan->numel[t] == 0) continue;
         const void *g = grads[t];
         if (g == nullptr || !aligned(g, dtype_bytes(plan->params[t].grad_dtype)))
             return fail(FSDPPACK_EINVAL, "pack_reduce_scatter_input: grads[" + std::to_string(t) +
                                              "] is NULL or not aligned to its element size");
-        key[t] = reinterpret_cast<uint64_t>(g);
     }
+    // the pack's pointer table is in member order (entry m = member m)
+    std::vector<uint64_t> key(b.pack.table_params.size());
+    for (size_t m = 0; m < key.size(); ++m) key[m] = reinterpret_cast<uint64_t>(grads[b.pack.table_params[m]]);
     try {
-        return run_list(plan, b.pack, static_cast<size_t>(bucket), key, static_cast<char *>(out), stream,
+        return run_op(plan, b.pack, static_cast<size_t>(bucket), key, static_cast<char *>(out), stream,
                         "pack_reduce_scatter_input");
     } catch (const std::bad_alloc &) {
         return fail(FSDPPACK_ENOMEM, "pack_reduce_scatter_input: out of host memory");
@@ -288,7 +280,7 @@ int fsdppack_all_gather_copy_in(const fsdppack_plan *cplan, int32_t rank, const 
     }
     char *row = static_cast<char *>(ag_out) + static_cast<int64_t>(rank) * plan->B;
     try {
-        return run_list(plan, plan->copy_in, plan->buckets.size(), key, row, stream, "all_gather_copy_in");
+        return run_op(plan, plan->copy_in, plan->buckets.size(), key, row, stream, "all_gather_copy_in");
     } catch (const std::bad_alloc &) {
         return fail(FSDPPACK_ENOMEM, "all_gather_copy_in: out of host memory");
     }
@@ -311,7 +303,7 @@ int fsdppack_all_gather_copy_out(const fsdppack_plan *cplan, const void *ag, voi
         key[t] = reinterpret_cast<uint64_t>(d);
     }
     try {
-        return run_list(plan, plan->copy_out, plan->buckets.size() + 1, key,
+        return run_op(plan, plan->copy_out, plan->buckets.size() + 1, key,
                         const_cast<char *>(static_cast<const char *>(ag)), stream, "all_gather_copy_out");
     } catch (const std::bad_alloc &) {
         return fail(FSDPPACK_ENOMEM, "all_gather_copy_out: out of host memory");
@@ -331,15 +323,15 @@ void fsdppack_plan_destroy(fsdppack_plan *plan)
                 if (s.h_stage) (void)hipHostFree(s.h_stage);
             }
         }
-        auto free_list = [](WorkList &wl) {
-            if (wl.d_segs) (void)hipFree(wl.d_segs);
-            if (wl.d_items) (void)hipFree(wl.d_items);
-            wl.d_segs = nullptr;
-            wl.d_items = nullptr;
+        auto free_table = [](OpTable &op) {
+            if (op.d_members) (void)hipFree(op.d_members);
+            if (op.d_columns) (void)hipFree(op.d_columns);
+            op.d_members = nullptr;
+            op.d_columns = nullptr;
         };
-        for (BucketPlan &b : plan->buckets) free_list(b.pack);
-        free_list(plan->copy_in);
-        free_list(plan->copy_out);
+        for (BucketPlan &b : plan->buckets) free_table(b.pack);
+        free_table(plan->copy_in);
+        free_table(plan->copy_out);
         plan->magic = 0;
     }
     delete plan;

@@ -1,7 +1,7 @@
-// fsdppack_kernels.hip -- the grouped multi-tensor segment kernel of
-// libfsdppack for gfx950 (MI355X).
+// fsdppack_kernels.hip -- the grouped multi-tensor kernels of libfsdppack
+// for gfx950 (MI355X).
 //
-// One launch moves a whole work list: the reduce-scatter pack of a bucket
+// One launch moves a whole operation: the reduce-scatter pack of a bucket
 // (every (rank, tensor) chunk, cast to the reduction dtype and zero-padded:
 // "PyTorch adds per-parameter mixed precision to FSDP2", paragraph 2), the
 // all-gather copy-in of one rank (every shard cast to its compute dtype,
@@ -10,8 +10,9 @@
 //
 // The work is pure data movement with a handful of integer operations per
 // element, so the design aims at HBM bandwidth, not at the matrix cores:
-//  * each workgroup (one wave64) owns one item of the host-built prefix map
-//    (4 KiB of destination) and walks the segments it overlaps;
+//  * each workgroup (one wave64) owns one 2 KiB window of destination,
+//    finds the rank chunks it overlaps from its index and the plan's small
+//    tables (a column map for the pack), and walks them;
 //  * every destination byte is written by a 16-byte vector store from its
 //    16-byte aligned address (scalar stores only at a range's unaligned head
 //    and tail), 64-lane wavefronts covering 1 KiB per store instruction;
@@ -34,14 +35,16 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// One wavefront per workgroup, each lane holding four destination vectors
-// in flight: an item of kBlock * kUnroll * 16 = 4 KiB of destination is one
-// unrolled pass (all loads issued, then all stores), and a launch has many
-// thousands of short workgroups, which kept more bytes in flight than
-// longer-lived or persistent workgroups in measurements on MI355X.
+// One wavefront per workgroup, two destination vectors per lane: a window
+// of kBlock * kUnroll * 16 = 2 KiB is one pass (loads issued, then stores),
+// and a launch has tens of thousands of short workgroups.  On MI355X this
+// shape kept the most bytes in flight once each wave's table reads are paid:
+// one vector per lane leaves too few bytes per wave behind those reads;
+// more vectors per lane, wider workgroups or persistent workgroups measured
+// no better.
 constexpr int kBlock = 64;    // threads per workgroup (one wave64)
-constexpr int kUnroll = 4;    // destination vectors in flight per thread
-static_assert(kBlock * kUnroll * 16 == kItemBytes, "one item is one unrolled pass of the workgroup");
+constexpr int kUnroll = 2;    // destination vectors per thread per pass
+static_assert(kBlock * kUnroll * 16 == kWindowBytes, "one window is one pass of the workgroup");
 
 template <int DT> struct ElemT;
 template <> struct ElemT<kBF16> { using T = uint16_t; };
@@ -161,7 +164,7 @@ __device__ __forceinline__ void copy_one(const char *src, char *dst, int64_t i, 
 }
 
 // A destination vector that straddles the end of the valid prefix (at most
-// one per segment): element-wise loads of the valid part only.
+// one per range): element-wise loads of the valid part only.
 template <int S, int D>
 __device__ __forceinline__ void copy_straddle(const char *src, char *dst, int64_t i0, int64_t valid)
 {
@@ -178,8 +181,8 @@ __device__ __forceinline__ void copy_straddle(const char *src, char *dst, int64_
     store16(dst + i0 * (int64_t)sizeof(typename P::DT), r);
 }
 
-// Elements [lo, hi) of one segment: dst[i] = i < valid ? cast(src[i]) : +0,
-// where src / dst address element 0 of the segment.  All threads of the
+// Elements [lo, hi) of one range: dst[i] = i < valid ? cast(src[i]) : +0,
+// where src / dst address element 0 of the range's chunk.  All threads of the
 // workgroup take part; no two threads write the same byte.
 template <int S, int D>
 __device__ void copy_range(const char *__restrict__ src, char *__restrict__ dst, int64_t lo,
@@ -251,53 +254,47 @@ __device__ void copy_range(const char *__restrict__ src, char *__restrict__ dst,
     if (tid < hi - t0) copy_one<S, D>(src, dst, t0 + tid, valid);
 }
 
-__device__ __forceinline__ void run_segment(const Seg &g, int64_t lo, int64_t hi,
-                                            const uint64_t *table, char *base)
+__device__ __forceinline__ void run_range(const RangeRef &g, char *base)
 {
-    char *tp = reinterpret_cast<char *>(table[g.slot]);
+    char *tp = reinterpret_cast<char *>(g.ptr);
     const char *src;
     char *dst;
     if (g.table_side == kTableIsSource) { src = tp + g.src_off; dst = base + g.dst_off; }
     else { src = base + g.src_off; dst = tp + g.dst_off; }
     switch (g.src_dt * 4 + g.dst_dt) {
-    case kBF16 * 4 + kFP32: copy_range<kBF16, kFP32>(src, dst, lo, hi, g.valid); break;
-    case kFP32 * 4 + kFP32: copy_range<kFP32, kFP32>(src, dst, lo, hi, g.valid); break;
-    case kFP32 * 4 + kBF16: copy_range<kFP32, kBF16>(src, dst, lo, hi, g.valid); break;
-    case kBF16 * 4 + kBF16: copy_range<kBF16, kBF16>(src, dst, lo, hi, g.valid); break;
+    case kBF16 * 4 + kFP32: copy_range<kBF16, kFP32>(src, dst, g.lo, g.hi, g.valid); break;
+    case kFP32 * 4 + kFP32: copy_range<kFP32, kFP32>(src, dst, g.lo, g.hi, g.valid); break;
+    case kFP32 * 4 + kBF16: copy_range<kFP32, kBF16>(src, dst, g.lo, g.hi, g.valid); break;
+    case kBF16 * 4 + kBF16: copy_range<kBF16, kBF16>(src, dst, g.lo, g.hi, g.valid); break;
     default: break;   // the planner only emits the four pairs above
     }
 }
 
-// One workgroup per item.  An item's end is either inside a segment
-// (off_b > 0) or the start of segment seg_b (off_b == 0, possibly the end of
-// the list), so the loop never reads past the segment array.
-__device__ __forceinline__ void run_item(const LaunchArgs &a, int32_t k)
+// One workgroup per window; the window's ranges come from its index and a
+// binary search over the (cache-resident) member table.
+template <int OP>
+__global__ void __launch_bounds__(kBlock) window_kernel(WindowArgs a)
 {
-    const Item it = a.items[item_slot(k, a.n_items)];
-    for (int32_t s = it.seg_a; s < it.seg_b || (s == it.seg_b && it.off_b > 0); ++s) {
-        const Seg g = a.segs[s];
-        const int64_t lo = (s == it.seg_a) ? it.off_a : 0;
-        const int64_t hi = (s == it.seg_b) ? it.off_b : g.len;
-        if (hi > lo) run_segment(g, lo, hi, a.table, a.base);
-    }
-}
-
-__global__ void __launch_bounds__(kBlock) segments_kernel(LaunchArgs a)
-{
-    run_item(a, static_cast<int32_t>(blockIdx.x));
+    const int32_t w = static_cast<int32_t>(blockIdx.x);
+    auto body = [&](const RangeRef &g) { run_range(g, a.base); };
+    if constexpr (OP == kOpPack) pack_window(a, w, body);
+    else if constexpr (OP == kOpCopyIn) copy_in_window(a, w, body);
+    else copy_out_window(a, w, body);
 }
 
 }  // namespace
 
-int launch_segments(const LaunchArgs &args, void *stream, void *start_event, void *stop_event)
+int launch_windows(const WindowArgs &args, void *stream, void *start_event, void *stop_event)
 {
-    if (args.n_items <= 0) return static_cast<int>(hipSuccess);
-    const uint32_t grid = static_cast<uint32_t>(args.n_items);
+    if (args.n_windows <= 0) return static_cast<int>(hipSuccess);
+    const dim3 grid(static_cast<uint32_t>(args.n_windows)), block(kBlock);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipEvent_t e0 = static_cast<hipEvent_t>(start_event), e1 = static_cast<hipEvent_t>(stop_event);
     // hipExtLaunchKernelGGL: when events are given they are stamped by the
     // dispatch itself, so they bracket exactly this kernel's execution
-    hipExtLaunchKernelGGL(segments_kernel, dim3(grid), dim3(kBlock), 0,
-                          static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(start_event),
-                          static_cast<hipEvent_t>(stop_event), 0, args);
+    if (args.op == kOpPack) hipExtLaunchKernelGGL(window_kernel<kOpPack>, grid, block, 0, st, e0, e1, 0, args);
+    else if (args.op == kOpCopyIn) hipExtLaunchKernelGGL(window_kernel<kOpCopyIn>, grid, block, 0, st, e0, e1, 0, args);
+    else hipExtLaunchKernelGGL(window_kernel<kOpCopyOut>, grid, block, 0, st, e0, e1, 0, args);
     return static_cast<int>(hipGetLastError());
 }
 

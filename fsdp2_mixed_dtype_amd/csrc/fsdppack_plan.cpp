@@ -33,49 +33,14 @@ constexpr int64_t kMaxBytes = INT64_MAX / 4;
 
 }  // namespace
 
-void build_items(const std::vector<Seg> &segs, const std::vector<int64_t> &vpos, int64_t item_bytes,
-                 std::vector<Item> &items)
-{
-    // item starts in list order: a new item wherever the virtual position
-    // crosses a multiple of item_bytes
-    struct Start { int32_t seg; int64_t off; };
-    std::vector<Start> starts;
-    int64_t current = -1;   // virtual window of the item being filled
-    for (size_t i = 0; i < segs.size(); ++i) {
-        const Seg &g = segs[i];
-        if (g.len == 0) continue;
-        const int64_t esz = dtype_bytes(g.dst_dt);
-        const int64_t a = vpos[i], e = vpos[i] + g.len * esz;
-        const int64_t k0 = a / item_bytes, k1 = (e - 1) / item_bytes;
-        for (int64_t k = k0; k <= k1; ++k) {
-            if (k == current) continue;   // the open item runs on into this segment
-            const int64_t off = (k == k0) ? 0 : (k * item_bytes - a) / esz;
-            starts.push_back(Start{static_cast<int32_t>(i), off});
-            current = k;
-        }
-    }
-    const int32_t n = static_cast<int32_t>(starts.size());
-    items.assign(n, Item{});
-    for (int32_t b = 0; b < n; ++b) {
-        Item it{};
-        it.seg_a = starts[b].seg;
-        it.off_a = starts[b].off;
-        if (b + 1 < n) { it.seg_b = starts[b + 1].seg; it.off_b = starts[b + 1].off; }
-        else { it.seg_b = static_cast<int32_t>(segs.size()); it.off_b = 0; }
-        items[item_slot(b, n)] = it;
-    }
-}
-
-int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, int64_t item_bytes,
-               fsdppack_plan *plan, std::string &err)
+int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdppack_plan *plan,
+               std::string &err)
 {
     if (n < 0 || (n > 0 && params == nullptr)) { err = "plan_buckets: params is NULL or n < 0"; return FSDPPACK_EINVAL; }
     if (world < 1) { err = "plan_buckets: world size must be >= 1"; return FSDPPACK_EINVAL; }
-    if (item_bytes < 256 || item_bytes % 16) { err = "plan_buckets: bad work-item size"; return FSDPPACK_EINVAL; }
     const int64_t W = world;
     plan->W = world;
     plan->n = n;
-    plan->item_bytes = item_bytes;
     plan->params.assign(params, params + n);
     plan->numel.resize(n);
     plan->P.resize(n);
@@ -135,107 +100,99 @@ int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, int6
     }
     plan->B = round_up16(cursor);
 
-    // ---- work lists
-    std::vector<int64_t> vpos;
+    // ---- operation tables (members with nothing to move are left out, so
+    // every lookup lands on a non-empty member)
+    const int64_t kMaxWindows = INT32_MAX;
     for (BucketPlan &b : plan->buckets) {
-        // reduce-scatter pack: rank-major, members in unit order, i.e. the
-        // order of the [W, S] destination in memory
-        WorkList &wl = b.pack;
+        // reduce-scatter pack: members in unit order along the columns of
+        // every row; window w covers row w / gx
+        OpTable &op = b.pack;
+        op.op = kOpPack;
+        op.dst_dt = b.dtype;
+        op.S = b.S;
         const int64_t dsz = dtype_bytes(b.dtype);
-        vpos.clear();
-        for (int64_t r = 0; r < W; ++r) {
-            for (size_t k = 0; k < b.members.size(); ++k) {
-                const int32_t t = b.members[k];
-                const int64_t Pt = b.P[k];
-                if (Pt == 0) continue;
-                const int64_t valid = std::max<int64_t>(0, std::min<int64_t>(Pt, plan->numel[t] - r * Pt));
-                Seg g{};
-                g.dst_off = (r * b.S + b.O[k]) * dsz;
-                g.src_off = r * Pt * dtype_bytes(plan->params[t].grad_dtype);
-                g.len = Pt;
-                g.valid = valid;
-                g.slot = t;
-                g.src_dt = static_cast<uint8_t>(plan->params[t].grad_dtype);
-                g.dst_dt = static_cast<uint8_t>(b.dtype);
-                g.table_side = kTableIsSource;
-                wl.segs.push_back(g);
-                vpos.push_back(g.dst_off);
-                wl.src_bytes += valid * dtype_bytes(g.src_dt);
-            }
+        std::vector<PackMember> mem;
+        for (size_t k = 0; k < b.members.size(); ++k) {
+            const int32_t t = b.members[k];
+            if (b.P[k] == 0) continue;
+            PackMember m{};
+            m.O = b.O[k];
+            m.P = b.P[k];
+            m.numel = plan->numel[t];
+            m.param = t;
+            m.src_dt = plan->params[t].grad_dtype;
+            op.add(m);
+            mem.push_back(m);
+            op.table_params.push_back(t);
+            op.src_bytes += plan->numel[t] * dtype_bytes(m.src_dt);
         }
-        wl.dst_bytes = W * b.S * dsz;
-        if (wl.segs.size() > static_cast<size_t>(INT32_MAX) - 1) { err = "plan_buckets: too many rank chunks"; return FSDPPACK_EINVAL; }
-        build_items(wl.segs, vpos, item_bytes, wl.items);
+        const int64_t gx = (b.S * dsz + kWindowBytes - 1) / kWindowBytes;
+        if (gx * W > kMaxWindows) { err = "plan_buckets: reduce-scatter buffer needs too many workgroups"; return FSDPPACK_EINVAL; }
+        op.gx = static_cast<int32_t>(gx);
+        // column map: the members each window of a row overlaps (members
+        // tile [0, S) in column order, so one sweep finds them all)
+        const int64_t E = kWindowBytes / dsz;
+        op.columns.resize(static_cast<size_t>(gx));
+        size_t first = 0;
+        for (int64_t x = 0; x < gx; ++x) {
+            const int64_t c0 = x * E, c1 = std::min(b.S, c0 + E);
+            while (first < mem.size() && mem[first].O + mem[first].P <= c0) ++first;
+            size_t last = first;
+            while (last < mem.size() && mem[last].O < c1) ++last;
+            if (last - first > static_cast<size_t>(INT32_MAX)) { err = "plan_buckets: column window too crowded"; return FSDPPACK_EINVAL; }
+            op.columns[x] = ColumnWindow{static_cast<int32_t>(first), static_cast<int32_t>(last - first)};
+        }
+        op.n_windows = static_cast<int32_t>(gx * W);
+        op.dst_bytes = W * b.S * dsz;
     }
 
-    {   // all-gather copy-in: one segment per parameter, each covering its
-        // 16-byte aligned slot (cast shard, then zero gap up to the next
-        // slot); grouped by (storage, param) dtype pair, unit order inside
-        WorkList &wl = plan->copy_in;
-        std::map<int32_t, int32_t> pair_group;   // dtype pair -> first-appearance index
-        std::vector<int32_t> group(n), order(n);
+    {   // all-gather copy-in: each parameter owns bytes [A_t, A_{t+1}) of the
+        // row: its cast shard, then zero gap bytes up to the next slot
+        OpTable &op = plan->copy_in;
+        op.op = kOpCopyIn;
+        op.B = plan->B;
         for (int32_t t = 0; t < n; ++t) {
-            const int32_t key = plan->params[t].storage_dtype * 4 + plan->params[t].param_dtype;
-            group[t] = pair_group.emplace(key, static_cast<int32_t>(pair_group.size())).first->second;
-            order[t] = t;
-        }
-        std::stable_sort(order.begin(), order.end(),
-                         [&](int32_t x, int32_t y) { return group[x] < group[y]; });
-        vpos.clear();
-        int64_t v = 0;
-        for (int32_t t : order) {
             const int64_t next = (t + 1 < n) ? plan->A[t + 1] : plan->B;
-            const int64_t span = next - plan->A[t];
-            if (span == 0) continue;
-            const int64_t psz = dtype_bytes(plan->params[t].param_dtype);
-            Seg g{};
-            g.dst_off = plan->A[t];
-            g.src_off = 0;
-            g.len = span / psz;
-            g.valid = plan->P[t];
-            g.slot = t;
-            g.src_dt = static_cast<uint8_t>(plan->params[t].storage_dtype);
-            g.dst_dt = static_cast<uint8_t>(plan->params[t].param_dtype);
-            g.table_side = kTableIsSource;
-            wl.segs.push_back(g);
-            vpos.push_back(v);
-            v += span;
-            wl.src_bytes += plan->P[t] * dtype_bytes(g.src_dt);
+            if (next == plan->A[t]) continue;
+            CopyInMember m{};
+            m.A = plan->A[t];
+            m.A_next = next;
+            m.P = plan->P[t];
+            m.slot = t;
+            m.src_dt = static_cast<int16_t>(plan->params[t].storage_dtype);
+            m.dst_dt = static_cast<int16_t>(plan->params[t].param_dtype);
+            op.add(m);
+            op.src_bytes += plan->P[t] * dtype_bytes(m.src_dt);
         }
-        wl.dst_bytes = plan->B;
-        build_items(wl.segs, vpos, item_bytes, wl.items);
+        const int64_t nw = (plan->B + kWindowBytes - 1) / kWindowBytes;
+        if (nw > kMaxWindows) { err = "plan_buckets: all-gather row needs too many workgroups"; return FSDPPACK_EINVAL; }
+        op.n_windows = static_cast<int32_t>(nw);
+        op.dst_bytes = plan->B;
     }
 
-    {   // all-gather copy-out: per parameter, per rank, the non-padding part
-        // of the gathered segment back into the full tensor
-        WorkList &wl = plan->copy_out;
-        vpos.clear();
-        int64_t v = 0;
+    {   // all-gather copy-out: each parameter's bytes cut into windows; a
+        // window is split at rank-chunk boundaries by the kernel
+        OpTable &op = plan->copy_out;
+        op.op = kOpCopyOut;
+        op.B = plan->B;
+        int64_t win = 0;
         for (int32_t t = 0; t < n; ++t) {
-            const int64_t psz = dtype_bytes(plan->params[t].param_dtype);
-            const int64_t Pt = plan->P[t];
-            v = round_up16(v);
-            for (int64_t r = 0; r < W && Pt > 0; ++r) {
-                const int64_t valid = std::max<int64_t>(0, std::min<int64_t>(Pt, plan->numel[t] - r * Pt));
-                if (valid == 0) break;
-                Seg g{};
-                g.dst_off = r * Pt * psz;
-                g.src_off = r * plan->B + plan->A[t];
-                g.len = valid;
-                g.valid = valid;
-                g.slot = t;
-                g.src_dt = static_cast<uint8_t>(plan->params[t].param_dtype);
-                g.dst_dt = g.src_dt;
-                g.table_side = kTableIsDest;
-                wl.segs.push_back(g);
-                vpos.push_back(v + g.dst_off);
-            }
-            v += plan->numel[t] * psz;
-            wl.src_bytes += plan->numel[t] * psz;
+            if (plan->numel[t] == 0) continue;
+            const int64_t bytes = plan->numel[t] * dtype_bytes(plan->params[t].param_dtype);
+            CopyOutTensor m{};
+            m.win0 = win;
+            m.numel = plan->numel[t];
+            m.P = plan->P[t];
+            m.A = plan->A[t];
+            m.slot = t;
+            m.dt = plan->params[t].param_dtype;
+            op.add(m);
+            win += (bytes + kWindowBytes - 1) / kWindowBytes;
+            if (win > kMaxWindows) { err = "plan_buckets: parameters need too many copy-out workgroups"; return FSDPPACK_EINVAL; }
+            op.src_bytes += bytes;
         }
-        wl.dst_bytes = wl.src_bytes;
-        if (wl.segs.size() > static_cast<size_t>(INT32_MAX) - 1) { err = "plan_buckets: too many rank chunks"; return FSDPPACK_EINVAL; }
-        build_items(wl.segs, vpos, item_bytes, wl.items);
+        op.n_windows = static_cast<int32_t>(win);
+        op.dst_bytes = op.src_bytes;
     }
     return FSDPPACK_OK;
 }

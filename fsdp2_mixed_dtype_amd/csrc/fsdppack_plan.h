@@ -4,7 +4,7 @@
 // (ainewsletter.today), paragraph 2, for bucketing (one reduction buffer per
 // effective reduction dtype), and "The unit you wrapped" (kernels.rudrite.com),
 // padding paragraphs, for the equal right-padded rank pieces.  It also builds
-// the three work lists the kernels consume (segments + prefix map).
+// the member tables the kernels search (one per operation).
 #pragma once
 
 #include <cstdint>
@@ -17,16 +17,45 @@
 
 namespace fsdppack {
 
-// A work list and, once uploaded, its device copy.
-struct WorkList {
-    std::vector<Seg> segs;
-    std::vector<Item> items;          // n_items records, stored by item_slot()
-    int64_t dst_bytes = 0;            // bytes the list writes
-    int64_t src_bytes = 0;            // bytes the list reads
-    // device side (owned by the plan)
-    Seg *d_segs = nullptr;
-    Item *d_items = nullptr;
-    int32_t n_items() const { return static_cast<int32_t>(items.size()); }
+// One launchable operation: its member table (uploaded once) and launch
+// geometry.
+struct OpTable {
+    int32_t op = kOpPack;
+    std::vector<unsigned char> members;   // PackMember / CopyInMember / CopyOutTensor records
+    std::vector<ColumnWindow> columns;    // pack: per window of a row
+    std::vector<int32_t> table_params;    // pointer-table entry -> parameter index
+    int32_t n = 0;                        // records
+    int32_t n_windows = 0;                // workgroups per launch
+    int32_t gx = 0;                       // pack: windows per row
+    int32_t dst_dt = 0;                   // pack: reduction dtype
+    int64_t S = 0;                        // pack: row length (elements)
+    int64_t B = 0;                        // all-gather row bytes
+    int64_t dst_bytes = 0;                // bytes the operation writes
+    int64_t src_bytes = 0;                // bytes it reads
+    void *d_members = nullptr;            // device copies (owned by the plan)
+    void *d_columns = nullptr;
+
+    template <typename T> void add(const T &rec)
+    {
+        const unsigned char *p = reinterpret_cast<const unsigned char *>(&rec);
+        members.insert(members.end(), p, p + sizeof(T));
+        ++n;
+    }
+    // launch arguments against host (`device == false`) or device members
+    WindowArgs args(bool device) const
+    {
+        WindowArgs a{};
+        a.op = op;
+        a.n = n;
+        a.n_windows = n_windows;
+        a.gx = gx;
+        a.dst_dt = dst_dt;
+        a.S = S;
+        a.B = B;
+        a.members = device ? d_members : static_cast<const void *>(members.data());
+        a.columns = device ? d_columns : static_cast<const void *>(columns.data());
+        return a;
+    }
 };
 
 struct BucketPlan {
@@ -34,7 +63,7 @@ struct BucketPlan {
     int64_t S = 0;
     std::vector<int32_t> members;
     std::vector<int64_t> P, O;
-    WorkList pack;
+    OpTable pack;
 };
 
 // Per-call pointer tables, cached on the device by content: the same grads /
@@ -73,8 +102,7 @@ struct fsdppack_plan {
     std::vector<int64_t> numel, P, A;
     int64_t B = 0;
     std::vector<fsdppack::BucketPlan> buckets;
-    fsdppack::WorkList copy_in, copy_out;
-    int64_t item_bytes = 0;
+    fsdppack::OpTable copy_in, copy_out;
 
     // device state (guarded by mu)
     std::mutex mu;
@@ -86,13 +114,7 @@ struct fsdppack_plan {
 namespace fsdppack {
 
 // Build the plan (host work only).  Returns a status code and fills `err`.
-int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, int64_t item_bytes,
-               fsdppack_plan *plan, std::string &err);
-
-// Cut a segment list into items of about `item_bytes` destination bytes;
-// vpos[i] is segment i's position in a virtual destination space
-// (monotonic; gaps allowed) so that cuts land on aligned offsets.
-void build_items(const std::vector<Seg> &segs, const std::vector<int64_t> &vpos, int64_t item_bytes,
-                 std::vector<Item> &items);
+int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdppack_plan *plan,
+               std::string &err);
 
 }  // namespace fsdppack

@@ -147,7 +147,7 @@ int fsdppack_pack_reduce_scatter_input(const fsdppack_plan *plan, int32_t bucket
  * cast from its storage dtype to its param dtype at byte A_t; the row's gap
  * bytes are written as zero, the other rows are not touched.  shards: n host
  * entries of device pointers to P_t elements each (storage dtype).  The
- * copies are grouped by (storage, param) dtype pair inside one launch.
+ * (storage, param) dtype pairs all run in the same single launch.
  * Errors: EINVAL, ESTATE, EHIP, ENOMEM. */
 int fsdppack_all_gather_copy_in(const fsdppack_plan *plan, int32_t rank, const void *const *shards,
                                 void *ag_out, void *stream);

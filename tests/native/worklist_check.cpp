@@ -1,25 +1,23 @@
-// worklist_check.cpp -- host-side bounds check of libfsdppack's work lists.
+// worklist_check.cpp -- host-side bounds check of libfsdppack's launches.
 //
 // Builds a plan with the library's own planner (fsdppack_plan.cpp, compiled
 // into this program with the address and undefined-behaviour sanitizers) and
-// checks, for every work list the kernels would run, the invariants the
-// grouped segment kernel relies on:
-//  * the item records are stored by a bijective slot map, each covers a
-//    non-empty range inside the segment array, and consecutive items meet
-//    exactly (the last one ends the list);
-//  * every segment's destination range lies inside its destination buffer,
-//    its source range (the `valid` prefix) inside its source buffer, its
-//    pointer-table slot inside the table, and its dtypes are supported;
-//  * walking the items exactly as the kernel does writes every destination
-//    byte exactly once (checked on the sorted list of written intervals).
+// walks every window of every operation through the very window -> range
+// mapping the kernels run (fsdppack_internal.h, compiled for the host here),
+// checking the invariants the kernels rely on:
+//  * each range lies inside its chunk, reads only the source bytes of its
+//    `valid` prefix, and writes inside its destination buffer;
+//  * ranges use a valid pointer-table slot and supported dtypes;
+//  * over all windows of a launch, every destination byte is written exactly
+//    once (checked on the sorted list of written intervals).
 //
-// Input (stdin): "world item_bytes n" then n lines
+// Input (stdin): "world n" then n lines
 // "dim0 inner grad reduce storage param".  Prints "OK" or the first failure.
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
-#include <utility>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "../../fsdp2_mixed_dtype_amd/csrc/fsdppack_plan.h"
@@ -38,72 +36,60 @@ static std::string g_fail;
         }                                                                 \
     } while (0)
 
-// dst_size(seg): bytes of the buffer the segment writes into;
-// src_size(seg): bytes of the buffer it reads from.
+using Intervals = std::vector<std::pair<int64_t, int64_t>>;
+
+// Check one range produced for window w.
 template <typename DstSize, typename SrcSize>
-static bool check_list(const char *name, const WorkList &wl, int32_t nparams, DstSize dst_size, SrcSize src_size,
-                       std::vector<std::vector<std::pair<int64_t, int64_t>>> &written)
+static bool check_range(const char *name, int32_t w, const RangeRef &g, const OpTable &op, int32_t nparams,
+                        DstSize dst_size, SrcSize src_size, std::vector<Intervals> &written)
 {
-    const int64_t nseg = static_cast<int64_t>(wl.segs.size());
-    const int32_t n = static_cast<int32_t>(wl.items.size());
-    // item_slot must be a bijection on [0, n)
-    std::vector<uint8_t> hit(n, 0);
-    for (int32_t b = 0; b < n; ++b) {
-        const int32_t slot = item_slot(b, n);
-        CHECK(slot >= 0 && slot < n && !hit[slot], "%s: item_slot not a bijection at %d", name, b);
-        hit[slot] = 1;
+    CHECK(dtype_ok(g.src_dt) && dtype_ok(g.dst_dt), "%s: window %d bad dtype", name, w);
+    const int32_t entries = op.op == kOpPack ? op.n : nparams;     // pointer-table entries
+    CHECK(g.slot >= 0 && g.slot < entries, "%s: window %d slot %d out of range", name, w, g.slot);
+    CHECK(g.param >= 0 && g.param < nparams, "%s: window %d param %d out of range", name, w, g.param);
+    CHECK(op.op != kOpPack || op.table_params[g.slot] == g.param, "%s: window %d table entry mismatch", name, w);
+    CHECK(g.lo >= 0 && g.lo < g.hi, "%s: window %d empty or reversed range", name, w);
+    CHECK(g.valid >= 0, "%s: window %d negative valid", name, w);
+    const int64_t dsz = dtype_bytes(g.dst_dt), ssz = dtype_bytes(g.src_dt);
+    const int64_t d0 = g.dst_off + g.lo * dsz, d1 = g.dst_off + g.hi * dsz;
+    CHECK(g.dst_off >= 0 && g.dst_off % dsz == 0 && d1 <= dst_size(g), "%s: window %d writes [%lld,%lld) past %lld",
+          name, w, (long long)d0, (long long)d1, (long long)dst_size(g));
+    if (g.lo < g.valid) {
+        const int64_t s1 = g.src_off + std::min(g.hi, g.valid) * ssz;
+        CHECK(g.src_off >= 0 && s1 <= src_size(g), "%s: window %d reads up to %lld past %lld", name, w,
+              (long long)s1, (long long)src_size(g));
     }
-    for (int32_t b = 0; b < n; ++b) {
-        const Item &it = wl.items[item_slot(b, n)];
-        CHECK(it.seg_a >= 0 && it.seg_a < nseg, "%s: item %d start segment %d out of range", name, b, it.seg_a);
-        CHECK(it.off_a >= 0 && it.off_a < wl.segs[it.seg_a].len, "%s: item %d start offset out of range", name, b);
-        CHECK(it.seg_b >= 0 && it.seg_b <= nseg, "%s: item %d end segment out of range", name, b);
-        CHECK(it.seg_b < nseg ? (it.off_b >= 0 && it.off_b < wl.segs[it.seg_b].len) : it.off_b == 0,
-              "%s: item %d end offset out of range", name, b);
-        CHECK(it.seg_a < it.seg_b || (it.seg_a == it.seg_b && it.off_a < it.off_b), "%s: item %d empty or reversed",
-              name, b);
-        if (b + 1 < n) {
-            const Item &nx = wl.items[item_slot(b + 1, n)];
-            CHECK(nx.seg_a == it.seg_b && nx.off_a == it.off_b, "%s: item %d does not end where %d starts", name, b, b + 1);
-        } else {
-            CHECK(it.seg_b == nseg && it.off_b == 0, "%s: last item does not end the list", name);
-        }
-    }
-    for (int64_t i = 0; i < nseg; ++i) {
-        const Seg &g = wl.segs[i];
-        CHECK(dtype_ok(g.src_dt) && dtype_ok(g.dst_dt), "%s: segment %lld bad dtype", name, (long long)i);
-        CHECK(g.slot >= 0 && g.slot < nparams, "%s: segment %lld slot %d out of range", name, (long long)i, g.slot);
-        CHECK(g.len >= 0 && g.valid >= 0 && g.valid <= g.len, "%s: segment %lld bad len/valid", name, (long long)i);
-        const int64_t dend = g.dst_off + g.len * dtype_bytes(g.dst_dt);
-        CHECK(g.dst_off >= 0 && dend <= dst_size(g), "%s: segment %lld writes [%lld,%lld) past %lld", name,
-              (long long)i, (long long)g.dst_off, (long long)dend, (long long)dst_size(g));
-        CHECK(g.dst_off % dtype_bytes(g.dst_dt) == 0, "%s: segment %lld destination misaligned", name, (long long)i);
-        if (g.valid > 0) {
-            const int64_t send = g.src_off + g.valid * dtype_bytes(g.src_dt);
-            CHECK(g.src_off >= 0 && send <= src_size(g), "%s: segment %lld reads [%lld,%lld) past %lld", name,
-                  (long long)i, (long long)g.src_off, (long long)send, (long long)src_size(g));
-        }
-    }
-    // walk items the way the kernel does and record written byte ranges
-    for (int32_t b = 0; b < n; ++b) {
-        const Item it = wl.items[item_slot(b, n)];
-        for (int32_t s = it.seg_a; s < it.seg_b || (s == it.seg_b && it.off_b > 0); ++s) {
-            CHECK(s < nseg, "%s: item walk reads segment %d of %lld", name, s, (long long)nseg);
-            const Seg &g = wl.segs[s];
-            const int64_t lo = (s == it.seg_a) ? it.off_a : 0;
-            const int64_t hi = (s == it.seg_b) ? it.off_b : g.len;
-            if (hi <= lo) continue;
-            CHECK(hi <= g.len, "%s: range past segment end", name);
-            const int64_t esz = dtype_bytes(g.dst_dt);
-            const int buf = g.table_side == kTableIsDest ? g.slot : 0;
-            written[buf].emplace_back(g.dst_off + lo * esz, g.dst_off + hi * esz);
-        }
+    written[g.table_side == kTableIsDest ? g.param : 0].emplace_back(d0, d1);
+    return true;
+}
+
+template <typename DstSize, typename SrcSize>
+static bool check_op(const char *name, const OpTable &op, int32_t W, int32_t nparams, DstSize dst_size,
+                     SrcSize src_size, std::vector<Intervals> &written)
+{
+    WindowArgs a = op.args(false);
+    a.W = W;
+    const size_t rec = op.op == kOpPack ? sizeof(PackMember)
+                       : op.op == kOpCopyIn ? sizeof(CopyInMember) : sizeof(CopyOutTensor);
+    CHECK(op.members.size() == static_cast<size_t>(op.n) * rec, "%s: member table size", name);
+    CHECK(op.n_windows == 0 || op.n > 0, "%s: windows without members", name);
+    CHECK(op.op != kOpPack || (op.columns.size() == static_cast<size_t>(op.gx) &&
+                               op.table_params.size() == static_cast<size_t>(op.n)), "%s: column map size", name);
+    for (int32_t w = 0; w < op.n_windows; ++w) {
+        int ranges = 0;
+        bool ok = true;
+        for_each_range(a, w, [&](const RangeRef &g) {
+            if (ok) ok = check_range(name, w, g, op, nparams, dst_size, src_size, written);
+            ++ranges;
+        });
+        if (!ok) return false;
+        CHECK(ranges > 0, "%s: window %d has no range", name, w);
     }
     return true;
 }
 
 // The written intervals of one buffer must tile [0, size) exactly.
-static bool tiles(std::vector<std::pair<int64_t, int64_t>> v, int64_t size, const char *name)
+static bool tiles(Intervals v, int64_t size, const char *name)
 {
     std::sort(v.begin(), v.end());
     int64_t at = 0;
@@ -119,8 +105,7 @@ static bool tiles(std::vector<std::pair<int64_t, int64_t>> v, int64_t size, cons
 int main()
 {
     int32_t world, n;
-    long long item_bytes;
-    if (std::scanf("%d %lld %d", &world, &item_bytes, &n) != 3) { std::puts("FAIL bad header"); return 1; }
+    if (std::scanf("%d %d", &world, &n) != 2) { std::puts("FAIL bad header"); return 1; }
     std::vector<fsdppack_param_desc> d(n);
     for (int32_t i = 0; i < n; ++i) {
         long long a, b;
@@ -131,37 +116,39 @@ int main()
     }
     fsdppack_plan plan;
     std::string err;
-    if (build_plan(d.data(), n, world, item_bytes, &plan, err) != FSDPPACK_OK) {
+    if (build_plan(d.data(), n, world, &plan, err) != FSDPPACK_OK) {
         std::printf("FAIL plan: %s\n", err.c_str());
         return 1;
     }
     const int64_t W = plan.W;
-    auto grad_bytes = [&](const Seg &g) { return plan.numel[g.slot] * dtype_bytes(plan.params[g.slot].grad_dtype); };
+    auto grad_bytes = [&](const RangeRef &g) { return plan.numel[g.param] * dtype_bytes(plan.params[g.param].grad_dtype); };
     for (size_t bi = 0; bi < plan.buckets.size(); ++bi) {
         const BucketPlan &b = plan.buckets[bi];
         const int64_t out_bytes = W * b.S * dtype_bytes(b.dtype);
-        std::vector<std::vector<std::pair<int64_t, int64_t>>> written(1);
+        std::vector<Intervals> written(1);
         char name[64];
         std::snprintf(name, sizeof name, "pack[%zu]", bi);
-        if (!check_list(name, b.pack, n, [&](const Seg &) { return out_bytes; }, grad_bytes, written) ||
+        if (!check_op(name, b.pack, plan.W, n, [&](const RangeRef &) { return out_bytes; }, grad_bytes, written) ||
             !tiles(written[0], out_bytes, name)) {
             std::printf("FAIL %s\n", g_fail.c_str());
             return 1;
         }
     }
     {
-        std::vector<std::vector<std::pair<int64_t, int64_t>>> written(1);
-        auto shard_bytes = [&](const Seg &g) { return plan.P[g.slot] * dtype_bytes(plan.params[g.slot].storage_dtype); };
-        if (!check_list("copy_in", plan.copy_in, n, [&](const Seg &) { return plan.B; }, shard_bytes, written) ||
+        std::vector<Intervals> written(1);
+        auto shard_bytes = [&](const RangeRef &g) { return plan.P[g.param] * dtype_bytes(plan.params[g.param].storage_dtype); };
+        if (!check_op("copy_in", plan.copy_in, plan.W, n, [&](const RangeRef &) { return plan.B; }, shard_bytes,
+                      written) ||
             !tiles(written[0], plan.B, "copy_in")) {
             std::printf("FAIL %s\n", g_fail.c_str());
             return 1;
         }
     }
     {
-        std::vector<std::vector<std::pair<int64_t, int64_t>>> written(n);
-        auto param_bytes = [&](const Seg &g) { return plan.numel[g.slot] * dtype_bytes(plan.params[g.slot].param_dtype); };
-        if (!check_list("copy_out", plan.copy_out, n, param_bytes, [&](const Seg &) { return W * plan.B; }, written)) {
+        std::vector<Intervals> written(n);
+        auto param_bytes = [&](const RangeRef &g) { return plan.numel[g.param] * dtype_bytes(plan.params[g.param].param_dtype); };
+        if (!check_op("copy_out", plan.copy_out, plan.W, n, param_bytes, [&](const RangeRef &) { return W * plan.B; },
+                      written)) {
             std::printf("FAIL %s\n", g_fail.c_str());
             return 1;
         }
@@ -174,8 +161,8 @@ int main()
             }
         }
     }
-    std::printf("OK %zu buckets, items:", plan.buckets.size());
-    for (const BucketPlan &b : plan.buckets) std::printf(" %d", b.pack.n_items());
-    std::printf(" copy_in %d copy_out %d\n", plan.copy_in.n_items(), plan.copy_out.n_items());
+    std::printf("OK %zu buckets, windows:", plan.buckets.size());
+    for (const BucketPlan &b : plan.buckets) std::printf(" %d", b.pack.n_windows);
+    std::printf(" copy_in %d copy_out %d\n", plan.copy_in.n_windows, plan.copy_out.n_windows);
     return 0;
 }
