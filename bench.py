@@ -41,7 +41,9 @@ METRIC = "ms per fused mixed-dtype pack + achieved HBM GB/s (% of MI355X peak)"
 HBM_PEAK_GBPS = 8000.0
 PAGES_H100_FUSED_MS = 0.1888      # isolated H100 test, 50.3M-element layout (context only)
 PAGES_H100_PRECAST_MS = 0.3582
-KERNEL_SOURCE = os.path.join(ROOT, "fsdp2_mixed_dtype_amd", "csrc", "fsdppack_kernels.hip")
+# the sources that decide what a pack launch reads and writes
+KERNEL_SOURCES = [os.path.join(ROOT, "fsdp2_mixed_dtype_amd", "csrc", f)
+                  for f in ("fsdppack_kernels.hip", "fsdppack_internal.h", "fsdppack_plan.cpp")]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "pack_traffic.json")
 
 
@@ -62,8 +64,11 @@ def parse():
 
 
 def kernel_source_hash():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def main():

@@ -148,13 +148,15 @@ int acquire_table(PtrCache &c, const std::vector<uint64_t> &key, hipStream_t str
 int run_op(fsdppack_plan *p, const OpTable &op, size_t cache_index, const std::vector<uint64_t> &key, char *base,
            void *stream, const char *what)
 {
-    if (op.n_windows <= 0) return FSDPPACK_OK;
+    // window boundaries follow the cache lines of memory, not the buffer's start
+    const int32_t shift = static_cast<int32_t>(reinterpret_cast<uintptr_t>(base) & (kLineBytes - 1));
+    if (op.windows(shift) <= 0) return FSDPPACK_OK;
     std::lock_guard<std::mutex> lock(p->mu);
     if (int rc = ensure_device(p)) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     PtrSlot *slot = nullptr;
     if (int rc = acquire_table(p->caches[cache_index], key, s, &slot)) return rc;
-    WindowArgs args = op.args(true);
+    WindowArgs args = op.args(true, shift);
     args.W = p->W;
     args.table = slot->d_table;
     args.base = base;

@@ -10,14 +10,20 @@
 // table; the other side is an offset into the call's single packed buffer.
 //
 // Work is cut into fixed *windows* of kWindowBytes of destination, one per
-// workgroup.  A workgroup finds its ranges arithmetically from its window
-// index plus small per-plan tables (a column map and member records for the
-// pack, a binary search over member offsets for the all-gather copies).  The
-// tables are a few KB to a few hundred KB and read by many workgroups, so
-// they stay resident in the scalar cache and L2: no workgroup waits on a
-// cold record of its own before touching data (a per-workgroup record, read
-// cold, measured ~20 % slower on MI355X), and the dependent table reads in
-// front of a wave's data are kept to two for the pack.  The mapping functions below are compiled both for the device
+// workgroup.  For the pack (per row) and the copy-in, window boundaries sit
+// on cache-line boundaries of memory (the launch passes how far the buffer
+// starts past one), so a line is written by one workgroup only: a line split
+// between two workgroups, possibly on different XCDs with separate L2s,
+// reaches HBM as two partial writes.  A workgroup finds its ranges
+// arithmetically from its window index plus small per-plan tables: a map
+// with one entry per kWindowBytes of a row (pack, copy-in) or per group of
+// windows (copy-out) that names the records to visit, and the records.  The
+// tables are a few KB to a few hundred KB and every entry is read by many
+// workgroups, so they stay resident in the scalar cache and L2: no workgroup
+// waits on a cold record of its own before touching data (a per-workgroup
+// record, read cold, measured ~20 % slower on MI355X), and a wave makes two
+// rounds of table reads before its data (a binary search over hundreds of
+// records would make nine).  The mapping functions below are compiled both for the device
 // (the kernels) and for the host (the planner's bounds checker), so the
 // checker runs exactly the code the kernels run.
 #pragma once
@@ -49,7 +55,12 @@ inline bool dtype_ok(int32_t dt) { return dt == kBF16 || dt == kFP32; }
 
 // Destination bytes per workgroup (one wave64 moving two 16-byte vectors
 // per lane).
-constexpr int64_t kWindowBytes = 2048;
+constexpr int kWindowLog2 = 11;
+constexpr int64_t kWindowBytes = int64_t{1} << kWindowLog2;
+// Cache line of the L2 (window boundaries are aligned to it in memory).
+constexpr int64_t kLineBytes = 128;
+// Copy-out windows per entry of its group map.
+constexpr int kGroupLog2 = 6;
 
 // Which side of a range is the caller's tensor (reached through the pointer
 // table); the other side is the call's packed buffer.
@@ -70,8 +81,11 @@ struct PackMember {
 };
 static_assert(sizeof(PackMember) == 32, "shared with the device");
 
-// The members a pack column window overlaps: first, first + 1, ...,
-// first + count - 1.  One entry per window of a row, shared by all W rows.
+// The records a stretch of work touches: first, first + 1, ...,
+// first + count - 1.  Pack: the members overlapping columns [x*E, (x+1)*E)
+// of a row (E = kWindowBytes of elements), shared by all W rows.  Copy-in:
+// the members overlapping bytes [x*kWindowBytes, (x+1)*kWindowBytes) of the
+// row.  Copy-out: the tensors owning windows [j*64, (j+1)*64).
 struct ColumnWindow {
     int32_t first;
     int32_t count;
@@ -108,13 +122,15 @@ struct WindowArgs {
     int32_t op;              // kOpPack / kOpCopyIn / kOpCopyOut
     int32_t n;               // entries of `members`
     int32_t n_windows;       // workgroups
-    int32_t gx;              // pack: windows per row
+    int32_t gx;              // pack: entries of the column map (windows per row: gx + 1)
     int32_t W;               // world size
     int32_t dst_dt;          // pack: reduction dtype
+    int32_t shift;           // pack / copy-in: bytes the destination starts past a cache-line boundary
+    int32_t group_lg;        // pack: rows interleaved per row group, log2 (W is a multiple of 2^group_lg)
     int64_t S;               // pack: row length in elements
     int64_t B;               // copy-in row bytes / copy-out row stride
     const void *members;     // PackMember / CopyInMember / CopyOutTensor array
-    const void *columns;     // pack: ColumnWindow per window of a row
+    const void *columns;     // ColumnWindow map: per kWindowBytes of a row (pack, copy-in) or per group (copy-out)
     const uint64_t *table;   // device pointer table, indexed by slot
     char *base;              // the call's packed buffer (destination or source)
 };
@@ -142,6 +158,26 @@ FSDPPACK_HD inline uint64_t table_entry(const WindowArgs &a, int32_t slot)
     return a.table ? ((const FSDPPACK_TABLE uint64_t *)a.table)[slot] : 0;
 }
 
+// Record m of a table of 32-byte records, in one scalar load.  Read field by
+// field, the compiler may defer the fields a later branch does not test (a
+// second wait on the scalar cache before the wave's first data load), and it
+// reads a 16-bit field with a vector load, whose wait also waits for every
+// store the wave has issued.
+template <typename T>
+FSDPPACK_HD inline T read_record(const void *table, int32_t m)
+{
+    static_assert(sizeof(T) == 32, "32-byte records");
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+    const u32x8 v = ((const FSDPPACK_TABLE u32x8 *)table)[m];
+    T rec;
+    __builtin_memcpy(&rec, &v, sizeof rec);
+    return rec;
+#else
+    return static_cast<const T *>(table)[m];
+#endif
+}
+
 FSDPPACK_HD inline int64_t imin(int64_t a, int64_t b) { return a < b ? a : b; }
 FSDPPACK_HD inline int64_t imax(int64_t a, int64_t b) { return a > b ? a : b; }
 
@@ -152,32 +188,66 @@ FSDPPACK_HD inline int64_t udiv(int64_t a, int64_t b)
     return static_cast<int64_t>(static_cast<uint64_t>(a) / static_cast<uint64_t>(b));
 }
 
-// Pack window w: row r = w / gx, columns [x*E, min(S, (x+1)*E)) with x = w %
-// gx and E the window in elements.  The column map names the members the
-// window overlaps, so a wave needs two dependent table reads (the column
-// entry, then the member record and its pointer together) before its data.
+// Bytes [y0, y1) of a destination of `total` bytes that window w covers when
+// the destination starts `shift` bytes past a cache-line boundary: window
+// boundaries fall on line boundaries of memory.
+FSDPPACK_HD inline void window_span(int32_t w, int32_t shift, int64_t total, int64_t &y0, int64_t &y1)
+{
+    const int64_t start = (static_cast<int64_t>(w) << kWindowLog2) - shift;
+    y0 = imax(0, start);
+    y1 = imin(total, start + kWindowBytes);
+}
+
+// Row r and window k of that row for pack window w.  Every row has gx + 1
+// windows; rows go in groups of G = 2^group_lg, and inside a group the
+// windows interleave row by row (window k of rows g*G ... g*G + G - 1, then
+// window k + 1): with small rank chunks, the windows in flight then read a
+// few contiguous stretches of each gradient instead of many scattered ones.
+FSDPPACK_HD inline void pack_row_window(const WindowArgs &a, int32_t w, int32_t &r, int32_t &k)
+{
+    const int32_t span = (a.gx + 1) << a.group_lg;       // windows per row group
+    const int32_t g = w / span, within = w - g * span;
+    k = within >> a.group_lg;
+    r = (g << a.group_lg) + (within & ((1 << a.group_lg) - 1));
+}
+
+// Pack window w: window k of row r (pack_row_window).  The row's window
+// boundaries sit on line boundaries of memory: window k covers bytes
+// [k*kWindowBytes - s_r, (k+1)*kWindowBytes - s_r) of the row, clipped to it,
+// with s_r how far the row starts past a line boundary (a row's last window
+// is empty when its bytes fit in gx windows).  Its columns [c0, c1) lie in one
+// or two windows of the column map, whose entries name the members to visit:
+// a wave makes two rounds of table reads (the column entries, then each
+// member record with its pointer) before its data.
 template <typename F>
 FSDPPACK_HD inline void pack_window(const WindowArgs &a, int32_t w, F &&f)
 {
-    const FSDPPACK_TABLE PackMember *M = (const FSDPPACK_TABLE PackMember *)a.members;
     const FSDPPACK_TABLE ColumnWindow *C = (const FSDPPACK_TABLE ColumnWindow *)a.columns;
-    const int64_t dsz = dtype_bytes(a.dst_dt);
-    const int64_t E = kWindowBytes / dsz;
-    const int32_t r = w / a.gx, x = w % a.gx;
-    const int64_t c0 = static_cast<int64_t>(x) * E, c1 = imin(a.S, c0 + E);
-    const ColumnWindow cw = C[x];
-    for (int32_t i = 0; i < cw.count; ++i) {
-        const int32_t m = cw.first + i;
+    const int lg = a.dst_dt == kBF16 ? 1 : 2;            // log2 of the element size
+    int32_t r, k;
+    pack_row_window(a, w, r, k);
+    const int64_t rb = a.S << lg;                         // bytes per row
+    const int32_t s_r = static_cast<int32_t>((a.shift + r * rb) & (kLineBytes - 1));
+    int64_t y0, y1;
+    window_span(k, s_r, rb, y0, y1);
+    if (y1 <= y0) return;                                 // the row's spare window
+    const int64_t c0 = y0 >> lg, c1 = y1 >> lg;
+    const int32_t x0 = static_cast<int32_t>(c0 >> (kWindowLog2 - lg));
+    const int32_t x1 = static_cast<int32_t>((c1 - 1) >> (kWindowLog2 - lg));
+    const int32_t m0 = C[x0].first;
+    const ColumnWindow last = C[x1];
+    for (int32_t m = m0; m < last.first + last.count; ++m) {
         const uint64_t ptr = table_entry(a, m);          // issued with the member read
-        const PackMember pm = M[m];
+        const PackMember pm = read_record<PackMember>(a.members, m);
         const int64_t b0 = imax(c0, pm.O), b1 = imin(c1, pm.O + pm.P);
+        if (b1 <= b0) continue;                          // in the column window, not in this window
         RangeRef g;
         g.ptr = ptr;
-        g.src_off = static_cast<int64_t>(r) * pm.P * dtype_bytes(pm.src_dt);
-        g.dst_off = (static_cast<int64_t>(r) * a.S + pm.O) * dsz;
+        g.src_off = r * pm.P * dtype_bytes(pm.src_dt);
+        g.dst_off = (r * a.S + pm.O) << lg;
         g.lo = b0 - pm.O;
         g.hi = b1 - pm.O;
-        g.valid = imax(0, imin(pm.P, pm.numel - static_cast<int64_t>(r) * pm.P));
+        g.valid = imax(0, imin(pm.P, pm.numel - r * pm.P));
         g.slot = m;
         g.param = pm.param;
         g.src_dt = pm.src_dt;
@@ -187,22 +257,21 @@ FSDPPACK_HD inline void pack_window(const WindowArgs &a, int32_t w, F &&f)
     }
 }
 
-// Copy-in window w: bytes [w*kWindowBytes, ...) of the row; members by
-// binary search on A.  Every member's span is a multiple of 16 bytes.
+// Copy-in window w: bytes [y0, y1) of the row, which lie in one or two
+// kWindowBytes stretches of the member map.  Every member's span is a
+// multiple of 16 bytes.
 template <typename F>
 FSDPPACK_HD inline void copy_in_window(const WindowArgs &a, int32_t w, F &&f)
 {
-    const FSDPPACK_TABLE CopyInMember *M = (const FSDPPACK_TABLE CopyInMember *)a.members;
-    const int64_t y0 = static_cast<int64_t>(w) * kWindowBytes, y1 = imin(a.B, y0 + kWindowBytes);
-    int32_t lo = 0, hi = a.n - 1;                        // last member with A <= y0
-    while (lo < hi) {
-        const int32_t mid = (lo + hi + 1) >> 1;
-        if (M[mid].A <= y0) lo = mid; else hi = mid - 1;
-    }
-    for (int32_t m = lo; m < a.n && M[m].A < y1; ++m) {
-        const CopyInMember cm = M[m];
+    const FSDPPACK_TABLE ColumnWindow *C = (const FSDPPACK_TABLE ColumnWindow *)a.columns;
+    int64_t y0, y1;
+    window_span(w, a.shift, a.B, y0, y1);
+    const int32_t m0 = C[y0 >> kWindowLog2].first;
+    const ColumnWindow last = C[(y1 - 1) >> kWindowLog2];
+    for (int32_t m = m0; m < last.first + last.count; ++m) {
+        const CopyInMember cm = read_record<CopyInMember>(a.members, m);
         const int64_t b0 = imax(y0, cm.A), b1 = imin(y1, cm.A_next);
-        if (b1 <= b0) continue;
+        if (b1 <= b0) continue;                          // in the map's stretch, not in this window
         const int64_t esz = dtype_bytes(cm.dst_dt);
         RangeRef g;
         g.ptr = table_entry(a, cm.slot);
@@ -220,14 +289,17 @@ FSDPPACK_HD inline void copy_in_window(const WindowArgs &a, int32_t w, F &&f)
     }
 }
 
-// Copy-out window w: the tensor whose windows contain w (binary search on
-// win0), bytes [x*kWindowBytes, ...) of that tensor, split at rank-chunk
-// boundaries; chunk r comes from byte r*B + A of the gathered buffer.
+// Copy-out window w: the tensor whose windows contain w (a binary search on
+// win0 among the few tensors the group map names for w's group), bytes
+// [x*kWindowBytes, ...) of that tensor (windows start at each tensor's own
+// first byte; `shift` is unused), split at rank-chunk boundaries; chunk r
+// comes from byte r*B + A of the gathered buffer.
 template <typename F>
 FSDPPACK_HD inline void copy_out_window(const WindowArgs &a, int32_t w, F &&f)
 {
     const FSDPPACK_TABLE CopyOutTensor *T = (const FSDPPACK_TABLE CopyOutTensor *)a.members;
-    int32_t lo = 0, hi = a.n - 1;                        // last tensor with win0 <= w
+    const ColumnWindow grp = ((const FSDPPACK_TABLE ColumnWindow *)a.columns)[w >> kGroupLog2];
+    int32_t lo = grp.first, hi = grp.first + grp.count - 1;   // last tensor with win0 <= w
     while (lo < hi) {
         const int32_t mid = (lo + hi + 1) >> 1;
         if (T[mid].win0 <= w) lo = mid; else hi = mid - 1;

@@ -22,11 +22,12 @@ namespace fsdppack {
 struct OpTable {
     int32_t op = kOpPack;
     std::vector<unsigned char> members;   // PackMember / CopyInMember / CopyOutTensor records
-    std::vector<ColumnWindow> columns;    // pack: per window of a row
+    std::vector<ColumnWindow> columns;    // record map (pack, copy-in: per kWindowBytes of a row; copy-out: per window group)
     std::vector<int32_t> table_params;    // pointer-table entry -> parameter index
     int32_t n = 0;                        // records
-    int32_t n_windows = 0;                // workgroups per launch
-    int32_t gx = 0;                       // pack: windows per row
+    int32_t n_windows = 0;                // workgroups per launch (pack / copy-in: destination window-aligned)
+    int32_t gx = 0;                       // pack: column-map entries
+    int32_t group_lg = 0;                 // pack: log2 of the rows interleaved per row group
     int32_t dst_dt = 0;                   // pack: reduction dtype
     int64_t S = 0;                        // pack: row length (elements)
     int64_t B = 0;                        // all-gather row bytes
@@ -41,14 +42,28 @@ struct OpTable {
         members.insert(members.end(), p, p + sizeof(T));
         ++n;
     }
+    // Workgroups of a launch whose destination starts `shift` bytes past a
+    // cache-line boundary: the pack gives every row gx + 1 windows (enough
+    // for any alignment of the row), the copy-in cuts its row at line
+    // boundaries of memory, and the copy-out's windows start at each
+    // parameter's first byte.
+    int64_t windows(int32_t shift) const
+    {
+        if (op == kOpCopyOut) return n_windows;
+        if (dst_bytes == 0) return 0;
+        if (op == kOpPack) return (static_cast<int64_t>(gx) + 1) * (dst_bytes / (S * dtype_bytes(dst_dt)));
+        return (shift + dst_bytes + kWindowBytes - 1) >> kWindowLog2;
+    }
     // launch arguments against host (`device == false`) or device members
-    WindowArgs args(bool device) const
+    WindowArgs args(bool device, int32_t shift) const
     {
         WindowArgs a{};
         a.op = op;
         a.n = n;
-        a.n_windows = n_windows;
+        a.shift = op == kOpCopyOut ? 0 : shift;
+        a.n_windows = static_cast<int32_t>(windows(a.shift));
         a.gx = gx;
+        a.group_lg = group_lg;
         a.dst_dt = dst_dt;
         a.S = S;
         a.B = B;

@@ -9,7 +9,14 @@
 //    `valid` prefix, and writes inside its destination buffer;
 //  * ranges use a valid pointer-table slot and supported dtypes;
 //  * over all windows of a launch, every destination byte is written exactly
-//    once (checked on the sorted list of written intervals).
+//    once (checked on the sorted list of written intervals);
+//  * for the pack and the copy-in, whose windows follow memory, each window
+//    starts and ends on a cache-line boundary of memory unless it starts or
+//    ends with its row, for several offsets of the destination past a line
+//    boundary; only the pack's spare window at the end of a row may have no
+//    range;
+//  * the record maps have one entry per kWindowBytes of a row (pack,
+//    copy-in) or per group of windows (copy-out).
 //
 // Input (stdin): "world n" then n lines
 // "dim0 inner grad reduce storage param".  Prints "OK" or the first failure.
@@ -40,8 +47,8 @@ using Intervals = std::vector<std::pair<int64_t, int64_t>>;
 
 // Check one range produced for window w.
 template <typename DstSize, typename SrcSize>
-static bool check_range(const char *name, int32_t w, const RangeRef &g, const OpTable &op, int32_t nparams,
-                        DstSize dst_size, SrcSize src_size, std::vector<Intervals> &written)
+static bool check_range(const char *name, int32_t w, int32_t shift, const RangeRef &g, const OpTable &op,
+                        int32_t nparams, DstSize dst_size, SrcSize src_size, std::vector<Intervals> &written)
 {
     CHECK(dtype_ok(g.src_dt) && dtype_ok(g.dst_dt), "%s: window %d bad dtype", name, w);
     const int32_t entries = op.op == kOpPack ? op.n : nparams;     // pointer-table entries
@@ -64,26 +71,54 @@ static bool check_range(const char *name, int32_t w, const RangeRef &g, const Op
 }
 
 template <typename DstSize, typename SrcSize>
-static bool check_op(const char *name, const OpTable &op, int32_t W, int32_t nparams, DstSize dst_size,
-                     SrcSize src_size, std::vector<Intervals> &written)
+static bool check_op(const char *name, const OpTable &op, int32_t W, int32_t shift, int32_t nparams,
+                     DstSize dst_size, SrcSize src_size, std::vector<Intervals> &written)
 {
-    WindowArgs a = op.args(false);
+    WindowArgs a = op.args(false, shift);
     a.W = W;
+    CHECK(a.n_windows == op.windows(shift) && (shift != 0 || a.n_windows == op.n_windows), "%s: window count", name);
     const size_t rec = op.op == kOpPack ? sizeof(PackMember)
                        : op.op == kOpCopyIn ? sizeof(CopyInMember) : sizeof(CopyOutTensor);
     CHECK(op.members.size() == static_cast<size_t>(op.n) * rec, "%s: member table size", name);
     CHECK(op.n_windows == 0 || op.n > 0, "%s: windows without members", name);
     CHECK(op.op != kOpPack || (op.columns.size() == static_cast<size_t>(op.gx) &&
                                op.table_params.size() == static_cast<size_t>(op.n)), "%s: column map size", name);
-    for (int32_t w = 0; w < op.n_windows; ++w) {
+    CHECK(op.op != kOpCopyIn || op.columns.size() == static_cast<size_t>((op.B + kWindowBytes - 1) / kWindowBytes),
+          "%s: member map size", name);
+    CHECK(op.op != kOpCopyOut ||
+              op.columns.size() == static_cast<size_t>((op.n_windows + (1 << kGroupLog2) - 1) >> kGroupLog2),
+          "%s: group map size", name);
+    for (int32_t w = 0; w < a.n_windows; ++w) {
         int ranges = 0;
         bool ok = true;
+        int64_t lo = INT64_MAX, hi = INT64_MIN;       // bytes the window writes, from the aligned origin
         for_each_range(a, w, [&](const RangeRef &g) {
-            if (ok) ok = check_range(name, w, g, op, nparams, dst_size, src_size, written);
+            if (ok) ok = check_range(name, w, a.shift, g, op, nparams, dst_size, src_size, written);
+            const int64_t dsz = dtype_bytes(g.dst_dt);
+            lo = std::min(lo, a.shift + g.dst_off + g.lo * dsz);
+            hi = std::max(hi, a.shift + g.dst_off + g.hi * dsz);
             ++ranges;
         });
         if (!ok) return false;
-        CHECK(ranges > 0, "%s: window %d has no range", name, w);
+        int64_t row0 = shift, row1 = shift + op.B;        // the window's row, from the aligned origin
+        if (op.op == kOpPack) {
+            // window k of row r is empty exactly when the row ends before it
+            int32_t r, k;
+            pack_row_window(a, w, r, k);
+            const int64_t rb = op.S * dtype_bytes(op.dst_dt);
+            const int64_t s_r = (shift + r * rb) % kLineBytes;
+            const bool spare = static_cast<int64_t>(k) * kWindowBytes - s_r >= rb;
+            CHECK((ranges == 0) == spare, "%s: window %d (row %d, shift %d) has %d ranges", name, w, r, shift, ranges);
+            row0 = shift + r * rb;
+            row1 = row0 + rb;
+        } else {
+            CHECK(ranges > 0, "%s: window %d has no range", name, w);
+        }
+        if (op.op != kOpCopyOut && ranges > 0)
+            CHECK((lo == row0 || lo % kLineBytes == 0) && (hi == row1 || hi % kLineBytes == 0) &&
+                      hi - lo <= kWindowBytes,
+                  "%s: window %d (shift %d) writes [%lld,%lld) from the aligned origin, off the line boundaries",
+                  name, w, shift, (long long)lo, (long long)hi);
     }
     return true;
 }
@@ -122,24 +157,40 @@ int main()
     }
     const int64_t W = plan.W;
     auto grad_bytes = [&](const RangeRef &g) { return plan.numel[g.param] * dtype_bytes(plan.params[g.param].grad_dtype); };
+    // destination offsets past a window boundary: the pack's output is only
+    // element aligned, the copy-in row 4-byte aligned
+    const int32_t kShiftUnits[] = {0, 1, 4, 27, 31};
     for (size_t bi = 0; bi < plan.buckets.size(); ++bi) {
         const BucketPlan &b = plan.buckets[bi];
         const int64_t out_bytes = W * b.S * dtype_bytes(b.dtype);
-        std::vector<Intervals> written(1);
-        char name[64];
-        std::snprintf(name, sizeof name, "pack[%zu]", bi);
-        if (!check_op(name, b.pack, plan.W, n, [&](const RangeRef &) { return out_bytes; }, grad_bytes, written) ||
-            !tiles(written[0], out_bytes, name)) {
-            std::printf("FAIL %s\n", g_fail.c_str());
-            return 1;
+        // the planner's row grouping, and every other one the world size allows
+        for (int32_t glg = -1; glg <= 3; ++glg) {
+            if (glg >= 0 && (glg == b.pack.group_lg || W % (1 << glg) != 0)) continue;
+            OpTable op = b.pack;
+            if (glg >= 0) op.group_lg = glg;
+            for (int32_t u : kShiftUnits) {
+                const int32_t shift = static_cast<int32_t>((u * dtype_bytes(b.dtype)) % kLineBytes);
+                std::vector<Intervals> written(1);
+                char name[80];
+                std::snprintf(name, sizeof name, "pack[%zu] rows/group %d shift %d", bi, 1 << op.group_lg, shift);
+                if (!check_op(name, op, plan.W, shift, n, [&](const RangeRef &) { return out_bytes; }, grad_bytes,
+                              written) ||
+                    !tiles(written[0], out_bytes, name)) {
+                    std::printf("FAIL %s\n", g_fail.c_str());
+                    return 1;
+                }
+            }
         }
     }
-    {
+    for (int32_t u : kShiftUnits) {
+        const int32_t shift = (u * 4) % static_cast<int32_t>(kLineBytes);
         std::vector<Intervals> written(1);
+        char name[64];
+        std::snprintf(name, sizeof name, "copy_in shift %d", shift);
         auto shard_bytes = [&](const RangeRef &g) { return plan.P[g.param] * dtype_bytes(plan.params[g.param].storage_dtype); };
-        if (!check_op("copy_in", plan.copy_in, plan.W, n, [&](const RangeRef &) { return plan.B; }, shard_bytes,
+        if (!check_op(name, plan.copy_in, plan.W, shift, n, [&](const RangeRef &) { return plan.B; }, shard_bytes,
                       written) ||
-            !tiles(written[0], plan.B, "copy_in")) {
+            !tiles(written[0], plan.B, name)) {
             std::printf("FAIL %s\n", g_fail.c_str());
             return 1;
         }
@@ -147,7 +198,7 @@ int main()
     {
         std::vector<Intervals> written(n);
         auto param_bytes = [&](const RangeRef &g) { return plan.numel[g.param] * dtype_bytes(plan.params[g.param].param_dtype); };
-        if (!check_op("copy_out", plan.copy_out, plan.W, n, param_bytes, [&](const RangeRef &) { return W * plan.B; },
+        if (!check_op("copy_out", plan.copy_out, plan.W, 0, n, param_bytes, [&](const RangeRef &) { return W * plan.B; },
                       written)) {
             std::printf("FAIL %s\n", g_fail.c_str());
             return 1;
@@ -162,7 +213,7 @@ int main()
         }
     }
     std::printf("OK %zu buckets, windows:", plan.buckets.size());
-    for (const BucketPlan &b : plan.buckets) std::printf(" %d", b.pack.n_windows);
+    for (const BucketPlan &b : plan.buckets) std::printf(" %d (rows/group %d)", b.pack.n_windows, 1 << b.pack.group_lg);
     std::printf(" copy_in %d copy_out %d\n", plan.copy_in.n_windows, plan.copy_out.n_windows);
     return 0;
 }
