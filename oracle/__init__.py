@@ -1,5 +1,6 @@
-"""Plain CPU oracle for FSDP2's mixed-dtype reduce-scatter pack and its
-all-gather copy-in / copy-out.
+"""Plain CPU oracle for FSDP2's mixed-dtype reduce-scatter pack, the write-back
+of a reduce-scatter output into sharded gradients, and the all-gather
+copy-in / copy-out.
 
 TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by ``__graft_entry__.smoke()``
 and by the CPU-baseline leg of ``bench.py``.  The product package never imports
@@ -71,7 +72,9 @@ def _load():
         lib.oracle_copy_in.argtypes = [i32, i32, vp, vp, vp, vp, vp, i64, vp]
         lib.oracle_copy_out.argtypes = [i32, i32, vp, i64, vp, vp, vp, vp, vp]
         lib.oracle_convert.argtypes = [vp, i32, vp, i32, i64]
-        for f in (lib.oracle_pack, lib.oracle_unpack, lib.oracle_copy_in, lib.oracle_copy_out):
+        lib.oracle_rs_copy_out.argtypes = [i32, i32, vp, i32, i64, ctypes.c_float, vp, vp, vp, vp, vp]
+        for f in (lib.oracle_pack, lib.oracle_unpack, lib.oracle_copy_in, lib.oracle_copy_out,
+                  lib.oracle_rs_copy_out):
             f.restype = ctypes.c_int
         lib.oracle_convert.restype = None
         _lib = lib
@@ -254,6 +257,26 @@ def copy_out(pl: Plan, ag: np.ndarray):
     pdt = _i32([p.param_dtype for p in pl.params])
     _load().oracle_copy_out(pl.W, len(outs), ag.ctypes.data, pl.B, A.ctypes.data, P.ctypes.data,
                             numel.ctypes.data, pdt.ctypes.data, _ptrs(outs))
+    return outs
+
+
+def rs_copy_out(pl: Plan, bucket: int, rank: int, row: np.ndarray, divide_factor: float = 1.0):
+    """Rank `rank`'s sharded gradients of the members of bucket `bucket` (in
+    member order; each the rank chunk's real elements, in the member's storage
+    dtype) from the rank's reduced row: S elements of the bucket dtype,
+    divided by `divide_factor` (a binary32 value) in that dtype unless it is 1."""
+    b = pl.buckets[bucket]
+    row = np.ascontiguousarray(row).reshape(-1)
+    _check(row, b.dtype, b.S)
+    outs = [np.zeros(valid_in_chunk(pl.params[i].numel, P, rank), dtype=NP_DTYPE[pl.params[i].storage_dtype])
+            for i, P in zip(b.members, b.P)]
+    numel = _i64([pl.params[i].numel for i in b.members])
+    sdt = _i32([pl.params[i].storage_dtype for i in b.members])
+    P, O = _i64(b.P), _i64(b.O)
+    rc = _load().oracle_rs_copy_out(rank, len(outs), row.ctypes.data, b.dtype, b.S, float(np.float32(divide_factor)),
+                                    numel.ctypes.data, P.ctypes.data, O.ctypes.data, sdt.ctypes.data, _ptrs(outs))
+    if rc:
+        raise RuntimeError("oracle_rs_copy_out: bad layout")
     return outs
 
 

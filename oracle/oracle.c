@@ -41,6 +41,13 @@
  *    aligned, in unit order, zero gap bytes) are a reading the pages leave
  *    open: parity unpinned for the layout beyond that round trip and the
  *    closed-form offsets.
+ *  - oracle_rs_copy_out: torch's CPU division of the reduced row by a tensor
+ *    of the divide factor, then its cast to the storage dtype, on every
+ *    non-NaN element (the two operations FSDP2 applies to a reduce-scatter
+ *    output); with no divide, the unpacked pack cast to the storage dtype;
+ *    the divide of W summed identical rows by a power-of-two W gives the row
+ *    back exactly.  The NaN rule of the divide (not divided, quiet bit set) is
+ *    a reading: parity unpinned for NaN payloads there.
  */
 #include <stddef.h>
 #include <stdint.h>
@@ -100,6 +107,33 @@ static void store_as(void *base, int32_t dtype, int64_t i, uint32_t bits)
         ((uint16_t *)base)[i] = (uint16_t)bits;
     else
         ((uint32_t *)base)[i] = bits;
+}
+
+/* An element's bit pattern cast from one dtype to another. */
+static uint32_t cast_bits(uint32_t bits, int32_t from, int32_t to)
+{
+    if (from == to) return bits;
+    if (from == ORACLE_BF16) return oracle_bf16_to_f32_bits((uint16_t)bits);
+    return (uint32_t)oracle_f32_to_bf16_bits(bits);
+}
+
+/* An element of `dtype` divided by d in that dtype: the quotient of the
+ * element's binary32 value by d, correctly rounded to binary32 (the host
+ * compiler's IEEE single-precision division), then rounded once more to
+ * bfloat16 when that is the dtype.  A NaN is not divided; it keeps its sign
+ * and payload and gets the quiet bit. */
+static uint32_t divide_in(uint32_t bits, int32_t dtype, float d)
+{
+    uint32_t f = cast_bits(bits, dtype, ORACLE_FP32);
+    if (((f >> 23) & 0xFFu) == 0xFFu && (f & 0x7FFFFFu) != 0u) {
+        f |= 0x00400000u;
+    } else {
+        float x;
+        memcpy(&x, &f, sizeof x);
+        x = x / d;
+        memcpy(&f, &x, sizeof f);
+    }
+    return cast_bits(f, ORACLE_FP32, dtype);
 }
 
 /* Number of source elements that land in rank r's chunk of a tensor with
@@ -200,6 +234,38 @@ int oracle_copy_out(int32_t W, int32_t n, const void *ag, int64_t B, const int64
             for (int64_t j = 0; j < v; ++j)
                 store_as(params[t], param_dtype[t], r * P[t] + j,
                          load_as(seg, param_dtype[t], j, param_dtype[t]));
+        }
+    }
+    return 0;
+}
+
+/*
+ * Reduce-scatter output write-back for one rank: the step after the
+ * reduce-scatter on the gradient path, where each rank keeps the gradient
+ * slice of the parameters it owns ("The unit you wrapped", the paragraphs on
+ * the collectives FSDP issues), in the resident parameter's dtype
+ * ("Mixed-Precision Training": reduce_dtype only sets how gradients are
+ * summed; the gradient buffer follows the resident parameter dtype).
+ *
+ * `row` holds the rank's S reduced elements of one bucket in the reduction
+ * dtype.  When divide_factor is not 1 each element is first divided by it in
+ * the reduction dtype (divide_in).  Member t then receives the real
+ * (non-padding) elements of its rank chunk, cast to its storage dtype:
+ *     grad_t[j] = cast(div(row[O[t] + j]))     for j < valid_rank(t)
+ * Returns 0, or -1 if a member's columns leave [0, S).
+ */
+int oracle_rs_copy_out(int32_t rank, int32_t n, const void *row, int32_t reduce_dtype, int64_t S,
+                       float divide_factor, const int64_t *numel, const int64_t *P, const int64_t *O,
+                       const int32_t *storage_dtype, void *const *grads)
+{
+    for (int32_t t = 0; t < n; ++t)
+        if (O[t] < 0 || P[t] < 0 || O[t] + P[t] > S) return -1;
+    for (int32_t t = 0; t < n; ++t) {
+        int64_t v = valid_in_chunk(numel[t], P[t], rank);
+        for (int64_t j = 0; j < v; ++j) {
+            uint32_t x = load_as(row, reduce_dtype, O[t] + j, reduce_dtype);
+            if (divide_factor != 1.0f) x = divide_in(x, reduce_dtype, divide_factor);
+            store_as(grads[t], storage_dtype[t], j, cast_bits(x, reduce_dtype, storage_dtype[t]));
         }
     }
     return 0;
