@@ -243,6 +243,35 @@ def main():
         extra["copy_ceiling_GBps"] = round(2 * (nbytes // 4) * 4 / (copy_ms * 1e-3) / 1e9, 1)
         del src, dst
 
+        # ---- reduce-scatter write-back of rank 0 (the step after the
+        # reduce-scatter): row 0 of each bucket's packed buffer stands in for
+        # the rank's reduced row, divided by W and cast to the storage dtypes
+        wb_bytes = 0
+        for bi, b in enumerate(plan.buckets):
+            for i in b.members:
+                wb_bytes += fp.valid_in_chunk(plan, i, 0) * (esz(b.dtype) + esz(w.tensors[i].storage_dtype))
+        wsets = []
+        for r in range(R):
+            per_bucket = []
+            for bi, b in enumerate(plan.buckets):
+                dsts = [torch.empty(fp.valid_in_chunk(plan, i, 0), dtype=fp.TORCH_DTYPE[t.storage_dtype], device=dev)
+                        if i in b.members else None for i, t in enumerate(w.tensors)]
+                per_bucket.append((sets[r][1][bi][:b.S], fp.prepare_shard_grads(plan, bi, 0, dsts)))
+            wsets.append(per_bucket)
+        e_w = [[(new_event(), new_event()) for _ in range(nb)] for _ in range(K)]
+        for i in range(args.warmup + K):
+            for bi in range(nb):
+                row, dsts = wsets[i % R][bi]
+                timed(e_w[i - args.warmup][bi] if i >= args.warmup else None)
+                fp.reduce_scatter_copy_out(plan, bi, 0, row, dsts, float(W), stream)
+        torch.cuda.synchronize()
+        wb_ms = sum(a.elapsed_time(b) for e in e_w for a, b in e) / K
+        extra["rs_copy_out"] = {"ms": round(wb_ms, 5), "bytes": wb_bytes,
+                                "GBps": round(wb_bytes / (wb_ms * 1e-3) / 1e9, 1),
+                                "frac_of_peak": round(wb_bytes / (wb_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                                "rank": 0, "divide_factor": W, "buckets": nb}
+        del wsets
+
     if args.calib_copy:
         # plain device-to-device copies of a known size: what a byte counter
         # reads for them calibrates the counter against real traffic

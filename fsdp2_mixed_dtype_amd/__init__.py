@@ -1,5 +1,6 @@
 """Python binding of libfsdppack: FSDP2's mixed-dtype gradient pack for
-reduce-scatter and its all-gather copy-in / copy-out on MI355X (gfx950).
+reduce-scatter, the write-back of a reduce-scatter output into sharded
+gradients, and the all-gather copy-in / copy-out on MI355X (gfx950).
 
 This module only marshals arguments (torch tensors -> device pointers, the
 current HIP stream) and calls the C ABI declared in ``include/fsdppack.h``;
@@ -11,6 +12,7 @@ Functions (same names as the C ABI without the ``fsdppack_`` prefix):
   pack_reduce_scatter_input(plan, bucket, grads, out, stream=None)
   all_gather_copy_in(plan, rank, shards, ag_out, stream=None)
   all_gather_copy_out(plan, ag, params, stream=None)
+  reduce_scatter_copy_out(plan, bucket, rank, rs_out, shard_grads, divide_factor=1.0, stream=None)
 
 The tensor lists may also be given as a PointerArray from prepare_grads /
 prepare_shards / prepare_params: validated once and reused across calls, the
@@ -68,6 +70,7 @@ def lib():
         L.fsdppack_pack_reduce_scatter_input.argtypes = [vp, i32, vp, vp, vp]
         L.fsdppack_all_gather_copy_in.argtypes = [vp, i32, vp, vp, vp]
         L.fsdppack_all_gather_copy_out.argtypes = [vp, vp, vp, vp]
+        L.fsdppack_reduce_scatter_copy_out.argtypes = [vp, i32, i32, vp, ctypes.c_float, vp, vp]
         L.fsdppack_plan_destroy.argtypes = [vp]
         L.fsdppack_plan_destroy.restype = None
         L.fsdppack_last_error.argtypes = []
@@ -76,8 +79,8 @@ def lib():
         L.fsdppack_time_next_launch.argtypes = [vp, vp]
         for f in (L.fsdppack_plan_buckets, L.fsdppack_plan_info, L.fsdppack_plan_bucket,
                   L.fsdppack_plan_all_gather_layout, L.fsdppack_pack_reduce_scatter_input,
-                  L.fsdppack_all_gather_copy_in, L.fsdppack_all_gather_copy_out, L.fsdppack_counters,
-                  L.fsdppack_time_next_launch):
+                  L.fsdppack_all_gather_copy_in, L.fsdppack_all_gather_copy_out,
+                  L.fsdppack_reduce_scatter_copy_out, L.fsdppack_counters, L.fsdppack_time_next_launch):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -265,6 +268,53 @@ def all_gather_copy_out(plan: Plan, ag, params, stream=None):
     aptr = _bytes_ptr(ag, plan.world * plan.B, "ag")
     _check(lib().fsdppack_all_gather_copy_out(plan.handle, aptr, arr, _stream(stream)))
     return params
+
+
+def valid_in_chunk(plan: Plan, index: int, rank: int) -> int:
+    """Real (non-padding) elements of parameter `index` in rank `rank`'s chunk."""
+    P = plan.P[index]
+    return max(0, min(P, plan.numel[index] - rank * P))
+
+
+def prepare_shard_grads(plan: Plan, bucket: int, rank: int, grads) -> PointerArray:
+    """Sharded gradients by parameter index for the write-back of `bucket` on
+    `rank`: each member's entry holds the rank chunk's real elements (storage
+    dtype); entries of non-members and of members with nothing on this rank
+    may be None."""
+    if len(grads) != plan.n:
+        raise ValueError(f"shard_grads: expected {plan.n} entries, got {len(grads)}")
+    members = set(plan.buckets[bucket].members)
+    ptrs = []
+    for i, g in enumerate(grads):
+        v = valid_in_chunk(plan, i, rank)
+        if i in members and v:
+            ptrs.append(_ptr(g, plan.descs[i].storage_dtype, v, f"shard_grads[{i}]"))
+        else:
+            ptrs.append(0)
+    arr = PointerArray(plan, "shard_grads", grads, ptrs)
+    arr.bucket, arr.rank = bucket, rank
+    return arr
+
+
+def reduce_scatter_copy_out(plan: Plan, bucket: int, rank: int, rs_out, shard_grads, divide_factor: float = 1.0,
+                            stream=None):
+    """Write rank `rank`'s sharded gradients of the members of `bucket` from
+    the rank's reduced row `rs_out` (S elements of the bucket's reduction
+    dtype): each element divided by `divide_factor` in the reduction dtype
+    (unless it is 1), then cast to the member's storage dtype.  `shard_grads`
+    is indexed by parameter (see prepare_shard_grads)."""
+    b = plan.buckets[bucket]
+    if isinstance(shard_grads, PointerArray):
+        if (shard_grads.kind != "shard_grads" or shard_grads.plan_handle != plan.handle.value
+                or shard_grads.bucket != bucket or shard_grads.rank != rank):
+            raise ValueError("pointer array was prepared for another plan, bucket or rank")
+        arr = shard_grads.array
+    else:
+        arr = prepare_shard_grads(plan, bucket, rank, shard_grads).array
+    rptr = _ptr(rs_out, b.dtype, b.S, "rs_out")
+    _check(lib().fsdppack_reduce_scatter_copy_out(plan.handle, bucket, int(rank), rptr, float(divide_factor), arr,
+                                                  _stream(stream)))
+    return shard_grads
 
 
 def time_next_launch(start, stop):

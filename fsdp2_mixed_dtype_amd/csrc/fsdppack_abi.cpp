@@ -7,6 +7,7 @@
 // a training loop that passes the same buffers each step pays no upload.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdio>
 #include <cstdlib>
@@ -80,11 +81,13 @@ int ensure_device(fsdppack_plan *p)
                                              " but the current device is " + std::to_string(dev));
         return FSDPPACK_OK;
     }
-    for (BucketPlan &b : p->buckets)
+    for (BucketPlan &b : p->buckets) {
         if (int rc = upload_table(b.pack)) return rc;
+        if (int rc = upload_table(b.write_back)) return rc;
+    }
     if (int rc = upload_table(p->copy_in)) return rc;
     if (int rc = upload_table(p->copy_out)) return rc;
-    p->caches.resize(p->buckets.size() + 2);
+    p->caches.resize(2 * p->buckets.size() + 2);
     p->device = dev;
     p->uploaded = true;
     g_counters[3]++;
@@ -146,7 +149,7 @@ int acquire_table(PtrCache &c, const std::vector<uint64_t> &key, hipStream_t str
 
 // Run one operation: pointer-table lookup, then one kernel launch.
 int run_op(fsdppack_plan *p, const OpTable &op, size_t cache_index, const std::vector<uint64_t> &key, char *base,
-           void *stream, const char *what)
+           void *stream, const char *what, int32_t rank = 0, float divisor = 1.0f)
 {
     // window boundaries follow the cache lines of memory, not the buffer's start
     const int32_t shift = static_cast<int32_t>(reinterpret_cast<uintptr_t>(base) & (kLineBytes - 1));
@@ -160,6 +163,8 @@ int run_op(fsdppack_plan *p, const OpTable &op, size_t cache_index, const std::v
     args.W = p->W;
     args.table = slot->d_table;
     args.base = base;
+    args.rank = rank;
+    args.divisor = divisor;
     void *ev0 = g_next_start, *ev1 = g_next_stop;
     g_next_start = g_next_stop = nullptr;
     const int le = launch_windows(args, stream, ev0, ev1);
@@ -312,6 +317,42 @@ int fsdppack_all_gather_copy_out(const fsdppack_plan *cplan, const void *ag, voi
     }
 }
 
+int fsdppack_reduce_scatter_copy_out(const fsdppack_plan *cplan, int32_t bucket, int32_t rank, const void *rs_out,
+                                     float divide_factor, void *const *shard_grads, void *stream)
+{
+    fsdppack_plan *plan = const_cast<fsdppack_plan *>(cplan);
+    if (!plan_ok(plan)) return fail(FSDPPACK_ESTATE, "reduce_scatter_copy_out: invalid plan handle");
+    if (bucket < 0 || bucket >= static_cast<int32_t>(plan->buckets.size()))
+        return fail(FSDPPACK_EINVAL, "reduce_scatter_copy_out: bucket index out of range");
+    if (rank < 0 || rank >= plan->W) return fail(FSDPPACK_EINVAL, "reduce_scatter_copy_out: rank out of range");
+    if (!(divide_factor > 0.0f) || divide_factor > 3.4028235e38f)
+        return fail(FSDPPACK_EINVAL, "reduce_scatter_copy_out: divide_factor must be finite and positive");
+    if (shard_grads == nullptr) return fail(FSDPPACK_EINVAL, "reduce_scatter_copy_out: shard_grads is NULL");
+    BucketPlan &b = plan->buckets[bucket];
+    if (b.S > 0 && (rs_out == nullptr || !aligned(rs_out, dtype_bytes(b.dtype))))
+        return fail(FSDPPACK_EINVAL, "reduce_scatter_copy_out: rs_out is NULL or not aligned to its element size");
+    // the table is indexed by parameter; members with no real element on this
+    // rank (and non-members) are not touched and may be NULL
+    std::vector<uint64_t> key(plan->n, 0);
+    for (size_t k = 0; k < b.members.size(); ++k) {
+        const int32_t t = b.members[k];
+        const int64_t v = std::max<int64_t>(0, std::min<int64_t>(b.P[k], plan->numel[t] - int64_t{rank} * b.P[k]));
+        if (v == 0) continue;
+        void *g = shard_grads[t];
+        if (g == nullptr || !aligned(g, dtype_bytes(plan->params[t].storage_dtype)))
+            return fail(FSDPPACK_EINVAL, "reduce_scatter_copy_out: shard_grads[" + std::to_string(t) +
+                                             "] is NULL or not aligned to its element size");
+        key[t] = reinterpret_cast<uint64_t>(g);
+    }
+    try {
+        return run_op(plan, b.write_back, plan->buckets.size() + 2 + static_cast<size_t>(bucket), key,
+                      const_cast<char *>(static_cast<const char *>(rs_out)), stream, "reduce_scatter_copy_out", rank,
+                      divide_factor);
+    } catch (const std::bad_alloc &) {
+        return fail(FSDPPACK_ENOMEM, "reduce_scatter_copy_out: out of host memory");
+    }
+}
+
 void fsdppack_plan_destroy(fsdppack_plan *plan)
 {
     if (!plan_ok(plan)) return;
@@ -331,7 +372,10 @@ void fsdppack_plan_destroy(fsdppack_plan *plan)
             op.d_members = nullptr;
             op.d_columns = nullptr;
         };
-        for (BucketPlan &b : plan->buckets) free_table(b.pack);
+        for (BucketPlan &b : plan->buckets) {
+            free_table(b.pack);
+            free_table(b.write_back);
+        }
         free_table(plan->copy_in);
         free_table(plan->copy_out);
         plan->magic = 0;

@@ -66,7 +66,7 @@ constexpr int kGroupLog2 = 6;
 // table); the other side is the call's packed buffer.
 enum : int32_t { kTableIsSource = 0, kTableIsDest = 1 };
 
-enum : int32_t { kOpPack = 0, kOpCopyIn = 1, kOpCopyOut = 2 };
+enum : int32_t { kOpPack = 0, kOpCopyIn = 1, kOpCopyOut = 2, kOpWriteBack = 3 };
 
 // One bucket member of a reduce-scatter pack: columns [O, O + P) of every
 // row; `numel` elements of dtype src_dt.  The pack's pointer table is in
@@ -106,7 +106,10 @@ static_assert(sizeof(CopyInMember) == 32, "shared with the device");
 
 // One parameter of the all-gather copy-out: its windows start at window
 // index win0; numel elements of dtype dt, rank chunks of P elements found
-// at byte A of each all-gather row.
+// at byte A of each all-gather row.  The reduce-scatter write-back uses the
+// same record for a bucket member: its windows cover the P-element rank
+// chunk in the storage dtype dt, read from byte A = O * size(reduce dtype)
+// of the rank's reduced row.
 struct CopyOutTensor {
     int64_t win0;
     int64_t numel;
@@ -124,9 +127,11 @@ struct WindowArgs {
     int32_t n_windows;       // workgroups
     int32_t gx;              // pack: entries of the column map (windows per row: gx + 1)
     int32_t W;               // world size
-    int32_t dst_dt;          // pack: reduction dtype
+    int32_t reduce_dt;       // the bucket's reduction dtype (pack: destination; write-back: source)
     int32_t shift;           // pack / copy-in: bytes the destination starts past a cache-line boundary
     int32_t group_lg;        // pack: rows interleaved per row group, log2 (W is a multiple of 2^group_lg)
+    int32_t rank;            // write-back: the rank whose reduced row is written back
+    float divisor;           // write-back: divide factor (1: no division)
     int64_t S;               // pack: row length in elements
     int64_t B;               // copy-in row bytes / copy-out row stride
     const void *members;     // PackMember / CopyInMember / CopyOutTensor array
@@ -223,7 +228,7 @@ template <typename F>
 FSDPPACK_HD inline void pack_window(const WindowArgs &a, int32_t w, F &&f)
 {
     const FSDPPACK_TABLE ColumnWindow *C = (const FSDPPACK_TABLE ColumnWindow *)a.columns;
-    const int lg = a.dst_dt == kBF16 ? 1 : 2;            // log2 of the element size
+    const int lg = a.reduce_dt == kBF16 ? 1 : 2;            // log2 of the element size
     int32_t r, k;
     pack_row_window(a, w, r, k);
     const int64_t rb = a.S << lg;                         // bytes per row
@@ -251,7 +256,7 @@ FSDPPACK_HD inline void pack_window(const WindowArgs &a, int32_t w, F &&f)
         g.slot = m;
         g.param = pm.param;
         g.src_dt = pm.src_dt;
-        g.dst_dt = a.dst_dt;
+        g.dst_dt = a.reduce_dt;
         g.table_side = kTableIsSource;
         f(g);
     }
@@ -289,22 +294,28 @@ FSDPPACK_HD inline void copy_in_window(const WindowArgs &a, int32_t w, F &&f)
     }
 }
 
-// Copy-out window w: the tensor whose windows contain w (a binary search on
-// win0 among the few tensors the group map names for w's group), bytes
-// [x*kWindowBytes, ...) of that tensor (windows start at each tensor's own
-// first byte; `shift` is unused), split at rank-chunk boundaries; chunk r
-// comes from byte r*B + A of the gathered buffer.
-template <typename F>
-FSDPPACK_HD inline void copy_out_window(const WindowArgs &a, int32_t w, F &&f)
+// The tensor record whose windows contain window w: a binary search on win0
+// among the few records the group map names for w's group (usually one).
+FSDPPACK_HD inline CopyOutTensor find_tensor(const WindowArgs &a, int32_t w)
 {
     const FSDPPACK_TABLE CopyOutTensor *T = (const FSDPPACK_TABLE CopyOutTensor *)a.members;
     const ColumnWindow grp = ((const FSDPPACK_TABLE ColumnWindow *)a.columns)[w >> kGroupLog2];
-    int32_t lo = grp.first, hi = grp.first + grp.count - 1;   // last tensor with win0 <= w
+    int32_t lo = grp.first, hi = grp.first + grp.count - 1;   // last record with win0 <= w
     while (lo < hi) {
         const int32_t mid = (lo + hi + 1) >> 1;
         if (T[mid].win0 <= w) lo = mid; else hi = mid - 1;
     }
-    const CopyOutTensor t = T[lo];
+    return T[lo];
+}
+
+// Copy-out window w: bytes [x*kWindowBytes, ...) of the tensor owning w
+// (windows start at each tensor's own first byte; `shift` is unused), split
+// at rank-chunk boundaries; chunk r comes from byte r*B + A of the gathered
+// buffer.
+template <typename F>
+FSDPPACK_HD inline void copy_out_window(const WindowArgs &a, int32_t w, F &&f)
+{
+    const CopyOutTensor t = find_tensor(a, w);
     const uint64_t ptr = table_entry(a, t.slot);
     const int64_t esz = dtype_bytes(t.dt);
     const int64_t e0 = (w - t.win0) * (kWindowBytes / esz);
@@ -327,12 +338,41 @@ FSDPPACK_HD inline void copy_out_window(const WindowArgs &a, int32_t w, F &&f)
     }
 }
 
+// Reduce-scatter write-back window w: bytes [x*kWindowBytes, ...) of the
+// rank chunk of the member owning w, in its storage dtype, clipped to the
+// chunk's real elements for rank a.rank (a window past them does nothing);
+// the source is the member's columns of the rank's reduced row.
+template <typename F>
+FSDPPACK_HD inline void write_back_window(const WindowArgs &a, int32_t w, F &&f)
+{
+    const CopyOutTensor t = find_tensor(a, w);
+    const int64_t esz = dtype_bytes(t.dt);
+    const int64_t e0 = (w - t.win0) * (kWindowBytes / esz);
+    const int64_t valid = imax(0, imin(t.P, t.numel - static_cast<int64_t>(a.rank) * t.P));
+    const int64_t e1 = imin(valid, e0 + kWindowBytes / esz);
+    if (e1 <= e0) return;
+    RangeRef g;
+    g.ptr = table_entry(a, t.slot);
+    g.src_off = t.A;
+    g.dst_off = 0;
+    g.lo = e0;
+    g.hi = e1;
+    g.valid = e1;
+    g.slot = t.slot;
+    g.param = t.slot;
+    g.src_dt = a.reduce_dt;
+    g.dst_dt = t.dt;
+    g.table_side = kTableIsDest;
+    f(g);
+}
+
 template <typename F>
 FSDPPACK_HD inline void for_each_range(const WindowArgs &a, int32_t w, F &&f)
 {
     if (a.op == kOpPack) pack_window(a, w, f);
     else if (a.op == kOpCopyIn) copy_in_window(a, w, f);
-    else copy_out_window(a, w, f);
+    else if (a.op == kOpCopyOut) copy_out_window(a, w, f);
+    else write_back_window(a, w, f);
 }
 
 // Launch the window kernel on `stream`: one workgroup per window.

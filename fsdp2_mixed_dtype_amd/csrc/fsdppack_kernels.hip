@@ -69,6 +69,32 @@ __device__ __forceinline__ uint32_t convert1(uint32_t bits)
     else return bits;
 }
 
+// Division by the write-back's divide factor in the source (reduction)
+// dtype: a correctly rounded binary32 division (the compiler's IEEE divide
+// sequence; fp32 denormals are kept), rounded once more to bfloat16 when that
+// is the dtype.  A NaN is not divided: it keeps sign and payload and gets the
+// quiet bit.
+__device__ __forceinline__ uint32_t div_f32(uint32_t u, float d)
+{
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return u | 0x00400000u;
+    return __float_as_uint(__uint_as_float(u) / d);
+}
+
+template <int S>
+__device__ __forceinline__ uint32_t divide_in(uint32_t bits, float d)
+{
+    if constexpr (S == kBF16) return f32_to_bf16(div_f32(bits << 16, d));
+    else return div_f32(bits, d);
+}
+
+// One element of S cast to D, divided first when DIV.
+template <int S, int D, bool DIV>
+__device__ __forceinline__ uint32_t convert1_div(uint32_t bits, float d)
+{
+    if constexpr (DIV) bits = divide_in<S>(bits, d);
+    return convert1<S, D>(bits);
+}
+
 template <int S, int D>
 struct Path {
     using ST = typename ElemT<S>::T;
@@ -94,9 +120,24 @@ __device__ __forceinline__ const FSDPPACK_GLOBAL T *gin(const char *p) { return 
 template <typename T>
 __device__ __forceinline__ FSDPPACK_GLOBAL T *gout(char *p) { return (FSDPPACK_GLOBAL T *)p; }
 
-// One global load, non-temporal when NT (a source read exactly once).
-template <bool NT, typename T>
-__device__ __forceinline__ T gload(const FSDPPACK_GLOBAL T *p)
+// Global loads of 16, 8 and 4 bytes from dword-aligned addresses,
+// non-temporal when NT (a source read exactly once).  One function per width,
+// so that each load assumes the 4-byte alignment its pointer type declares
+// (a template would deduce the naturally aligned vector type).
+template <bool NT>
+__device__ __forceinline__ u32x4 gload4(const FSDPPACK_GLOBAL u32x4_a4 *p)
+{
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+template <bool NT>
+__device__ __forceinline__ u32x2 gload2(const FSDPPACK_GLOBAL u32x2_a4 *p)
+{
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+template <bool NT>
+__device__ __forceinline__ uint32_t gload1(const FSDPPACK_GLOBAL uint32_t *p)
 {
     if constexpr (NT) return __builtin_nontemporal_load(p);
     else return *p;
@@ -110,14 +151,14 @@ __device__ __forceinline__ void load_dwords(const char *p, uint32_t *w)
     int i = 0;
 #pragma unroll
     for (; i + 4 <= N; i += 4) {
-        const u32x4 v = gload<NT>((const FSDPPACK_GLOBAL u32x4_a4 *)(g + i));
+        const u32x4 v = gload4<NT>((const FSDPPACK_GLOBAL u32x4_a4 *)(g + i));
         w[i] = v.x; w[i + 1] = v.y; w[i + 2] = v.z; w[i + 3] = v.w;
     }
     if constexpr (N % 4 >= 2) {
-        const u32x2 v = gload<NT>((const FSDPPACK_GLOBAL u32x2_a4 *)(g + (N / 4) * 4));
+        const u32x2 v = gload2<NT>((const FSDPPACK_GLOBAL u32x2_a4 *)(g + (N / 4) * 4));
         w[(N / 4) * 4] = v.x; w[(N / 4) * 4 + 1] = v.y;
     }
-    if constexpr (N % 2 == 1) w[N - 1] = gload<NT>(g + N - 1);
+    if constexpr (N % 2 == 1) w[N - 1] = gload1<NT>(g + N - 1);
 }
 
 // Source vector of NSRC dwords starting 2 bytes past a dword boundary (a
@@ -154,6 +195,19 @@ __device__ __forceinline__ u32x4 convert_vec(const uint32_t (&w)[Path<S, D>::NSR
     return r;
 }
 
+// Divide every source element of a vector's dwords (two per dword for bf16).
+template <int S, int N>
+__device__ __forceinline__ void divide_words(uint32_t (&w)[N], float d)
+{
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        if constexpr (S == kBF16)
+            w[k] = divide_in<kBF16>(w[k] & 0xFFFFu, d) | (divide_in<kBF16>(w[k] >> 16, d) << 16);
+        else
+            w[k] = divide_in<kFP32>(w[k], d);
+    }
+}
+
 // Cache-policy bits of a gfx950 memory instruction.
 constexpr int kNT = 2, kSC1 = 16;   // (sc0 is bit 0)
 // Whole destination vectors: device scope, non-temporal.  The written
@@ -181,28 +235,28 @@ struct VecOut {
 };
 
 // One element: dst[i] = i < valid ? cast(src[i]) : +0.
-template <int S, int D>
-__device__ __forceinline__ void copy_one(const char *src, char *dst, int64_t i, int64_t valid)
+template <int S, int D, bool DIV>
+__device__ __forceinline__ void copy_one(const char *src, char *dst, int64_t i, int64_t valid, float d)
 {
     using P = Path<S, D>;
     uint32_t v = 0;
-    if (i < valid) v = convert1<S, D>(gin<typename P::ST>(src)[i]);
+    if (i < valid) v = convert1_div<S, D, DIV>(gin<typename P::ST>(src)[i], d);
     gout<typename P::DT>(dst)[i] = static_cast<typename P::DT>(v);
 }
 
 // A destination vector (vector q of `out`, element i0 of the chunk) that
 // straddles the end of the valid prefix (at most one per range): element-wise
 // loads of the valid part only.
-template <int S, int D>
+template <int S, int D, bool DIV>
 __device__ __forceinline__ void copy_straddle(const char *src, const VecOut &out, int64_t q, int64_t i0,
-                                              int64_t valid)
+                                              int64_t valid, float d)
 {
     using P = Path<S, D>;
     typename P::DT e[P::V];
 #pragma unroll
     for (int k = 0; k < P::V; ++k) {
         uint32_t v = 0;
-        if (i0 + k < valid) v = convert1<S, D>(gin<typename P::ST>(src)[i0 + k]);
+        if (i0 + k < valid) v = convert1_div<S, D, DIV>(gin<typename P::ST>(src)[i0 + k], d);
         e[k] = static_cast<typename P::DT>(v);
     }
     u32x4 r;
@@ -213,10 +267,11 @@ __device__ __forceinline__ void copy_straddle(const char *src, const VecOut &out
 // Elements [lo, hi) of one range: dst[i] = i < valid ? cast(src[i]) : +0,
 // where src / dst address element 0 of the range's chunk.  All threads of the
 // workgroup take part; no two threads write the same byte.  NT: the whole
-// source vectors are loaded non-temporally.
-template <int S, int D, bool NT>
+// source vectors are loaded non-temporally.  DIV: every element is divided
+// by d (in S) before the cast.
+template <int S, int D, bool NT, bool DIV>
 __device__ void copy_range(const char *__restrict__ src, char *__restrict__ dst, int64_t lo,
-                           int64_t hi, int64_t valid)
+                           int64_t hi, int64_t valid, float d)
 {
     using P = Path<S, D>;
     constexpr int64_t SB = sizeof(typename P::ST), DB = sizeof(typename P::DT);
@@ -226,7 +281,7 @@ __device__ void copy_range(const char *__restrict__ src, char *__restrict__ dst,
     const uint32_t dmis = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst + lo * DB) & 15u);
     int64_t head = static_cast<int64_t>(((16u - dmis) & 15u) / DB);
     if (head > hi - lo) head = hi - lo;
-    if (tid < head) copy_one<S, D>(src, dst, lo + tid, valid);
+    if (tid < head) copy_one<S, D, DIV>(src, dst, lo + tid, valid, d);
 
     const int64_t v0 = lo + head;                 // first aligned vector
     const int64_t nvec = (hi - v0) / P::V;
@@ -250,7 +305,10 @@ __device__ void copy_range(const char *__restrict__ src, char *__restrict__ dst,
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
                     const int64_t qq = q + u * kBlock;
-                    if (qq < nfull) out.put(qq, convert_vec<S, D>(w[u]));
+                    if (qq < nfull) {
+                        if constexpr (DIV) divide_words<S>(w[u], d);
+                        out.put(qq, convert_vec<S, D>(w[u]));
+                    }
                 }
             }
         } else if constexpr (S == kBF16) {
@@ -265,7 +323,10 @@ __device__ void copy_range(const char *__restrict__ src, char *__restrict__ dst,
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
                     const int64_t qq = q + u * kBlock;
-                    if (qq < nfull) out.put(qq, convert_vec<S, D>(w[u]));
+                    if (qq < nfull) {
+                        if constexpr (DIV) divide_words<S>(w[u], d);
+                        out.put(qq, convert_vec<S, D>(w[u]));
+                    }
                 }
             }
         }
@@ -276,19 +337,20 @@ __device__ void copy_range(const char *__restrict__ src, char *__restrict__ dst,
     for (int64_t q = nfull + tid; q < nvec; q += kBlock) {
         const int64_t i0 = v0 + q * P::V;
         if (i0 >= valid) out.put(q, zero);
-        else copy_straddle<S, D>(src, out, q, i0, valid);
+        else copy_straddle<S, D, DIV>(src, out, q, i0, valid, d);
     }
 
     // tail: elements after the last whole vector
     const int64_t t0 = v0 + nvec * P::V;
-    if (tid < hi - t0) copy_one<S, D>(src, dst, t0 + tid, valid);
+    if (tid < hi - t0) copy_one<S, D, DIV>(src, dst, t0 + tid, valid, d);
 }
 
-// Source loads: plain for the pack, non-temporal for the all-gather copies.
-// On MI355X non-temporal loads sped the copies up by 2-6 %, but moved the
-// pack by -3 % to +5 % depending on the layout.
-template <bool NT>
-__device__ __forceinline__ void run_range(const RangeRef &g, char *base)
+// Source loads: plain for the pack, non-temporal for the all-gather copies
+// and the write-back (sources read once).  On MI355X non-temporal loads sped
+// the copies up by 2-6 %, but moved the pack by -3 % to +5 % depending on the
+// layout.  DIV: divide every element by d before the cast (write-back only).
+template <bool NT, bool DIV>
+__device__ __forceinline__ void run_range(const RangeRef &g, char *base, float d)
 {
     char *tp = reinterpret_cast<char *>(g.ptr);
     const char *src;
@@ -296,24 +358,28 @@ __device__ __forceinline__ void run_range(const RangeRef &g, char *base)
     if (g.table_side == kTableIsSource) { src = tp + g.src_off; dst = base + g.dst_off; }
     else { src = base + g.src_off; dst = tp + g.dst_off; }
     switch (g.src_dt * 4 + g.dst_dt) {
-    case kBF16 * 4 + kFP32: copy_range<kBF16, kFP32, NT>(src, dst, g.lo, g.hi, g.valid); break;
-    case kFP32 * 4 + kFP32: copy_range<kFP32, kFP32, NT>(src, dst, g.lo, g.hi, g.valid); break;
-    case kFP32 * 4 + kBF16: copy_range<kFP32, kBF16, NT>(src, dst, g.lo, g.hi, g.valid); break;
-    case kBF16 * 4 + kBF16: copy_range<kBF16, kBF16, NT>(src, dst, g.lo, g.hi, g.valid); break;
+    case kBF16 * 4 + kFP32: copy_range<kBF16, kFP32, NT, DIV>(src, dst, g.lo, g.hi, g.valid, d); break;
+    case kFP32 * 4 + kFP32: copy_range<kFP32, kFP32, NT, DIV>(src, dst, g.lo, g.hi, g.valid, d); break;
+    case kFP32 * 4 + kBF16: copy_range<kFP32, kBF16, NT, DIV>(src, dst, g.lo, g.hi, g.valid, d); break;
+    case kBF16 * 4 + kBF16: copy_range<kBF16, kBF16, NT, DIV>(src, dst, g.lo, g.hi, g.valid, d); break;
     default: break;   // the planner only emits the four pairs above
     }
 }
 
-// One workgroup per window; the window's ranges come from its index and a
-// binary search over the (cache-resident) member table.
+// One workgroup per window; the window's ranges come from its index and the
+// plan's (cache-resident) record tables.
 template <int OP>
 __global__ void __launch_bounds__(kBlock) window_kernel(WindowArgs a)
 {
     const int32_t w = static_cast<int32_t>(blockIdx.x);
-    auto body = [&](const RangeRef &g) { run_range<OP != kOpPack>(g, a.base); };
+    auto body = [&](const RangeRef &g) { run_range<OP != kOpPack, false>(g, a.base, 1.0f); };
     if constexpr (OP == kOpPack) pack_window(a, w, body);
     else if constexpr (OP == kOpCopyIn) copy_in_window(a, w, body);
-    else copy_out_window(a, w, body);
+    else if constexpr (OP == kOpCopyOut) copy_out_window(a, w, body);
+    else if (a.divisor != 1.0f)    // uniform across the launch
+        write_back_window(a, w, [&](const RangeRef &g) { run_range<true, true>(g, a.base, a.divisor); });
+    else
+        write_back_window(a, w, body);
 }
 
 }  // namespace
@@ -328,7 +394,8 @@ int launch_windows(const WindowArgs &args, void *stream, void *start_event, void
     // dispatch itself, so they bracket exactly this kernel's execution
     if (args.op == kOpPack) hipExtLaunchKernelGGL(window_kernel<kOpPack>, grid, block, 0, st, e0, e1, 0, args);
     else if (args.op == kOpCopyIn) hipExtLaunchKernelGGL(window_kernel<kOpCopyIn>, grid, block, 0, st, e0, e1, 0, args);
-    else hipExtLaunchKernelGGL(window_kernel<kOpCopyOut>, grid, block, 0, st, e0, e1, 0, args);
+    else if (args.op == kOpCopyOut) hipExtLaunchKernelGGL(window_kernel<kOpCopyOut>, grid, block, 0, st, e0, e1, 0, args);
+    else hipExtLaunchKernelGGL(window_kernel<kOpWriteBack>, grid, block, 0, st, e0, e1, 0, args);
     return static_cast<int>(hipGetLastError());
 }
 

@@ -33,6 +33,25 @@ constexpr int64_t kMaxBytes = INT64_MAX / 4;
 
 }  // namespace
 
+// Group map of a table of CopyOutTensor records whose windows are
+// consecutive (record t owns windows [win0_t, win0_{t+1})): for each group of
+// 2^kGroupLog2 windows, the records owning its first and last windows.
+static void build_group_map(OpTable &op)
+{
+    const CopyOutTensor *T = reinterpret_cast<const CopyOutTensor *>(op.members.data());
+    const int64_t win = op.n_windows;
+    const int64_t ng = (win + (int64_t{1} << kGroupLog2) - 1) >> kGroupLog2;
+    op.columns.resize(static_cast<size_t>(ng));
+    int32_t t0 = 0;
+    for (int64_t j = 0; j < ng; ++j) {
+        const int64_t w0 = j << kGroupLog2, w1 = std::min(win, (j + 1) << kGroupLog2) - 1;
+        while (t0 + 1 < op.n && T[t0 + 1].win0 <= w0) ++t0;     // owner of the group's first window
+        int32_t t1 = t0;
+        while (t1 + 1 < op.n && T[t1 + 1].win0 <= w1) ++t1;     // owner of its last window
+        op.columns[j] = ColumnWindow{t0, t1 - t0 + 1};
+    }
+}
+
 int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdppack_plan *plan,
                std::string &err)
 {
@@ -108,7 +127,7 @@ int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdp
         // every row
         OpTable &op = b.pack;
         op.op = kOpPack;
-        op.dst_dt = b.dtype;
+        op.reduce_dt = b.dtype;
         op.S = b.S;
         const int64_t dsz = dtype_bytes(b.dtype);
         std::vector<PackMember> mem;
@@ -142,6 +161,34 @@ int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdp
         if (!mem.empty() && W % 2 == 0 &&
             static_cast<double>(op.src_bytes) <= 524288.0 * static_cast<double>(mem.size()) * W)
             op.group_lg = 1;
+
+        // reduce-scatter write-back: each member's rank chunk (P elements in
+        // its storage dtype) cut into windows from its first byte; a launch
+        // clips them to the chunk's real elements for its rank
+        OpTable &wb = b.write_back;
+        wb.op = kOpWriteBack;
+        wb.reduce_dt = b.dtype;
+        wb.S = b.S;
+        int64_t win = 0;
+        for (size_t k = 0; k < b.members.size(); ++k) {
+            if (b.P[k] == 0) continue;
+            const int32_t t = b.members[k];
+            const int64_t bytes = b.P[k] * dtype_bytes(plan->params[t].storage_dtype);
+            CopyOutTensor m{};
+            m.win0 = win;
+            m.numel = plan->numel[t];
+            m.P = b.P[k];
+            m.A = b.O[k] * dsz;
+            m.slot = t;
+            m.dt = plan->params[t].storage_dtype;
+            wb.add(m);
+            win += (bytes + kWindowBytes - 1) / kWindowBytes;
+            if (win > kMaxWindows) { err = "plan_buckets: sharded gradients need too many write-back workgroups"; return FSDPPACK_EINVAL; }
+            wb.dst_bytes += bytes;
+            wb.src_bytes += b.P[k] * dsz;
+        }
+        wb.n_windows = static_cast<int32_t>(win);
+        build_group_map(wb);
         // column map: the members each kWindowBytes column span of a row
         // overlaps (members tile [0, S) in column order, so one sweep finds
         // them all)
@@ -218,19 +265,7 @@ int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdp
         }
         op.n_windows = static_cast<int32_t>(win);
         op.dst_bytes = op.src_bytes;
-        // group map: the tensors owning the windows of each group of
-        // 2^kGroupLog2 windows (the tensors' windows are consecutive)
-        const CopyOutTensor *T = reinterpret_cast<const CopyOutTensor *>(op.members.data());
-        const int64_t ng = (win + (int64_t{1} << kGroupLog2) - 1) >> kGroupLog2;
-        op.columns.resize(static_cast<size_t>(ng));
-        int32_t t0 = 0;
-        for (int64_t j = 0; j < ng; ++j) {
-            const int64_t w0 = j << kGroupLog2, w1 = std::min(win, (j + 1) << kGroupLog2) - 1;
-            while (t0 + 1 < op.n && T[t0 + 1].win0 <= w0) ++t0;     // owner of the group's first window
-            int32_t t1 = t0;
-            while (t1 + 1 < op.n && T[t1 + 1].win0 <= w1) ++t1;     // owner of its last window
-            op.columns[j] = ColumnWindow{t0, t1 - t0 + 1};
-        }
+        build_group_map(op);
     }
     return FSDPPACK_OK;
 }

@@ -28,7 +28,7 @@ struct OpTable {
     int32_t n_windows = 0;                // workgroups per launch (pack / copy-in: destination window-aligned)
     int32_t gx = 0;                       // pack: column-map entries
     int32_t group_lg = 0;                 // pack: log2 of the rows interleaved per row group
-    int32_t dst_dt = 0;                   // pack: reduction dtype
+    int32_t reduce_dt = 0;                // pack, write-back: the bucket's reduction dtype
     int64_t S = 0;                        // pack: row length (elements)
     int64_t B = 0;                        // all-gather row bytes
     int64_t dst_bytes = 0;                // bytes the operation writes
@@ -45,13 +45,13 @@ struct OpTable {
     // Workgroups of a launch whose destination starts `shift` bytes past a
     // cache-line boundary: the pack gives every row gx + 1 windows (enough
     // for any alignment of the row), the copy-in cuts its row at line
-    // boundaries of memory, and the copy-out's windows start at each
-    // parameter's first byte.
+    // boundaries of memory, and the copy-out's and write-back's windows
+    // start at each parameter's first byte.
     int64_t windows(int32_t shift) const
     {
-        if (op == kOpCopyOut) return n_windows;
+        if (op == kOpCopyOut || op == kOpWriteBack) return n_windows;
         if (dst_bytes == 0) return 0;
-        if (op == kOpPack) return (static_cast<int64_t>(gx) + 1) * (dst_bytes / (S * dtype_bytes(dst_dt)));
+        if (op == kOpPack) return (static_cast<int64_t>(gx) + 1) * (dst_bytes / (S * dtype_bytes(reduce_dt)));
         return (shift + dst_bytes + kWindowBytes - 1) >> kWindowLog2;
     }
     // launch arguments against host (`device == false`) or device members
@@ -60,11 +60,11 @@ struct OpTable {
         WindowArgs a{};
         a.op = op;
         a.n = n;
-        a.shift = op == kOpCopyOut ? 0 : shift;
+        a.shift = (op == kOpCopyOut || op == kOpWriteBack) ? 0 : shift;
         a.n_windows = static_cast<int32_t>(windows(a.shift));
         a.gx = gx;
         a.group_lg = group_lg;
-        a.dst_dt = dst_dt;
+        a.reduce_dt = reduce_dt;
         a.S = S;
         a.B = B;
         a.members = device ? d_members : static_cast<const void *>(members.data());
@@ -79,6 +79,7 @@ struct BucketPlan {
     std::vector<int32_t> members;
     std::vector<int64_t> P, O;
     OpTable pack;
+    OpTable write_back;   // reduce-scatter output -> the members' sharded gradients
 };
 
 // Per-call pointer tables, cached on the device by content: the same grads /
@@ -123,7 +124,7 @@ struct fsdppack_plan {
     std::mutex mu;
     int device = -1;
     bool uploaded = false;
-    std::vector<fsdppack::PtrCache> caches;   // one per bucket, then copy-in, copy-out
+    std::vector<fsdppack::PtrCache> caches;   // pack per bucket, copy-in, copy-out, write-back per bucket
 };
 
 namespace fsdppack {

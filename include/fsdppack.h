@@ -1,6 +1,7 @@
 /*
  * fsdppack.h -- C ABI of libfsdppack: FSDP2's mixed-dtype gradient pack for
- * reduce-scatter and its all-gather copy-in / copy-out, on AMD MI355X (gfx950).
+ * reduce-scatter, the write-back of a reduce-scatter output into sharded
+ * gradients, and the all-gather copy-in / copy-out, on AMD MI355X (gfx950).
  *
  * What the calls compute (web pages on FSDP2 per-parameter mixed precision):
  *  - "PyTorch adds per-parameter mixed precision to FSDP2" (ainewsletter.today),
@@ -160,6 +161,30 @@ int fsdppack_all_gather_copy_in(const fsdppack_plan *plan, int32_t rank, const v
  * (param dtype), fully overwritten.  Errors: EINVAL, ESTATE, EHIP, ENOMEM. */
 int fsdppack_all_gather_copy_out(const fsdppack_plan *plan, const void *ag, void *const *params,
                                  void *stream);
+
+/* Reduce-scatter output write-back for rank `rank` (0 <= rank < W): the step
+ * after the bucket's reduce-scatter, where each rank keeps the gradient slice
+ * of the parameters it owns ("The unit you wrapped", the paragraphs on the
+ * collectives FSDP issues), in the resident parameter's dtype ("Mixed-
+ * Precision Training": reduce_dtype only sets how gradients are summed; the
+ * gradient buffer follows the resident parameter dtype):
+ *   shard_grads[t][j] = cast(div(rs_out[O_t + j]))   for j < min(P_t, numel_t - rank*P_t)
+ * for every member t of the bucket.  rs_out: device pointer to the rank's
+ * reduced row, S elements of the bucket's reduction dtype (row `rank` of a
+ * reduce-scatter of the packed [W, S] input), read only.  div: when
+ * divide_factor is not 1, the element divided by divide_factor in the
+ * reduction dtype (a correctly rounded binary32 division, then rounded once
+ * to bfloat16 when that is the reduction dtype; a NaN is not divided and gets
+ * the quiet bit); cast: the reduction dtype to the member's storage dtype.
+ * shard_grads: n host entries (by parameter index) of device pointers to the
+ * rank chunk's real elements (storage dtype), overwritten; entries of
+ * non-members, and of members with no real element on this rank, are not read
+ * and may be NULL.  divide_factor must be finite and > 0.  One kernel launch
+ * on `stream`.  Errors: EINVAL (bucket or rank out of range, bad
+ * divide_factor, NULL or misaligned pointer), ESTATE, EHIP, ENOMEM. */
+int fsdppack_reduce_scatter_copy_out(const fsdppack_plan *plan, int32_t bucket, int32_t rank,
+                                     const void *rs_out, float divide_factor, void *const *shard_grads,
+                                     void *stream);
 
 /* Free a plan and its device tables.  Synchronises the device first if the
  * plan was ever used there (no kernel may still read its tables).  NULL is a

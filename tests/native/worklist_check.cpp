@@ -16,7 +16,10 @@
 //    boundary; only the pack's spare window at the end of a row may have no
 //    range;
 //  * the record maps have one entry per kWindowBytes of a row (pack,
-//    copy-in) or per group of windows (copy-out).
+//    copy-in) or per group of windows (copy-out, write-back);
+//  * the reduce-scatter write-back of every rank (a sample of ranks for large
+//    W) writes each member's real rank-chunk elements exactly once and reads
+//    only the rank's reduced row.
 //
 // Input (stdin): "world n" then n lines
 // "dim0 inner grad reduce storage param".  Prints "OK" or the first failure.
@@ -72,10 +75,12 @@ static bool check_range(const char *name, int32_t w, int32_t shift, const RangeR
 
 template <typename DstSize, typename SrcSize>
 static bool check_op(const char *name, const OpTable &op, int32_t W, int32_t shift, int32_t nparams,
-                     DstSize dst_size, SrcSize src_size, std::vector<Intervals> &written)
+                     DstSize dst_size, SrcSize src_size, std::vector<Intervals> &written, int32_t rank = 0)
 {
     WindowArgs a = op.args(false, shift);
     a.W = W;
+    a.rank = rank;
+    a.divisor = 1.0f;
     CHECK(a.n_windows == op.windows(shift) && (shift != 0 || a.n_windows == op.n_windows), "%s: window count", name);
     const size_t rec = op.op == kOpPack ? sizeof(PackMember)
                        : op.op == kOpCopyIn ? sizeof(CopyInMember) : sizeof(CopyOutTensor);
@@ -85,7 +90,7 @@ static bool check_op(const char *name, const OpTable &op, int32_t W, int32_t shi
                                op.table_params.size() == static_cast<size_t>(op.n)), "%s: column map size", name);
     CHECK(op.op != kOpCopyIn || op.columns.size() == static_cast<size_t>((op.B + kWindowBytes - 1) / kWindowBytes),
           "%s: member map size", name);
-    CHECK(op.op != kOpCopyOut ||
+    CHECK((op.op != kOpCopyOut && op.op != kOpWriteBack) ||
               op.columns.size() == static_cast<size_t>((op.n_windows + (1 << kGroupLog2) - 1) >> kGroupLog2),
           "%s: group map size", name);
     for (int32_t w = 0; w < a.n_windows; ++w) {
@@ -105,16 +110,16 @@ static bool check_op(const char *name, const OpTable &op, int32_t W, int32_t shi
             // window k of row r is empty exactly when the row ends before it
             int32_t r, k;
             pack_row_window(a, w, r, k);
-            const int64_t rb = op.S * dtype_bytes(op.dst_dt);
+            const int64_t rb = op.S * dtype_bytes(op.reduce_dt);
             const int64_t s_r = (shift + r * rb) % kLineBytes;
             const bool spare = static_cast<int64_t>(k) * kWindowBytes - s_r >= rb;
             CHECK((ranges == 0) == spare, "%s: window %d (row %d, shift %d) has %d ranges", name, w, r, shift, ranges);
             row0 = shift + r * rb;
             row1 = row0 + rb;
-        } else {
+        } else if (op.op != kOpWriteBack) {   // write-back windows past a rank's real elements are empty
             CHECK(ranges > 0, "%s: window %d has no range", name, w);
         }
-        if (op.op != kOpCopyOut && ranges > 0)
+        if ((op.op == kOpPack || op.op == kOpCopyIn) && ranges > 0)
             CHECK((lo == row0 || lo % kLineBytes == 0) && (hi == row1 || hi % kLineBytes == 0) &&
                       hi - lo <= kWindowBytes,
                   "%s: window %d (shift %d) writes [%lld,%lld) from the aligned origin, off the line boundaries",
@@ -209,6 +214,37 @@ int main()
             if (!tiles(written[t], plan.numel[t] * dtype_bytes(plan.params[t].param_dtype), name)) {
                 std::printf("FAIL %s\n", g_fail.c_str());
                 return 1;
+            }
+        }
+    }
+    for (size_t bi = 0; bi < plan.buckets.size(); ++bi) {
+        const BucketPlan &b = plan.buckets[bi];
+        const int64_t row_bytes = b.S * dtype_bytes(b.dtype);
+        std::vector<int32_t> ranks;
+        for (int32_t r = 0; r < plan.W; ++r)
+            if (plan.W <= 16 || r < 2 || r == plan.W / 2 || r >= plan.W - 2) ranks.push_back(r);
+        for (int32_t r : ranks) {
+            std::vector<Intervals> written(n);
+            char name[64];
+            std::snprintf(name, sizeof name, "write-back[%zu] rank %d", bi, r);
+            auto valid_bytes = [&](int32_t t, int64_t P) {
+                return std::max<int64_t>(0, std::min<int64_t>(P, plan.numel[t] - int64_t{r} * P)) *
+                       dtype_bytes(plan.params[t].storage_dtype);
+            };
+            std::vector<int64_t> dst_limit(n, 0);
+            for (size_t k = 0; k < b.members.size(); ++k) dst_limit[b.members[k]] = valid_bytes(b.members[k], b.P[k]);
+            if (!check_op(name, b.write_back, plan.W, 0, n, [&](const RangeRef &g) { return dst_limit[g.param]; },
+                          [&](const RangeRef &) { return row_bytes; }, written, r)) {
+                std::printf("FAIL %s\n", g_fail.c_str());
+                return 1;
+            }
+            for (int32_t t = 0; t < n; ++t) {
+                char tn[96];
+                std::snprintf(tn, sizeof tn, "%s param %d", name, t);
+                if (!tiles(written[t], dst_limit[t], tn)) {
+                    std::printf("FAIL %s\n", g_fail.c_str());
+                    return 1;
+                }
             }
         }
     }

@@ -345,3 +345,96 @@ def test_copy_in_all_gather_copy_out_round_trip(name):
         want = oracle.convert(x, t.storage_dtype, t.param_dtype)
         assert np.array_equal(host_bytes(o), want.view(np.uint8)), f"param {i} differs after the round trip"
     plan.destroy()
+
+
+# --------------------------------------------------------------------------- reduce-scatter write-back
+
+def check_rs_copy_out(w, ref, plan, bucket, rank, row, factor, row_offset=0, dst_offsets=None):
+    """HIP write-back of rank `rank`'s reduced row of `bucket` vs the oracle,
+    byte for byte, into guarded destinations (nothing written outside them)."""
+    b = ref.buckets[bucket]
+    rs = to_dev(row, b.dtype, row_offset)
+    outs = [None] * len(w.tensors)
+    for k, i in enumerate(b.members):
+        v = oracle.valid_in_chunk(w.tensors[i].numel, b.P[k], rank)
+        if v:
+            off = dst_offsets[i] if dst_offsets else i % 3
+            outs[i] = Guarded(v, w.tensors[i].storage_dtype, off)
+    fp.reduce_scatter_copy_out(plan, bucket, rank, rs, [o.t if o is not None else None for o in outs], factor)
+    torch.cuda.synchronize()
+    wants = oracle.rs_copy_out(ref, bucket, rank, row, factor)
+    for k, i in enumerate(b.members):
+        if outs[i] is None:
+            assert wants[k].size == 0
+            continue
+        got = outs[i].result()
+        want = wants[k].view(np.uint8)
+        if not np.array_equal(got, want):
+            bad = np.flatnonzero(got != want)
+            pytest.fail(f"{w.name} bucket {bucket} rank {rank} factor {factor}: param {i}: {bad.size} bytes differ, "
+                        f"first at byte {bad[0]}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "mixed50m", "layout500", "kda_block", "hetero500"])
+def test_rs_copy_out_matches_oracle(name):
+    print(f"[write-back parity] workload={name}", flush=True)
+    w = wl.get(name)
+    ref = oracle.plan(w.descs(), w.world)
+    plan = fp.plan_buckets(w.descs(), w.world)
+    W = w.world
+    ranks = range(W) if W <= 4 else [0, 1, W // 2, W - 1]
+    factors = [1.0, float(W), 3.0]
+    for bi, b in enumerate(ref.buckets):
+        row = wl.random_array(b.S, b.dtype, seed=17 + bi)
+        wl.inject_specials([row], [b.dtype], seed=bi)
+        for rank in ranks:
+            for factor in factors:
+                print(f"[write-back parity] {name} bucket={bi} rank={rank} factor={factor}", flush=True)
+                check_rs_copy_out(w, ref, plan, bi, rank, row, factor)
+    plan.destroy()
+
+
+def test_rs_copy_out_random_layouts_misaligned():
+    rng = random.Random(4242)
+    for case in range(50):
+        w = _random_workload(rng, case)
+        ref = oracle.plan(w.descs(), w.world)
+        plan = fp.plan_buckets(w.descs(), w.world)
+        for bi, b in enumerate(ref.buckets):
+            row = wl.random_array(b.S, b.dtype, seed=case * 7 + bi)
+            wl.inject_specials([row], [b.dtype], seed=case)
+            rank = rng.randrange(w.world)
+            factor = rng.choice([1.0, 2.0, 3.0, 0.5, 6.0, 7.5, float(np.float32(1e-3)), 1e30])
+            row_off = rng.choice([0, 0, 1, 2, 3])
+            offs = {i: rng.choice([0, 0, 1, 2, 3, 5, 7]) for i in range(len(w.tensors))}
+            print(f"[write-back random] case={case} W={w.world} bucket={bi} rank={rank} factor={factor} "
+                  f"row_off={row_off} dst_off={offs}", flush=True)
+            check_rs_copy_out(w, ref, plan, bi, rank, row, factor, row_off, offs)
+        plan.destroy()
+
+
+def test_rs_copy_out_pack_round_trip_with_divide():
+    """pack -> W identical ranks summed (W * row, exact for power-of-two W) ->
+    write-back with divide W == the rank chunk of cast(cast(g)), on the GPU."""
+    print("[write-back round trip] mixed50m", flush=True)
+    w = wl.get("mixed50m")
+    ref = oracle.plan(w.descs(), w.world)
+    plan = fp.plan_buckets(w.descs(), w.world)
+    W = w.world
+    grads = wl.make_grads(w)
+    g_dev = [to_dev(g, t.grad_dtype) for g, t in zip(grads, w.tensors)]
+    b = plan.buckets[0]
+    out = torch.empty(W * b.S, dtype=fp.TORCH_DTYPE[b.dtype], device=DEV)
+    fp.pack_reduce_scatter_input(plan, 0, g_dev, out)
+    summed = (out.view(W, b.S).float() * W).to(fp.TORCH_DTYPE[b.dtype])   # exact: power-of-two scale
+    for rank in (0, W - 1):
+        dst = [torch.empty(fp.valid_in_chunk(plan, i, rank), dtype=fp.TORCH_DTYPE[t.storage_dtype], device=DEV)
+               for i, t in enumerate(w.tensors)]
+        fp.reduce_scatter_copy_out(plan, 0, rank, summed[rank].contiguous(), dst, float(W))
+        torch.cuda.synchronize()
+        for i, t in enumerate(w.tensors):
+            P = ref.P[i]
+            v = oracle.valid_in_chunk(t.numel, P, rank)
+            want = oracle.convert(oracle.convert(grads[i], t.grad_dtype, b.dtype), b.dtype, t.storage_dtype)
+            assert np.array_equal(host_bytes(dst[i]), want[rank * P: rank * P + v].view(np.uint8)), i
+    plan.destroy()

@@ -131,5 +131,19 @@ def test_compute_call_argument_errors_before_any_gpu_work():
     assert L.fsdppack_plan_bucket(p.handle, 3, None, None, None, None, None, None) == -1
     assert L.fsdppack_plan_bucket(None, 0, None, None, None, None, None, None) == -5
     assert L.fsdppack_pack_reduce_scatter_input(None, 0, ptrs, 0x4000, None) == -5
+    # reduce-scatter write-back (one fp32 bucket; parameter 1 holds 2 then 1 real elements)
+    wb = L.fsdppack_reduce_scatter_copy_out
+    assert wb(p.handle, 1, 0, 0x4000, 1.0, ptrs, None) == -1                                 # bucket out of range
+    assert wb(p.handle, 0, 2, 0x4000, 1.0, ptrs, None) == -1                                 # rank out of range
+    assert "rank out of range" in L.fsdppack_last_error().decode()
+    for factor in (0.0, -2.0, float("inf"), float("nan")):
+        assert wb(p.handle, 0, 0, 0x4000, factor, ptrs, None) == -1
+        assert "divide_factor" in L.fsdppack_last_error().decode()
+    assert wb(p.handle, 0, 0, 0x4000, 2.0, None, None) == -1                                 # NULL array
+    assert wb(p.handle, 0, 0, 0x4002, 2.0, ptrs, None) == -1                                 # misaligned row
+    assert wb(p.handle, 0, 0, 0x4000, 2.0, bad, None) == -1                                  # misaligned grad
+    assert "shard_grads[0]" in L.fsdppack_last_error().decode()
+    assert wb(p.handle, 0, 1, 0x4000, 2.0, nul, None) == -1                                  # NULL member with data
+    assert wb(None, 0, 0, 0x4000, 1.0, ptrs, None) == -5
     p.destroy()
     assert fp.counters()[0] == 0           # nothing was launched
