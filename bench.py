@@ -272,6 +272,64 @@ def main():
                                 "rank": 0, "divide_factor": W, "buckets": nb}
         del wsets
 
+        # ---- pack under concurrent load: packs on a side stream (default
+        # priority) while a stream of bf16 GEMMs keeps the GPU busy, as FSDP
+        # overlaps its gradient staging with the backward's compute
+        n_mm = 4096
+        ma = torch.randn(n_mm, n_mm, device=dev).to(torch.bfloat16)
+        mb = torch.randn(n_mm, n_mm, device=dev).to(torch.bfloat16)
+        mc = torch.empty(n_mm, n_mm, dtype=torch.bfloat16, device=dev)
+        side = torch.cuda.Stream(device=dev)
+
+        def gemms(k):
+            for _ in range(k):
+                torch.mm(ma, mb, out=mc)
+
+        gemms(5)
+        g0, g1 = new_event(), new_event()
+        torch.cuda.synchronize()
+        G = 100
+        g0.record(stream)
+        gemms(G)
+        g1.record(stream)
+        torch.cuda.synchronize()
+        gemm_ms = g0.elapsed_time(g1) / G
+        n_packs = max(K, math.ceil(G * gemm_ms / pack_total_ms))
+        e_p = [[(new_event(), new_event()) for _ in range(nb)] for _ in range(n_packs)]
+        c0, c1, m0, m1 = new_event(), new_event(), new_event(), new_event()
+        torch.cuda.synchronize()
+        c0.record(stream)
+        side.wait_event(c0)
+        for i in range(n_packs):
+            g, outs, _, _, _, _ = sets[i % R]
+            for bi in range(nb):
+                timed(e_p[i][bi])
+                fp.pack_reduce_scatter_input(plan, bi, g, outs[bi], side)
+        m0.record(stream)
+        gemms(G)
+        m1.record(stream)
+        side_done = torch.cuda.Event()
+        side_done.record(side)
+        stream.wait_event(side_done)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        both_ms = c0.elapsed_time(c1)
+        pack_load_ms = sum(a.elapsed_time(b) for e in e_p for a, b in e) / n_packs
+        extra["pack_under_load"] = {
+            "gemm": f"bf16 mm {n_mm}x{n_mm}x{n_mm}, {G} back to back on the current stream",
+            "gemm_ms_alone": round(gemm_ms, 5),
+            "gemm_TFLOPs_alone": round(2 * n_mm ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
+            "gemm_ms_beside_packs": round(m0.elapsed_time(m1) / G, 5),
+            "packs": n_packs,
+            "pack_ms_alone": round(pack_total_ms, 5),
+            "pack_ms_under_load": round(pack_load_ms, 5),
+            "pack_slowdown": round(pack_load_ms / pack_total_ms, 3),
+            "sequential_ms": round(G * gemm_ms + n_packs * pack_total_ms, 3),
+            "concurrent_ms": round(both_ms, 3),
+            "overlap_saving": round(1 - both_ms / (G * gemm_ms + n_packs * pack_total_ms), 4),
+        }
+        del ma, mb, mc
+
     if args.calib_copy:
         # plain device-to-device copies of a known size: what a byte counter
         # reads for them calibrates the counter against real traffic
@@ -307,10 +365,11 @@ def main():
         ref = oracle.plan(w.descs(), W)
         reps, t_cpu = 0, 0.0
         t_start = time.perf_counter()
+        packed_h = [None] * nb
         while reps == 0 or (time.perf_counter() - t_start) < args.cpu_seconds:
             ta = time.perf_counter()
             for bi in range(nb):
-                oracle.pack(ref, bi, grads_h)
+                packed_h[bi] = oracle.pack(ref, bi, grads_h)
             t_cpu += time.perf_counter() - ta
             reps += 1
         cpu_gbps = reps * sum(pack_bytes) / t_cpu / 1e9
@@ -318,6 +377,16 @@ def main():
                "sample": f"oracle pack of every bucket of {args.workload}, full size, repeated {reps}x "
                          f"({t_cpu:.1f} s, single thread); GB/s under the same byte model",
                "ms_per_pack": round(t_cpu / reps * 1e3, 2)}
+        if "rs_copy_out" in extra:
+            # the oracle's write-back of rank 0 beside the kernel's, same byte model
+            reps_w, t_w = 0, 0.0
+            while reps_w == 0 or t_w < min(args.cpu_seconds, 3.0):
+                ta = time.perf_counter()
+                for bi in range(nb):
+                    oracle.rs_copy_out(ref, bi, 0, packed_h[bi][0], float(W))
+                t_w += time.perf_counter() - ta
+                reps_w += 1
+            extra["rs_copy_out"]["cpu_oracle_GBps"] = round(reps_w * extra["rs_copy_out"]["bytes"] / t_w / 1e9, 3)
 
     out = {
         "metric": METRIC,

@@ -273,6 +273,46 @@ def test_pack_on_side_stream():
     plan.destroy()
 
 
+def test_pack_concurrent_with_gemm_and_write_back():
+    """Packs on one stream while a bf16 GEMM runs on the current stream and
+    write-backs run on a third (FSDP overlaps its staging with compute):
+    every result still matches the oracle."""
+    print("[concurrent] mixed50m pack + write-back beside a GEMM", flush=True)
+    w = wl.get("mixed50m")
+    W = w.world
+    grads = wl.make_grads(w)
+    ref = oracle.plan(w.descs(), W)
+    plan = fp.plan_buckets(w.descs(), W)
+    g_dev = fp.prepare_grads(plan, [to_dev(g, t.grad_dtype) for g, t in zip(grads, w.tensors)])
+    b = plan.buckets[0]
+    want = oracle.pack(ref, 0, grads)
+    a = torch.randn(4096, 4096, device=DEV).to(torch.bfloat16)
+    m = torch.randn(4096, 4096, device=DEV).to(torch.bfloat16)
+    main = torch.cuda.current_stream()
+    s_pack, s_wb = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = [torch.empty(W * b.S, dtype=torch.float32, device=DEV) for _ in range(3)]
+    dsts = [[torch.empty(fp.valid_in_chunk(plan, i, r), dtype=fp.TORCH_DTYPE[t.storage_dtype], device=DEV)
+             for i, t in enumerate(w.tensors)] for r in range(3)]
+    s_pack.wait_stream(main)
+    s_wb.wait_stream(main)
+    for k in range(3):
+        c = a
+        for _ in range(4):
+            c = torch.mm(c, m)                     # keeps the current stream busy
+        fp.pack_reduce_scatter_input(plan, 0, g_dev, outs[k], stream=s_pack)
+        done = torch.cuda.Event()
+        done.record(s_pack)
+        s_wb.wait_event(done)
+        fp.reduce_scatter_copy_out(plan, 0, k, outs[k][k * b.S:(k + 1) * b.S], dsts[k], float(W), stream=s_wb)
+    torch.cuda.synchronize()
+    for k in range(3):
+        assert np.array_equal(host_bytes(outs[k]), want.view(np.uint8).reshape(-1)), k
+        wb = oracle.rs_copy_out(ref, 0, k, want[k], float(W))
+        for i, wv in zip(b.members, wb):
+            assert np.array_equal(host_bytes(dsts[k][i]), wv.view(np.uint8)), (k, i)
+    plan.destroy()
+
+
 # --------------------------------------------------------------------------- all-gather staging
 
 def _shards_random(w, ref, rank):
