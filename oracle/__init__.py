@@ -73,8 +73,13 @@ def _load():
         lib.oracle_copy_out.argtypes = [i32, i32, vp, i64, vp, vp, vp, vp, vp]
         lib.oracle_convert.argtypes = [vp, i32, vp, i32, i64]
         lib.oracle_rs_copy_out.argtypes = [i32, i32, vp, i32, i64, ctypes.c_float, vp, vp, vp, vp, vp]
+        lib.oracle_pack_flat.argtypes = [i32, i32, vp, vp, vp, i64, i32, vp]
+        lib.oracle_rs_copy_out_flat.argtypes = [i32, i32, vp, i32, i64, ctypes.c_float, vp, vp, vp]
+        lib.oracle_copy_in_flat.argtypes = [i32, i32, vp, vp, i32, vp, i64, vp]
+        lib.oracle_copy_out_flat.argtypes = [i32, vp, i32, vp, vp]
         for f in (lib.oracle_pack, lib.oracle_unpack, lib.oracle_copy_in, lib.oracle_copy_out,
-                  lib.oracle_rs_copy_out):
+                  lib.oracle_rs_copy_out, lib.oracle_pack_flat, lib.oracle_rs_copy_out_flat,
+                  lib.oracle_copy_in_flat, lib.oracle_copy_out_flat):
             f.restype = ctypes.c_int
         lib.oracle_convert.restype = None
         _lib = lib
@@ -277,6 +282,101 @@ def rs_copy_out(pl: Plan, bucket: int, rank: int, row: np.ndarray, divide_factor
                                     numel.ctypes.data, P.ctypes.data, O.ctypes.data, sdt.ctypes.data, _ptrs(outs))
     if rc:
         raise RuntimeError("oracle_rs_copy_out: bad layout")
+    return outs
+
+
+# --------------------------------------------------------------------------- FSDP1 flat layout
+
+@dataclass
+class FlatPlan:
+    """A unit laid out as one FSDP1 flat parameter: the parameters flattened and
+    concatenated in unit order (N elements, parameter t at flat offset F[t]),
+    padded to W*c with c = ceil(N / W); rank r holds flat positions
+    [r*c, (r+1)*c).  One reduction dtype and one param dtype for the unit."""
+    W: int
+    params: list
+    dtype: int          # the unit's (effective) reduction dtype
+    param_dtype: int
+    N: int
+    c: int
+    F: list
+
+
+def plan_flat(params, W: int) -> FlatPlan:
+    if W < 1:
+        raise ValueError("world size must be >= 1")
+    params = [p if isinstance(p, ParamDesc) else ParamDesc(*p) for p in params]
+    eff = {p.reduce_dtype if p.reduce_dtype else p.grad_dtype for p in params}
+    pdt = {p.param_dtype for p in params}
+    if len(eff) > 1 or len(pdt) > 1:
+        raise ValueError("a flat parameter has one reduction dtype and one param dtype")
+    F, acc = [], 0
+    for p in params:
+        F.append(acc)
+        acc += p.numel
+    return FlatPlan(W=W, params=params, dtype=eff.pop() if eff else FP32, param_dtype=pdt.pop() if pdt else FP32,
+                    N=acc, c=_ceil_div(acc, W), F=F)
+
+
+def flat_piece(fp: FlatPlan, index: int, rank: int):
+    """Parameter `index`'s piece on `rank` as flat positions (lo, hi), lo >= hi when empty."""
+    a, b = fp.F[index], fp.F[index] + fp.params[index].numel
+    return max(a, rank * fp.c), min(b, (rank + 1) * fp.c)
+
+
+def piece_len(fp: FlatPlan, index: int, rank: int) -> int:
+    lo, hi = flat_piece(fp, index, rank)
+    return max(0, hi - lo)
+
+
+def pack_flat(fp: FlatPlan, grads) -> np.ndarray:
+    """Reduce-scatter input [W, c]: the concatenated gradients cast to the reduction dtype, +0 padded."""
+    gs = [np.ascontiguousarray(g).reshape(-1) for g in grads]
+    for p, g in zip(fp.params, gs):
+        _check(g, p.grad_dtype, p.numel)
+    out = np.empty((fp.W, fp.c), dtype=NP_DTYPE[fp.dtype])
+    gdt = _i32([p.grad_dtype for p in fp.params])
+    numel = _i64([p.numel for p in fp.params])
+    if _load().oracle_pack_flat(fp.W, len(gs), _ptrs(gs), gdt.ctypes.data, numel.ctypes.data, fp.c, fp.dtype,
+                                out.ctypes.data):
+        raise RuntimeError("oracle_pack_flat: bad layout")
+    return out
+
+
+def rs_copy_out_flat(fp: FlatPlan, rank: int, row: np.ndarray, divide_factor: float = 1.0):
+    """Each parameter's piece of rank `rank`'s sharded gradient (storage dtype) from the
+    rank's reduced row (c elements of the reduction dtype), divided as in rs_copy_out."""
+    row = np.ascontiguousarray(row).reshape(-1)
+    _check(row, fp.dtype, fp.c)
+    outs = [np.zeros(piece_len(fp, i, rank), dtype=NP_DTYPE[p.storage_dtype]) for i, p in enumerate(fp.params)]
+    numel = _i64([p.numel for p in fp.params])
+    sdt = _i32([p.storage_dtype for p in fp.params])
+    _load().oracle_rs_copy_out_flat(rank, len(outs), row.ctypes.data, fp.dtype, fp.c,
+                                    float(np.float32(divide_factor)), numel.ctypes.data, sdt.ctypes.data, _ptrs(outs))
+    return outs
+
+
+def copy_in_flat(fp: FlatPlan, rank: int, pieces) -> np.ndarray:
+    """Rank `rank`'s row of the gathered flat parameter (c elements of the param dtype)
+    from its per-parameter pieces (storage dtype)."""
+    pieces = [np.ascontiguousarray(x).reshape(-1) for x in pieces]
+    for i, (p, x) in enumerate(zip(fp.params, pieces)):
+        _check(x, p.storage_dtype, piece_len(fp, i, rank))
+    row = np.empty(fp.c, dtype=NP_DTYPE[fp.param_dtype])
+    sdt = _i32([p.storage_dtype for p in fp.params])
+    numel = _i64([p.numel for p in fp.params])
+    _load().oracle_copy_in_flat(rank, len(pieces), _ptrs(pieces), sdt.ctypes.data, fp.param_dtype,
+                                numel.ctypes.data, fp.c, row.ctypes.data)
+    return row
+
+
+def copy_out_flat(fp: FlatPlan, flat: np.ndarray):
+    """The parameters (param dtype) from the gathered flat parameter (W*c elements)."""
+    flat = np.ascontiguousarray(flat).reshape(-1)
+    _check(flat, fp.param_dtype, fp.W * fp.c)
+    outs = [np.zeros(p.numel, dtype=NP_DTYPE[fp.param_dtype]) for p in fp.params]
+    numel = _i64([p.numel for p in fp.params])
+    _load().oracle_copy_out_flat(len(outs), flat.ctypes.data, fp.param_dtype, numel.ctypes.data, _ptrs(outs))
     return outs
 
 

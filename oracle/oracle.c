@@ -48,6 +48,12 @@
  *    the divide of W summed identical rows by a power-of-two W gives the row
  *    back exactly.  The NaN rule of the divide (not divided, quiet bit set) is
  *    a reading: parity unpinned for NaN payloads there.
+ *  - oracle_pack_flat, oracle_rs_copy_out_flat, oracle_copy_in_flat,
+ *    oracle_copy_out_flat (the FSDP1 flat-parameter layout): the printed
+ *    36/18/9 shard sizes and the Linear(3,3) padding count; torch's
+ *    concatenate-pad-split of the cast gradients; the per-parameter pieces
+ *    put back together give the rank's flat shard; copy-out of the gathered
+ *    copy-ins gives the cast parameters back.
  */
 #include <stddef.h>
 #include <stdint.h>
@@ -267,6 +273,95 @@ int oracle_rs_copy_out(int32_t rank, int32_t n, const void *row, int32_t reduce_
             if (divide_factor != 1.0f) x = divide_in(x, reduce_dtype, divide_factor);
             store_as(grads[t], storage_dtype[t], j, cast_bits(x, reduce_dtype, storage_dtype[t]));
         }
+    }
+    return 0;
+}
+
+/*
+ * FSDP1 flat-parameter layout ("The unit you wrapped", the auto_wrap_policy
+ * paragraphs and the padding paragraph): a unit's parameters, flattened and
+ * concatenated in unit order, form one 1-D flat parameter of N elements;
+ * it is padded on the right to W*c elements, c = ceil(N / W), and rank r
+ * holds flat positions [r*c, (r+1)*c).  Parameter t sits at flat offset F[t]
+ * (the exclusive prefix sum of numel); its piece on rank r is the part of
+ * [F[t], F[t] + numel[t]) inside the rank's positions.
+ */
+
+/* Parameter t's piece on rank r, as flat positions [*lo, *hi) (empty when
+ * *lo >= *hi). */
+static void flat_piece(int64_t F, int64_t numel, int64_t c, int64_t r, int64_t *lo, int64_t *hi)
+{
+    int64_t a = F, b = F + numel, s0 = r * c, s1 = (r + 1) * c;
+    *lo = a > s0 ? a : s0;
+    *hi = b < s1 ? b : s1;
+}
+
+/* Reduce-scatter input: out (W*c elements of dst_dtype) = the concatenated
+ * gradients cast to the reduction dtype, then +0 up to W*c. */
+int oracle_pack_flat(int32_t W, int32_t n, const void *const *grads, const int32_t *grad_dtype,
+                     const int64_t *numel, int64_t c, int32_t dst_dtype, void *out)
+{
+    int64_t F = 0;
+    for (int32_t t = 0; t < n; ++t) {
+        for (int64_t j = 0; j < numel[t]; ++j)
+            store_as(out, dst_dtype, F + j, load_as(grads[t], grad_dtype[t], j, dst_dtype));
+        F += numel[t];
+    }
+    if (F > (int64_t)W * c) return -1;
+    for (int64_t k = F; k < (int64_t)W * c; ++k) store_as(out, dst_dtype, k, 0u);
+    return 0;
+}
+
+/* Write-back for rank r from its reduced row (c elements of reduce_dtype):
+ * each parameter's piece, divided as in oracle_rs_copy_out, cast to its
+ * storage dtype:  grads[t][f - lo_t] = cast(div(row[f - r*c])), f in the piece. */
+int oracle_rs_copy_out_flat(int32_t rank, int32_t n, const void *row, int32_t reduce_dtype, int64_t c,
+                            float divide_factor, const int64_t *numel, const int32_t *storage_dtype,
+                            void *const *grads)
+{
+    int64_t F = 0;
+    for (int32_t t = 0; t < n; ++t) {
+        int64_t lo, hi;
+        flat_piece(F, numel[t], c, rank, &lo, &hi);
+        for (int64_t f = lo; f < hi; ++f) {
+            uint32_t x = load_as(row, reduce_dtype, f - (int64_t)rank * c, reduce_dtype);
+            if (divide_factor != 1.0f) x = divide_in(x, reduce_dtype, divide_factor);
+            store_as(grads[t], storage_dtype[t], f - lo, cast_bits(x, reduce_dtype, storage_dtype[t]));
+        }
+        F += numel[t];
+    }
+    return 0;
+}
+
+/* All-gather copy-in for rank r: `row` (c elements of param_dtype) receives
+ * each parameter's piece (shards[t]: the piece's elements in the storage
+ * dtype) cast to param_dtype at its flat position minus r*c; positions past
+ * N are +0. */
+int oracle_copy_in_flat(int32_t rank, int32_t n, const void *const *shards, const int32_t *storage_dtype,
+                        int32_t param_dtype, const int64_t *numel, int64_t c, void *row)
+{
+    for (int64_t k = 0; k < c; ++k) store_as(row, param_dtype, k, 0u);
+    int64_t F = 0;
+    for (int32_t t = 0; t < n; ++t) {
+        int64_t lo, hi;
+        flat_piece(F, numel[t], c, rank, &lo, &hi);
+        for (int64_t f = lo; f < hi; ++f)
+            store_as(row, param_dtype, f - (int64_t)rank * c,
+                     load_as(shards[t], storage_dtype[t], f - lo, param_dtype));
+        F += numel[t];
+    }
+    return 0;
+}
+
+/* All-gather copy-out: params[t][j] = flat[F[t] + j], flat = the gathered
+ * W*c elements of param_dtype. */
+int oracle_copy_out_flat(int32_t n, const void *flat, int32_t param_dtype, const int64_t *numel, void *const *params)
+{
+    int64_t F = 0;
+    for (int32_t t = 0; t < n; ++t) {
+        for (int64_t j = 0; j < numel[t]; ++j)
+            store_as(params[t], param_dtype, j, load_as(flat, param_dtype, F + j, param_dtype));
+        F += numel[t];
     }
     return 0;
 }
