@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pack-only", action="store_true",
                     help="run only pack launches (for counter collection under rocprofv3)")
+    ap.add_argument("--flat", action="store_true",
+                    help="FSDP1 flat-parameter layout of the workload (reduce in fp32, compute in bf16)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run plain 256 MiB device copies (known size) to calibrate byte counters")
     return ap.parse_args()
@@ -87,9 +89,15 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = wl.get(args.workload)
+    if args.flat:
+        # one flat parameter per unit: one reduction and one param dtype
+        ts = w.tensors
+        w = wl.custom([t.shape for t in ts], [t.grad_dtype for t in ts], [fp.FP32] * len(ts), w.world, w.seed,
+                      storage_dtypes=[t.storage_dtype for t in ts], param_dtypes=[fp.BF16] * len(ts),
+                      grad_sigma=w.grad_sigma, param_sigma=w.param_sigma)
     W = w.world
     t_plan = time.perf_counter()
-    plan = fp.plan_buckets(w.descs(), W)
+    plan = (fp.plan_buckets_flat if args.flat else fp.plan_buckets)(w.descs(), W)
     plan_us = (time.perf_counter() - t_plan) * 1e6
 
     # ---- algorithmic bytes (read + write) per launch
@@ -99,7 +107,11 @@ def main():
     for b in plan.buckets:
         rd = sum(plan.numel[i] * esz(w.tensors[i].grad_dtype) for i in b.members)
         pack_bytes.append(rd + W * b.S * esz(b.dtype))
-    copy_in_bytes = sum(P * (esz(t.storage_dtype) + esz(t.param_dtype)) for P, t in zip(plan.P, w.tensors))
+    if args.flat:   # rank 0's pieces read, its whole row (padding included) written
+        copy_in_bytes = sum(fp.valid_in_chunk(plan, i, 0) * esz(t.storage_dtype) for i, t in enumerate(w.tensors)) \
+            + plan.B
+    else:
+        copy_in_bytes = sum(P * (esz(t.storage_dtype) + esz(t.param_dtype)) for P, t in zip(plan.P, w.tensors))
     copy_out_bytes = sum(2 * t.numel * esz(t.param_dtype) for t in w.tensors)
     step_bytes = sum(pack_bytes) + copy_in_bytes + copy_out_bytes
 
@@ -120,12 +132,13 @@ def main():
     for r in range(R):
         g = [to_dev(a, t.grad_dtype) for a, t in zip(grads_h, w.tensors)]
         outs = [torch.empty(W * b.S, dtype=fp.TORCH_DTYPE[b.dtype], device=dev) for b in plan.buckets]
-        shards = [torch.randn(P, device=dev).to(fp.TORCH_DTYPE[t.storage_dtype]) for P, t in zip(plan.P, w.tensors)]
+        shard_len = [fp.valid_in_chunk(plan, i, 0) if args.flat else plan.P[i] for i in range(len(w.tensors))]
+        shards = [torch.randn(P, device=dev).to(fp.TORCH_DTYPE[t.storage_dtype]) for P, t in zip(shard_len, w.tensors)]
         ag = torch.randint(0, 255, (W * plan.B,), dtype=torch.uint8, device=dev)
         params = [torch.empty(t.numel, dtype=fp.TORCH_DTYPE[t.param_dtype], device=dev) for t in w.tensors]
         # pointer arrays validated once, reused every step (as a training loop
         # reuses its buffers)
-        sets.append((fp.prepare_grads(plan, g), outs, fp.prepare_shards(plan, shards), ag,
+        sets.append((fp.prepare_grads(plan, g), outs, fp.prepare_shards(plan, shards, 0), ag,
                      fp.prepare_params(plan, params), g))
     torch.cuda.synchronize()
 
@@ -197,7 +210,7 @@ def main():
     if not args.pack_only:
         # ---- pre-cast then homogeneous pack (the pages' comparator), our kernels, 2 launches
         bf_idx = [i for i, t in enumerate(w.tensors) if t.grad_dtype == fp.BF16]
-        if bf_idx and nb == 1 and plan.buckets[0].dtype == fp.FP32:
+        if bf_idx and nb == 1 and plan.buckets[0].dtype == fp.FP32 and not args.flat:
             cast_plan = fp.plan_buckets([(w.tensors[i].numel, 1, fp.BF16, fp.FP32, fp.FP32, fp.FP32)
                                          for i in bf_idx], 1)
             homo = fp.plan_buckets([(t.dim0, t.inner, fp.FP32, fp.FP32, fp.FP32, fp.FP32) for t in w.tensors], W)
@@ -402,7 +415,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16,fp32",
         "data": "synthetic",
-        "config": {"workload": args.workload, "world": W, "tensors": len(w.tensors),
+        "config": {"workload": args.workload + (" (FSDP1 flat layout)" if args.flat else ""), "world": W,
+                   "tensors": len(w.tensors),
                    "elements": sum(t.numel for t in w.tensors), "buckets": nb,
                    "step": "pack(all buckets)" + ("" if args.pack_only else " + copy_in(rank 0) + copy_out"),
                    "rotated_sets": R},

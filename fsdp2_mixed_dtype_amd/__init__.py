@@ -9,6 +9,7 @@ fallback: if ``libfsdppack.so`` is missing, loading fails loudly.
 
 Functions (same names as the C ABI without the ``fsdppack_`` prefix):
   plan_buckets(params, world)                  -> Plan
+  plan_buckets_flat(params, world)             -> Plan   (FSDP1 flat-parameter layout)
   pack_reduce_scatter_input(plan, bucket, grads, out, stream=None)
   all_gather_copy_in(plan, rank, shards, ag_out, stream=None)
   all_gather_copy_out(plan, ag, params, stream=None)
@@ -64,6 +65,7 @@ def lib():
         P_i32, P_i64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
         PP_i32, PP_i64 = ctypes.POINTER(P_i32), ctypes.POINTER(P_i64)
         L.fsdppack_plan_buckets.argtypes = [ctypes.POINTER(ParamDesc), i32, i32, ctypes.POINTER(vp)]
+        L.fsdppack_plan_buckets_flat.argtypes = [ctypes.POINTER(ParamDesc), i32, i32, ctypes.POINTER(vp)]
         L.fsdppack_plan_info.argtypes = [vp, P_i32, P_i32, P_i32]
         L.fsdppack_plan_bucket.argtypes = [vp, i32, P_i32, P_i64, P_i32, PP_i32, PP_i64, PP_i64]
         L.fsdppack_plan_all_gather_layout.argtypes = [vp, P_i64, PP_i64, PP_i64]
@@ -77,7 +79,7 @@ def lib():
         L.fsdppack_last_error.restype = ctypes.c_char_p
         L.fsdppack_counters.argtypes = [P_i64, i32]
         L.fsdppack_time_next_launch.argtypes = [vp, vp]
-        for f in (L.fsdppack_plan_buckets, L.fsdppack_plan_info, L.fsdppack_plan_bucket,
+        for f in (L.fsdppack_plan_buckets, L.fsdppack_plan_buckets_flat, L.fsdppack_plan_info, L.fsdppack_plan_bucket,
                   L.fsdppack_plan_all_gather_layout, L.fsdppack_pack_reduce_scatter_input,
                   L.fsdppack_all_gather_copy_in, L.fsdppack_all_gather_copy_out,
                   L.fsdppack_reduce_scatter_copy_out, L.fsdppack_counters, L.fsdppack_time_next_launch):
@@ -103,9 +105,10 @@ class Bucket:
 class Plan:
     """A planned fully_shard unit (owns the library handle)."""
 
-    def __init__(self, handle: int, descs):
+    def __init__(self, handle: int, descs, flat: bool = False):
         self._h = ctypes.c_void_p(handle)
         self.descs = tuple(descs)
+        self.flat = flat                 # FSDP1 flat-parameter layout (plan_buckets_flat)
         L = lib()
         nb, n, w = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
         _check(L.fsdppack_plan_info(self._h, ctypes.byref(nb), ctypes.byref(n), ctypes.byref(w)))
@@ -128,6 +131,8 @@ class Plan:
         self.P = tuple(P[i] for i in range(self.n))
         self.A = tuple(A[i] for i in range(self.n))
         self.numel = tuple(d.dim0 * d.inner for d in self.descs)
+        # flat layout: c per rank, parameter t at flat offset O_t of the one bucket
+        self.c = self.buckets[0].S if flat and self.buckets else 0
 
     @property
     def handle(self):
@@ -155,6 +160,18 @@ def plan_buckets(params, world: int) -> Plan:
     h = ctypes.c_void_p()
     _check(lib().fsdppack_plan_buckets(arr, len(descs), int(world), ctypes.byref(h)))
     return Plan(h.value, descs)
+
+
+def plan_buckets_flat(params, world: int) -> Plan:
+    """Plan one unit in the FSDP1 flat-parameter layout: the parameters
+    flattened and concatenated into one flat parameter, padded to W*c, rank r
+    holding flat positions [r*c, (r+1)*c).  One reduction dtype and one param
+    dtype for the unit."""
+    descs = [p if isinstance(p, ParamDesc) else ParamDesc(*[int(x) for x in p]) for p in params]
+    arr = (ParamDesc * max(1, len(descs)))(*descs)
+    h = ctypes.c_void_p()
+    _check(lib().fsdppack_plan_buckets_flat(arr, len(descs), int(world), ctypes.byref(h)))
+    return Plan(h.value, descs, flat=True)
 
 
 def _stream(stream):
@@ -204,12 +221,22 @@ def prepare_grads(plan: Plan, grads) -> PointerArray:
     return PointerArray(plan, "grads", grads, ptrs)
 
 
-def prepare_shards(plan: Plan, shards) -> PointerArray:
-    """Padded local shards by parameter index (storage dtype, P elements)."""
+def prepare_shards(plan: Plan, shards, rank: int | None = None) -> PointerArray:
+    """Local shards by parameter index (storage dtype): the padded rank
+    chunks (P elements), or for a flat plan the parameters' pieces on `rank`
+    (None allowed for an empty piece)."""
     if len(shards) != plan.n:
         raise ValueError(f"shards: expected {plan.n} entries, got {len(shards)}")
-    ptrs = [_ptr(s, plan.descs[i].storage_dtype, plan.P[i], f"shards[{i}]") for i, s in enumerate(shards)]
-    return PointerArray(plan, "shards", shards, ptrs)
+    if plan.flat:
+        if rank is None:
+            raise ValueError("shards of a flat plan depend on the rank")
+        ptrs = [_ptr(s, plan.descs[i].storage_dtype, valid_in_chunk(plan, i, rank), f"shards[{i}]")
+                if valid_in_chunk(plan, i, rank) else 0 for i, s in enumerate(shards)]
+    else:
+        ptrs = [_ptr(s, plan.descs[i].storage_dtype, plan.P[i], f"shards[{i}]") for i, s in enumerate(shards)]
+    arr = PointerArray(plan, "shards", shards, ptrs)
+    arr.rank = rank if plan.flat else None
+    return arr
 
 
 def prepare_params(plan: Plan, params) -> PointerArray:
@@ -256,7 +283,15 @@ def _bytes_ptr(t, nbytes: int, what: str):
 def all_gather_copy_in(plan: Plan, rank: int, shards, ag_out, stream=None):
     """Write row `rank` of the [W, B]-byte all-gather buffer from the rank's
     padded shards (P elements each, storage dtype)."""
-    arr = _prepared(plan, shards, "shards", prepare_shards)
+    if plan.flat:
+        if isinstance(shards, PointerArray):
+            if shards.kind != "shards" or shards.plan_handle != plan.handle.value or shards.rank != rank:
+                raise ValueError("pointer array was prepared for another plan or rank")
+            arr = shards.array
+        else:
+            arr = prepare_shards(plan, shards, rank).array
+    else:
+        arr = _prepared(plan, shards, "shards", prepare_shards)
     aptr = _bytes_ptr(ag_out, plan.world * plan.B, "ag_out")
     _check(lib().fsdppack_all_gather_copy_in(plan.handle, int(rank), arr, aptr, _stream(stream)))
     return ag_out
@@ -271,7 +306,11 @@ def all_gather_copy_out(plan: Plan, ag, params, stream=None):
 
 
 def valid_in_chunk(plan: Plan, index: int, rank: int) -> int:
-    """Real (non-padding) elements of parameter `index` in rank `rank`'s chunk."""
+    """Real (non-padding) elements of parameter `index` on rank `rank`: of its
+    rank chunk, or for a flat plan of its piece inside the rank's positions."""
+    if plan.flat:
+        F = plan.buckets[0].O[index]
+        return max(0, min(F + plan.numel[index], (rank + 1) * plan.c) - max(F, rank * plan.c))
     P = plan.P[index]
     return max(0, min(P, plan.numel[index] - rank * P))
 

@@ -160,7 +160,7 @@ int run_op(fsdppack_plan *p, const OpTable &op, size_t cache_index, const std::v
     PtrSlot *slot = nullptr;
     if (int rc = acquire_table(p->caches[cache_index], key, s, &slot)) return rc;
     WindowArgs args = op.args(true, shift);
-    args.W = p->W;
+
     args.table = slot->d_table;
     args.base = base;
     args.rank = rank;
@@ -180,8 +180,8 @@ int run_op(fsdppack_plan *p, const OpTable &op, size_t cache_index, const std::v
 
 extern "C" {
 
-int fsdppack_plan_buckets(const fsdppack_param_desc *params, int32_t n, int32_t world,
-                          fsdppack_plan **out_plan)
+namespace {
+int make_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdppack_plan **out_plan, bool flat)
 {
     if (out_plan == nullptr) return fail(FSDPPACK_EINVAL, "plan_buckets: out_plan is NULL");
     *out_plan = nullptr;
@@ -190,7 +190,7 @@ int fsdppack_plan_buckets(const fsdppack_param_desc *params, int32_t n, int32_t 
     std::string err;
     int rc;
     try {
-        rc = build_plan(params, n, world, p, err);
+        rc = flat ? build_plan_flat(params, n, world, p, err) : build_plan(params, n, world, p, err);
     } catch (const std::bad_alloc &) {
         rc = FSDPPACK_ENOMEM;
         err = "plan_buckets: out of host memory";
@@ -201,6 +201,19 @@ int fsdppack_plan_buckets(const fsdppack_param_desc *params, int32_t n, int32_t 
     }
     *out_plan = p;
     return FSDPPACK_OK;
+}
+}  // namespace
+
+int fsdppack_plan_buckets(const fsdppack_param_desc *params, int32_t n, int32_t world,
+                          fsdppack_plan **out_plan)
+{
+    return make_plan(params, n, world, out_plan, false);
+}
+
+int fsdppack_plan_buckets_flat(const fsdppack_param_desc *params, int32_t n, int32_t world,
+                               fsdppack_plan **out_plan)
+{
+    return make_plan(params, n, world, out_plan, true);
 }
 
 int fsdppack_plan_info(const fsdppack_plan *plan, int32_t *num_buckets, int32_t *num_params, int32_t *world)
@@ -274,6 +287,28 @@ int fsdppack_all_gather_copy_in(const fsdppack_plan *cplan, int32_t rank, const 
     if (!plan_ok(plan)) return fail(FSDPPACK_ESTATE, "all_gather_copy_in: invalid plan handle");
     if (rank < 0 || rank >= plan->W) return fail(FSDPPACK_EINVAL, "all_gather_copy_in: rank out of range");
     if (shards == nullptr) return fail(FSDPPACK_EINVAL, "all_gather_copy_in: shards is NULL");
+    if (plan->flat) {
+        // the rank's row of the flat parameter from its per-parameter pieces
+        if (plan->B > 0 && (ag_out == nullptr || !aligned(ag_out, dtype_bytes(plan->copy_in.reduce_dt))))
+            return fail(FSDPPACK_EINVAL, "all_gather_copy_in: ag_out is NULL or not aligned to its element size");
+        const OpTable &op = plan->copy_in;
+        std::vector<uint64_t> key(op.table_params.size(), 0);
+        for (size_t m = 0; m < key.size(); ++m) {
+            const int32_t t = op.table_params[m];
+            if (shard_elements(*plan, t, rank) == 0) continue;
+            const void *s = shards[t];
+            if (s == nullptr || !aligned(s, dtype_bytes(plan->params[t].storage_dtype)))
+                return fail(FSDPPACK_EINVAL, "all_gather_copy_in: shards[" + std::to_string(t) +
+                                                 "] is NULL or not aligned to its element size");
+            key[m] = reinterpret_cast<uint64_t>(s);
+        }
+        char *row = static_cast<char *>(ag_out) + static_cast<int64_t>(rank) * plan->B;
+        try {
+            return run_op(plan, op, plan->buckets.size(), key, row, stream, "all_gather_copy_in", rank);
+        } catch (const std::bad_alloc &) {
+            return fail(FSDPPACK_ENOMEM, "all_gather_copy_in: out of host memory");
+        }
+    }
     if (plan->B > 0 && (ag_out == nullptr || !aligned(ag_out, 4)))
         return fail(FSDPPACK_EINVAL, "all_gather_copy_in: ag_out is NULL or not 4-byte aligned");
     std::vector<uint64_t> key(plan->n, 0);
@@ -298,8 +333,9 @@ int fsdppack_all_gather_copy_out(const fsdppack_plan *cplan, const void *ag, voi
     fsdppack_plan *plan = const_cast<fsdppack_plan *>(cplan);
     if (!plan_ok(plan)) return fail(FSDPPACK_ESTATE, "all_gather_copy_out: invalid plan handle");
     if (params == nullptr) return fail(FSDPPACK_EINVAL, "all_gather_copy_out: params is NULL");
-    if (plan->B > 0 && (ag == nullptr || !aligned(ag, 4)))
-        return fail(FSDPPACK_EINVAL, "all_gather_copy_out: ag is NULL or not 4-byte aligned");
+    const int64_t ag_align = plan->flat && plan->n > 0 ? dtype_bytes(plan->params[0].param_dtype) : 4;
+    if (plan->B > 0 && (ag == nullptr || !aligned(ag, ag_align)))
+        return fail(FSDPPACK_EINVAL, "all_gather_copy_out: ag is NULL or misaligned");
     std::vector<uint64_t> key(plan->n, 0);
     for (int32_t t = 0; t < plan->n; ++t) {
         if (plan->numel[t] == 0) continue;
@@ -331,18 +367,19 @@ int fsdppack_reduce_scatter_copy_out(const fsdppack_plan *cplan, int32_t bucket,
     BucketPlan &b = plan->buckets[bucket];
     if (b.S > 0 && (rs_out == nullptr || !aligned(rs_out, dtype_bytes(b.dtype))))
         return fail(FSDPPACK_EINVAL, "reduce_scatter_copy_out: rs_out is NULL or not aligned to its element size");
-    // the table is indexed by parameter; members with no real element on this
-    // rank (and non-members) are not touched and may be NULL
-    std::vector<uint64_t> key(plan->n, 0);
-    for (size_t k = 0; k < b.members.size(); ++k) {
-        const int32_t t = b.members[k];
-        const int64_t v = std::max<int64_t>(0, std::min<int64_t>(b.P[k], plan->numel[t] - int64_t{rank} * b.P[k]));
-        if (v == 0) continue;
+    // the table is indexed by parameter (record order in a flat plan);
+    // members with no real element on this rank (and non-members) are not
+    // touched and may be NULL
+    const bool by_record = plan->flat;
+    std::vector<uint64_t> key(by_record ? b.write_back.table_params.size() : plan->n, 0);
+    for (size_t k = 0; k < (by_record ? key.size() : b.members.size()); ++k) {
+        const int32_t t = by_record ? b.write_back.table_params[k] : b.members[k];
+        if (shard_elements(*plan, t, rank) == 0) continue;
         void *g = shard_grads[t];
         if (g == nullptr || !aligned(g, dtype_bytes(plan->params[t].storage_dtype)))
             return fail(FSDPPACK_EINVAL, "reduce_scatter_copy_out: shard_grads[" + std::to_string(t) +
                                              "] is NULL or not aligned to its element size");
-        key[t] = reinterpret_cast<uint64_t>(g);
+        key[by_record ? k : static_cast<size_t>(t)] = reinterpret_cast<uint64_t>(g);
     }
     try {
         return run_op(plan, b.write_back, plan->buckets.size() + 2 + static_cast<size_t>(bucket), key,

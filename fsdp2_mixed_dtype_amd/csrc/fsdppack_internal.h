@@ -66,7 +66,7 @@ constexpr int kGroupLog2 = 6;
 // table); the other side is the call's packed buffer.
 enum : int32_t { kTableIsSource = 0, kTableIsDest = 1 };
 
-enum : int32_t { kOpPack = 0, kOpCopyIn = 1, kOpCopyOut = 2, kOpWriteBack = 3 };
+enum : int32_t { kOpPack = 0, kOpCopyIn = 1, kOpCopyOut = 2, kOpWriteBack = 3, kOpWriteBackFlat = 4, kOpCopyInFlat = 5 };
 
 // One bucket member of a reduce-scatter pack: columns [O, O + P) of every
 // row; `numel` elements of dtype src_dt.  The pack's pointer table is in
@@ -120,7 +120,20 @@ struct CopyOutTensor {
 };
 static_assert(sizeof(CopyOutTensor) == 40, "shared with the device");
 
-// Arguments of one launch (all three operations).
+// One parameter of an FSDP1 flat layout, for the flat write-back and copy-in:
+// flat positions [F, F + numel); its pieces (the part inside a rank's
+// positions) live in caller tensors of dtype dt reached through pointer-table
+// entry `slot`.
+struct FlatMember {
+    int64_t F;
+    int64_t numel;
+    int32_t slot;
+    int32_t dt;
+    int64_t reserved;
+};
+static_assert(sizeof(FlatMember) == 32, "shared with the device");
+
+// Arguments of one launch (every operation).
 struct WindowArgs {
     int32_t op;              // kOpPack / kOpCopyIn / kOpCopyOut
     int32_t n;               // entries of `members`
@@ -130,12 +143,14 @@ struct WindowArgs {
     int32_t reduce_dt;       // the bucket's reduction dtype (pack: destination; write-back: source)
     int32_t shift;           // pack / copy-in: bytes the destination starts past a cache-line boundary
     int32_t group_lg;        // pack: rows interleaved per row group, log2 (W is a multiple of 2^group_lg)
-    int32_t rank;            // write-back: the rank whose reduced row is written back
+    int32_t rank;            // write-back, flat copy-in: the rank
     float divisor;           // write-back: divide factor (1: no division)
+    int64_t flat_n;          // flat layout: the flat parameter's real length N (its rows hold S = c each)
     int64_t S;               // pack: row length in elements
     int64_t B;               // copy-in row bytes / copy-out row stride
     const void *members;     // PackMember / CopyInMember / CopyOutTensor array
-    const void *columns;     // ColumnWindow map: per kWindowBytes of a row (pack, copy-in) or per group (copy-out)
+    const void *columns;     // ColumnWindow map: per kWindowBytes of a row (pack, copy-in), of flat
+                             // positions (flat ops) or per group of windows (copy-out, write-back)
     const uint64_t *table;   // device pointer table, indexed by slot
     char *base;              // the call's packed buffer (destination or source)
 };
@@ -366,13 +381,77 @@ FSDPPACK_HD inline void write_back_window(const WindowArgs &a, int32_t w, F &&f)
     f(g);
 }
 
+// FSDP1 flat layout, write-back (COPY_IN false) or copy-in (COPY_IN true)
+// window w of rank a.rank's row: S = c elements of dtype reduce_dt (the
+// reduction dtype for the write-back, the param dtype for the copy-in), flat
+// positions [rank*c, rank*c + c).  The window's row elements [e0, e1) lie in
+// one or two kWindowBytes stretches of the flat-position map, which names the
+// parameters there; each overlap is a range between the row and that
+// parameter's piece (its part inside the rank's positions, starting at flat
+// position max(F, rank*c)).  The copy-in also writes the row's padding
+// (positions past N) as +0, a range with no source.
+template <bool COPY_IN, typename F>
+FSDPPACK_HD inline void flat_window(const WindowArgs &a, int32_t w, F &&f)
+{
+    const FSDPPACK_TABLE ColumnWindow *C = (const FSDPPACK_TABLE ColumnWindow *)a.columns;
+    const int lg = a.reduce_dt == kBF16 ? 1 : 2;          // log2 of the row's element size
+    int64_t y0, y1;
+    window_span(w, a.shift, a.S << lg, y0, y1);
+    const int64_t e0 = y0 >> lg, e1 = y1 >> lg;
+    const int64_t base = static_cast<int64_t>(a.rank) * a.S;   // flat position of row element 0
+    const int64_t f0 = base + e0, f1 = imin(base + e1, a.flat_n);
+    if (f0 < f1) {
+        const int32_t m0 = C[f0 >> (kWindowLog2 - lg)].first;
+        const ColumnWindow last = C[(f1 - 1) >> (kWindowLog2 - lg)];
+        for (int32_t m = m0; m < last.first + last.count; ++m) {
+            const uint64_t ptr = table_entry(a, m);      // pointer table in record order
+            const FlatMember fm = read_record<FlatMember>(a.members, m);
+            const int64_t b0 = imax(f0, fm.F), b1 = imin(f1, fm.F + fm.numel);
+            if (b1 <= b0) continue;                      // in the map's stretch, not in this window
+            const int64_t piece0 = imax(fm.F, base);
+            const int64_t in_piece = (b0 - piece0) * dtype_bytes(fm.dt), in_row = (b0 - base) << lg;
+            RangeRef g;
+            g.ptr = ptr;
+            g.src_off = COPY_IN ? in_piece : in_row;
+            g.dst_off = COPY_IN ? in_row : in_piece;
+            g.lo = 0;
+            g.hi = b1 - b0;
+            g.valid = g.hi;
+            g.slot = m;
+            g.param = fm.slot;
+            g.src_dt = COPY_IN ? fm.dt : a.reduce_dt;
+            g.dst_dt = COPY_IN ? a.reduce_dt : fm.dt;
+            g.table_side = COPY_IN ? kTableIsSource : kTableIsDest;
+            f(g);
+        }
+    }
+    if (COPY_IN && base + e1 > a.flat_n) {
+        const int64_t z0 = imax(e0, a.flat_n - base);    // first padding element of the window
+        RangeRef g;
+        g.ptr = 0;
+        g.src_off = 0;
+        g.dst_off = z0 << lg;
+        g.lo = 0;
+        g.hi = e1 - z0;
+        g.valid = 0;                                      // all +0: no source element is read
+        g.slot = 0;
+        g.param = -1;
+        g.src_dt = a.reduce_dt;
+        g.dst_dt = a.reduce_dt;
+        g.table_side = kTableIsSource;
+        f(g);
+    }
+}
+
 template <typename F>
 FSDPPACK_HD inline void for_each_range(const WindowArgs &a, int32_t w, F &&f)
 {
     if (a.op == kOpPack) pack_window(a, w, f);
     else if (a.op == kOpCopyIn) copy_in_window(a, w, f);
     else if (a.op == kOpCopyOut) copy_out_window(a, w, f);
-    else write_back_window(a, w, f);
+    else if (a.op == kOpWriteBack) write_back_window(a, w, f);
+    else if (a.op == kOpWriteBackFlat) flat_window<false>(a, w, f);
+    else flat_window<true>(a, w, f);
 }
 
 // Launch the window kernel on `stream`: one workgroup per window.

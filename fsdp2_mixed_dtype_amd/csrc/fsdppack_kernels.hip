@@ -376,7 +376,13 @@ __global__ void __launch_bounds__(kBlock) window_kernel(WindowArgs a)
     if constexpr (OP == kOpPack) pack_window(a, w, body);
     else if constexpr (OP == kOpCopyIn) copy_in_window(a, w, body);
     else if constexpr (OP == kOpCopyOut) copy_out_window(a, w, body);
-    else if (a.divisor != 1.0f)    // uniform across the launch
+    else if constexpr (OP == kOpCopyInFlat) flat_window<true>(a, w, body);
+    else if constexpr (OP == kOpWriteBackFlat) {
+        if (a.divisor != 1.0f)     // uniform across the launch
+            flat_window<false>(a, w, [&](const RangeRef &g) { run_range<true, true>(g, a.base, a.divisor); });
+        else
+            flat_window<false>(a, w, body);
+    } else if (a.divisor != 1.0f)
         write_back_window(a, w, [&](const RangeRef &g) { run_range<true, true>(g, a.base, a.divisor); });
     else
         write_back_window(a, w, body);
@@ -395,7 +401,10 @@ int launch_windows(const WindowArgs &args, void *stream, void *start_event, void
     if (args.op == kOpPack) hipExtLaunchKernelGGL(window_kernel<kOpPack>, grid, block, 0, st, e0, e1, 0, args);
     else if (args.op == kOpCopyIn) hipExtLaunchKernelGGL(window_kernel<kOpCopyIn>, grid, block, 0, st, e0, e1, 0, args);
     else if (args.op == kOpCopyOut) hipExtLaunchKernelGGL(window_kernel<kOpCopyOut>, grid, block, 0, st, e0, e1, 0, args);
-    else hipExtLaunchKernelGGL(window_kernel<kOpWriteBack>, grid, block, 0, st, e0, e1, 0, args);
+    else if (args.op == kOpWriteBack) hipExtLaunchKernelGGL(window_kernel<kOpWriteBack>, grid, block, 0, st, e0, e1, 0, args);
+    else if (args.op == kOpWriteBackFlat)
+        hipExtLaunchKernelGGL(window_kernel<kOpWriteBackFlat>, grid, block, 0, st, e0, e1, 0, args);
+    else hipExtLaunchKernelGGL(window_kernel<kOpCopyInFlat>, grid, block, 0, st, e0, e1, 0, args);
     return static_cast<int>(hipGetLastError());
 }
 

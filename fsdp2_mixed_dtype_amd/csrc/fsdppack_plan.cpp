@@ -52,8 +52,10 @@ static void build_group_map(OpTable &op)
     }
 }
 
-int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdppack_plan *plan,
-               std::string &err)
+// Checks shared by both layouts; fills W, n, params, numel and the
+// per-parameter rank-chunk sizes P.
+static int validate(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdppack_plan *plan,
+                    std::string &err)
 {
     if (n < 0 || (n > 0 && params == nullptr)) { err = "plan_buckets: params is NULL or n < 0"; return FSDPPACK_EINVAL; }
     if (world < 1) { err = "plan_buckets: world size must be >= 1"; return FSDPPACK_EINVAL; }
@@ -86,6 +88,14 @@ int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdp
         plan->numel[t] = numel;
         plan->P[t] = chunk;
     }
+    return FSDPPACK_OK;
+}
+
+int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdppack_plan *plan,
+               std::string &err)
+{
+    if (int rc = validate(params, n, world, plan, err)) return rc;
+    const int64_t W = world;
 
     // buckets by effective reduction dtype, first appearance order
     std::map<int32_t, size_t> index_of;
@@ -127,6 +137,7 @@ int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdp
         // every row
         OpTable &op = b.pack;
         op.op = kOpPack;
+        op.rows = static_cast<int32_t>(W);
         op.reduce_dt = b.dtype;
         op.S = b.S;
         const int64_t dsz = dtype_bytes(b.dtype);
@@ -261,6 +272,180 @@ int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdp
             op.add(m);
             win += (bytes + kWindowBytes - 1) / kWindowBytes;
             if (win > kMaxWindows) { err = "plan_buckets: parameters need too many copy-out workgroups"; return FSDPPACK_EINVAL; }
+            op.src_bytes += bytes;
+        }
+        op.n_windows = static_cast<int32_t>(win);
+        op.dst_bytes = op.src_bytes;
+        build_group_map(op);
+    }
+    return FSDPPACK_OK;
+}
+
+int64_t shard_elements(const fsdppack_plan &plan, int32_t t, int32_t r)
+{
+    if (plan.flat) {
+        const int64_t lo = std::max(plan.fl.F[t], int64_t{r} * plan.fl.c);
+        const int64_t hi = std::min(plan.fl.F[t] + plan.numel[t], (int64_t{r} + 1) * plan.fl.c);
+        return std::max<int64_t>(0, hi - lo);
+    }
+    return std::max<int64_t>(0, std::min(plan.P[t], plan.numel[t] - int64_t{r} * plan.P[t]));
+}
+
+// Flat-position map of FlatMember records (consecutive, tiling [0, N) in
+// order, empty parameters left out): for each stretch of E positions, the
+// records overlapping it.
+static void build_flat_map(OpTable &op, const std::vector<FlatMember> &mem, int64_t N, int64_t E)
+{
+    const int64_t nx = (N + E - 1) / E;
+    op.columns.resize(static_cast<size_t>(nx));
+    size_t first = 0;
+    for (int64_t x = 0; x < nx; ++x) {
+        const int64_t f0 = x * E, f1 = std::min(N, f0 + E);
+        while (first < mem.size() && mem[first].F + mem[first].numel <= f0) ++first;
+        size_t last = first;
+        while (last < mem.size() && mem[last].F < f1) ++last;
+        op.columns[x] = ColumnWindow{static_cast<int32_t>(first), static_cast<int32_t>(last - first)};
+    }
+}
+
+int build_plan_flat(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdppack_plan *plan,
+                    std::string &err)
+{
+    if (int rc = validate(params, n, world, plan, err)) return rc;
+    const int64_t W = world;
+    plan->flat = true;
+    if (n == 0) return FSDPPACK_OK;
+    // one flat parameter: one reduction dtype, one param dtype
+    const int32_t rdt = params[0].reduce_dtype != kNone ? params[0].reduce_dtype : params[0].grad_dtype;
+    const int32_t pdt = params[0].param_dtype;
+    for (int32_t t = 1; t < n; ++t) {
+        const int32_t eff = params[t].reduce_dtype != kNone ? params[t].reduce_dtype : params[t].grad_dtype;
+        if (eff != rdt || params[t].param_dtype != pdt) {
+            err = "plan_buckets_flat: a flat parameter needs one reduction dtype and one param dtype (parameter " +
+                  std::to_string(t) + " differs)";
+            return FSDPPACK_EDTYPE;
+        }
+    }
+    FlatLayout &fl = plan->fl;
+    fl.F.resize(n);
+    for (int32_t t = 0; t < n; ++t) {
+        fl.F[t] = fl.N;
+        fl.N += plan->numel[t];
+        if (fl.N > kMaxBytes / 4) { err = "plan_buckets_flat: flat parameter too large"; return FSDPPACK_EINVAL; }
+    }
+    fl.c = (fl.N + W - 1) / W;
+    const int64_t bsz = dtype_bytes(rdt), psz = dtype_bytes(pdt);
+    const int64_t kMaxWindows = INT32_MAX;
+
+    // introspection: one bucket whose members sit at flat offsets
+    plan->buckets.emplace_back();
+    BucketPlan &b = plan->buckets.back();
+    b.dtype = rdt;
+    b.S = fl.c;
+    for (int32_t t = 0; t < n; ++t) {
+        b.members.push_back(t);
+        b.P.push_back(plan->numel[t]);
+        b.O.push_back(fl.F[t]);
+        plan->P[t] = plan->numel[t];
+        plan->A[t] = fl.F[t] * psz;
+    }
+    plan->B = fl.c * psz;
+
+    // pack: one row of W*c elements, members at their flat offsets; the last
+    // member's chunk also covers the padding up to W*c (+0, never read)
+    {
+        OpTable &op = b.pack;
+        op.op = kOpPack;
+        op.rows = 1;
+        op.reduce_dt = rdt;
+        op.S = W * fl.c;
+        std::vector<PackMember> mem;
+        for (int32_t t = 0; t < n; ++t) {
+            if (plan->numel[t] == 0) continue;
+            PackMember m{};
+            m.O = fl.F[t];
+            m.P = plan->numel[t];
+            m.numel = plan->numel[t];
+            m.param = t;
+            m.src_dt = params[t].grad_dtype;
+            mem.push_back(m);
+            op.table_params.push_back(t);
+            op.src_bytes += plan->numel[t] * dtype_bytes(m.src_dt);
+        }
+        if (!mem.empty()) mem.back().P += op.S - fl.N;
+        for (const PackMember &m : mem) op.add(m);
+        const int64_t gx = (op.S * bsz + kWindowBytes - 1) / kWindowBytes;
+        if (gx + 1 > kMaxWindows) { err = "plan_buckets_flat: reduce-scatter buffer needs too many workgroups"; return FSDPPACK_EINVAL; }
+        op.gx = static_cast<int32_t>(gx);
+        op.dst_bytes = op.S * bsz;
+        op.n_windows = static_cast<int32_t>(op.windows(0));
+        const int64_t E = kWindowBytes / bsz;
+        op.columns.resize(static_cast<size_t>(gx));
+        size_t first = 0;
+        for (int64_t x = 0; x < gx; ++x) {
+            const int64_t c0 = x * E, c1 = std::min(op.S, c0 + E);
+            while (first < mem.size() && mem[first].O + mem[first].P <= c0) ++first;
+            size_t last = first;
+            while (last < mem.size() && mem[last].O < c1) ++last;
+            op.columns[x] = ColumnWindow{static_cast<int32_t>(first), static_cast<int32_t>(last - first)};
+        }
+    }
+
+    // write-back and copy-in: windows over a rank's row, records by flat offset
+    std::vector<FlatMember> fm;
+    std::vector<int32_t> fm_params;
+    for (int32_t t = 0; t < n; ++t) {
+        if (plan->numel[t] == 0) continue;
+        FlatMember m{};
+        m.F = fl.F[t];
+        m.numel = plan->numel[t];
+        m.slot = t;
+        m.dt = params[t].storage_dtype;
+        fm.push_back(m);
+        fm_params.push_back(t);
+    }
+    for (int which = 0; which < 2; ++which) {
+        const bool copy_in = which == 1;
+        OpTable &op = copy_in ? plan->copy_in : b.write_back;
+        op.op = copy_in ? kOpCopyInFlat : kOpWriteBackFlat;
+        op.reduce_dt = copy_in ? pdt : rdt;        // the row's dtype
+        op.S = fl.c;
+        op.flat_n = fl.N;
+        for (const FlatMember &m : fm) op.add(m);
+        op.table_params = fm_params;               // pointer table in record order
+        const int64_t rsz = copy_in ? psz : bsz;
+        const int64_t row_bytes = fl.c * rsz;
+        op.B = row_bytes;
+        // the copy-in's windows follow the lines of its destination row; the
+        // write-back's row is its source, so its windows start at the row
+        op.dst_bytes = copy_in ? row_bytes : 0;
+        if ((row_bytes + kLineBytes - 1 + kWindowBytes - 1) / kWindowBytes > kMaxWindows) {
+            err = "plan_buckets_flat: a rank's row needs too many workgroups";
+            return FSDPPACK_EINVAL;
+        }
+        op.n_windows = static_cast<int32_t>(copy_in ? op.windows(0) : (row_bytes + kWindowBytes - 1) / kWindowBytes);
+        build_flat_map(op, fm, fl.N, kWindowBytes / rsz);
+    }
+
+    // copy-out: each parameter is one contiguous stretch of the gathered flat parameter
+    {
+        OpTable &op = plan->copy_out;
+        op.op = kOpCopyOut;
+        op.B = plan->B;
+        int64_t win = 0;
+        for (int32_t t = 0; t < n; ++t) {
+            if (plan->numel[t] == 0) continue;
+            const int64_t bytes = plan->numel[t] * psz;
+            CopyOutTensor m{};
+            m.win0 = win;
+            m.numel = plan->numel[t];
+            m.P = plan->numel[t];
+            m.A = fl.F[t] * psz;
+            m.slot = t;
+            m.dt = pdt;
+            op.add(m);
+            win += (bytes + kWindowBytes - 1) / kWindowBytes;
+            if (win > kMaxWindows) { err = "plan_buckets_flat: parameters need too many copy-out workgroups"; return FSDPPACK_EINVAL; }
             op.src_bytes += bytes;
         }
         op.n_windows = static_cast<int32_t>(win);

@@ -28,6 +28,8 @@ struct OpTable {
     int32_t n_windows = 0;                // workgroups per launch (pack / copy-in: destination window-aligned)
     int32_t gx = 0;                       // pack: column-map entries
     int32_t group_lg = 0;                 // pack: log2 of the rows interleaved per row group
+    int32_t rows = 1;                     // pack: rows of the launch (W; 1 for a flat layout)
+    int64_t flat_n = 0;                   // flat ops: the flat parameter's real length N
     int32_t reduce_dt = 0;                // pack, write-back: the bucket's reduction dtype
     int64_t S = 0;                        // pack: row length (elements)
     int64_t B = 0;                        // all-gather row bytes
@@ -49,7 +51,7 @@ struct OpTable {
     // start at each parameter's first byte.
     int64_t windows(int32_t shift) const
     {
-        if (op == kOpCopyOut || op == kOpWriteBack) return n_windows;
+        if (op == kOpCopyOut || op == kOpWriteBack || op == kOpWriteBackFlat) return n_windows;
         if (dst_bytes == 0) return 0;
         if (op == kOpPack) return (static_cast<int64_t>(gx) + 1) * (dst_bytes / (S * dtype_bytes(reduce_dt)));
         return (shift + dst_bytes + kWindowBytes - 1) >> kWindowLog2;
@@ -60,7 +62,9 @@ struct OpTable {
         WindowArgs a{};
         a.op = op;
         a.n = n;
-        a.shift = (op == kOpCopyOut || op == kOpWriteBack) ? 0 : shift;
+        a.shift = (op == kOpCopyOut || op == kOpWriteBack || op == kOpWriteBackFlat) ? 0 : shift;
+        a.W = rows;
+        a.flat_n = flat_n;
         a.n_windows = static_cast<int32_t>(windows(a.shift));
         a.gx = gx;
         a.group_lg = group_lg;
@@ -80,6 +84,14 @@ struct BucketPlan {
     std::vector<int64_t> P, O;
     OpTable pack;
     OpTable write_back;   // reduce-scatter output -> the members' sharded gradients
+};
+
+// FSDP1 flat layout of a unit: one flat parameter of N elements, c per rank;
+// parameter t at flat offset F[t].
+struct FlatLayout {
+    int64_t N = 0;
+    int64_t c = 0;
+    std::vector<int64_t> F;
 };
 
 // Per-call pointer tables, cached on the device by content: the same grads /
@@ -114,6 +126,8 @@ struct fsdppack_plan {
     uint64_t magic = fsdppack::kPlanMagic;
     int32_t W = 1;
     int32_t n = 0;
+    bool flat = false;                        // FSDP1 flat-parameter layout (build_plan_flat)
+    fsdppack::FlatLayout fl;
     std::vector<fsdppack_param_desc> params;
     std::vector<int64_t> numel, P, A;
     int64_t B = 0;
@@ -132,5 +146,14 @@ namespace fsdppack {
 // Build the plan (host work only).  Returns a status code and fills `err`.
 int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdppack_plan *plan,
                std::string &err);
+
+// Build an FSDP1 flat-parameter plan (one reduction dtype and one param
+// dtype for the unit).
+int build_plan_flat(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdppack_plan *plan,
+                    std::string &err);
+
+// Real elements of parameter t on rank r: the rank chunk's (per-parameter
+// layout) or the piece inside the rank's flat positions (flat layout).
+int64_t shard_elements(const fsdppack_plan &plan, int32_t t, int32_t r);
 
 }  // namespace fsdppack

@@ -113,6 +113,31 @@ typedef struct fsdppack_plan fsdppack_plan;   /* opaque, library-owned */
 int fsdppack_plan_buckets(const fsdppack_param_desc *params, int32_t n, int32_t world,
                           fsdppack_plan **out_plan);
 
+/* Plan one unit in the FSDP1 flat-parameter layout ("The unit you wrapped",
+ * the auto_wrap_policy and padding paragraphs): the n parameters, flattened
+ * and concatenated in unit order, form one flat parameter of N elements
+ * (parameter t at flat offset F_t), padded to W*c, c = ceil(N / W); rank r
+ * holds flat positions [r*c, (r+1)*c).  The unit needs one effective
+ * reduction dtype and one param dtype; gradient and storage dtypes may differ
+ * per parameter.  The plan has one bucket (none when n = 0), and the compute
+ * calls take the flat meaning:
+ *  - pack_reduce_scatter_input: out ([W, c], the reduction dtype) = the
+ *    concatenated gradients cast, +0 past N;
+ *  - reduce_scatter_copy_out, all_gather_copy_in: the per-parameter entries
+ *    are parameter t's piece on the rank (the part of [F_t, F_t + numel_t)
+ *    inside the rank's positions, in the storage dtype; NULL allowed when
+ *    empty); rs_out is the rank's c reduced elements; the copy-in writes the
+ *    rank's row (c elements of the param dtype, +0 past N) of ag_out;
+ *  - all_gather_copy_out: ag is the gathered flat parameter, W*c elements of
+ *    the param dtype; parameter t is its elements [F_t, F_t + numel_t).
+ * Introspection: plan_bucket gives S = c, P_t = numel_t and O_t = F_t;
+ * plan_all_gather_layout gives B = c * size(param dtype) bytes (no rounding),
+ * P_t = numel_t and A_t = F_t * size(param dtype).
+ * Errors: as fsdppack_plan_buckets, and EDTYPE when the parameters' effective
+ * reduction dtypes or param dtypes differ. */
+int fsdppack_plan_buckets_flat(const fsdppack_param_desc *params, int32_t n, int32_t world,
+                               fsdppack_plan **out_plan);
+
 /* Number of buckets and parameters of a plan. */
 int fsdppack_plan_info(const fsdppack_plan *plan, int32_t *num_buckets, int32_t *num_params,
                        int32_t *world);

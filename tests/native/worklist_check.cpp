@@ -54,11 +54,22 @@ static bool check_range(const char *name, int32_t w, int32_t shift, const RangeR
                         int32_t nparams, DstSize dst_size, SrcSize src_size, std::vector<Intervals> &written)
 {
     CHECK(dtype_ok(g.src_dt) && dtype_ok(g.dst_dt), "%s: window %d bad dtype", name, w);
-    const int32_t entries = op.op == kOpPack ? op.n : nparams;     // pointer-table entries
+    CHECK(g.lo >= 0 && g.lo < g.hi, "%s: window %d empty or reversed range", name, w);
+    const bool by_record = op.op == kOpPack || op.op == kOpWriteBackFlat || op.op == kOpCopyInFlat;
+    if (g.param < 0) {
+        // a flat copy-in's padding: +0 only, no source and no table entry
+        CHECK(op.op == kOpCopyInFlat && g.valid == 0 && g.table_side == kTableIsSource,
+              "%s: window %d has a range without a parameter", name, w);
+        const int64_t d1 = g.dst_off + g.hi * dtype_bytes(g.dst_dt);
+        CHECK(g.dst_off >= 0 && d1 <= dst_size(g), "%s: window %d zero range [%lld,%lld) past %lld", name, w,
+              (long long)(g.dst_off + g.lo * dtype_bytes(g.dst_dt)), (long long)d1, (long long)dst_size(g));
+        written[0].emplace_back(g.dst_off + g.lo * dtype_bytes(g.dst_dt), d1);
+        return true;
+    }
+    const int32_t entries = by_record ? op.n : nparams;             // pointer-table entries
     CHECK(g.slot >= 0 && g.slot < entries, "%s: window %d slot %d out of range", name, w, g.slot);
     CHECK(g.param >= 0 && g.param < nparams, "%s: window %d param %d out of range", name, w, g.param);
-    CHECK(op.op != kOpPack || op.table_params[g.slot] == g.param, "%s: window %d table entry mismatch", name, w);
-    CHECK(g.lo >= 0 && g.lo < g.hi, "%s: window %d empty or reversed range", name, w);
+    CHECK(!by_record || op.table_params[g.slot] == g.param, "%s: window %d table entry mismatch", name, w);
     CHECK(g.valid >= 0, "%s: window %d negative valid", name, w);
     const int64_t dsz = dtype_bytes(g.dst_dt), ssz = dtype_bytes(g.src_dt);
     const int64_t d0 = g.dst_off + g.lo * dsz, d1 = g.dst_off + g.hi * dsz;
@@ -78,18 +89,24 @@ static bool check_op(const char *name, const OpTable &op, int32_t W, int32_t shi
                      DstSize dst_size, SrcSize src_size, std::vector<Intervals> &written, int32_t rank = 0)
 {
     WindowArgs a = op.args(false, shift);
-    a.W = W;
+    (void)W;   // rows come from the op table
     a.rank = rank;
     a.divisor = 1.0f;
     CHECK(a.n_windows == op.windows(shift) && (shift != 0 || a.n_windows == op.n_windows), "%s: window count", name);
     const size_t rec = op.op == kOpPack ? sizeof(PackMember)
-                       : op.op == kOpCopyIn ? sizeof(CopyInMember) : sizeof(CopyOutTensor);
+                       : op.op == kOpCopyIn ? sizeof(CopyInMember)
+                       : (op.op == kOpCopyInFlat || op.op == kOpWriteBackFlat) ? sizeof(FlatMember)
+                                                                                  : sizeof(CopyOutTensor);
     CHECK(op.members.size() == static_cast<size_t>(op.n) * rec, "%s: member table size", name);
     CHECK(op.n_windows == 0 || op.n > 0, "%s: windows without members", name);
     CHECK(op.op != kOpPack || (op.columns.size() == static_cast<size_t>(op.gx) &&
                                op.table_params.size() == static_cast<size_t>(op.n)), "%s: column map size", name);
     CHECK(op.op != kOpCopyIn || op.columns.size() == static_cast<size_t>((op.B + kWindowBytes - 1) / kWindowBytes),
           "%s: member map size", name);
+    CHECK((op.op != kOpCopyInFlat && op.op != kOpWriteBackFlat) ||
+              op.columns.size() == static_cast<size_t>((op.flat_n * dtype_bytes(op.reduce_dt) + kWindowBytes - 1) /
+                                                       kWindowBytes),
+          "%s: flat map size", name);
     CHECK((op.op != kOpCopyOut && op.op != kOpWriteBack) ||
               op.columns.size() == static_cast<size_t>((op.n_windows + (1 << kGroupLog2) - 1) >> kGroupLog2),
           "%s: group map size", name);
@@ -116,10 +133,11 @@ static bool check_op(const char *name, const OpTable &op, int32_t W, int32_t shi
             CHECK((ranges == 0) == spare, "%s: window %d (row %d, shift %d) has %d ranges", name, w, r, shift, ranges);
             row0 = shift + r * rb;
             row1 = row0 + rb;
-        } else if (op.op != kOpWriteBack) {   // write-back windows past a rank's real elements are empty
+        } else if (op.op != kOpWriteBack && op.op != kOpWriteBackFlat) {
+            // (write-back windows past a rank's real elements are empty)
             CHECK(ranges > 0, "%s: window %d has no range", name, w);
         }
-        if ((op.op == kOpPack || op.op == kOpCopyIn) && ranges > 0)
+        if ((op.op == kOpPack || op.op == kOpCopyIn || op.op == kOpCopyInFlat) && ranges > 0)
             CHECK((lo == row0 || lo % kLineBytes == 0) && (hi == row1 || hi % kLineBytes == 0) &&
                       hi - lo <= kWindowBytes,
                   "%s: window %d (shift %d) writes [%lld,%lld) from the aligned origin, off the line boundaries",
@@ -142,8 +160,9 @@ static bool tiles(Intervals v, int64_t size, const char *name)
     return true;
 }
 
-int main()
+int main(int argc, char **argv)
 {
+    const bool flat = argc > 1 && std::strcmp(argv[1], "flat") == 0;
     int32_t world, n;
     if (std::scanf("%d %d", &world, &n) != 2) { std::puts("FAIL bad header"); return 1; }
     std::vector<fsdppack_param_desc> d(n);
@@ -156,21 +175,30 @@ int main()
     }
     fsdppack_plan plan;
     std::string err;
-    if (build_plan(d.data(), n, world, &plan, err) != FSDPPACK_OK) {
+    const int rc = flat ? build_plan_flat(d.data(), n, world, &plan, err) : build_plan(d.data(), n, world, &plan, err);
+    if (rc != FSDPPACK_OK) {
         std::printf("FAIL plan: %s\n", err.c_str());
         return 1;
     }
     const int64_t W = plan.W;
+    auto fail = [] { std::printf("FAIL %s\n", g_fail.c_str()); return 1; };
     auto grad_bytes = [&](const RangeRef &g) { return plan.numel[g.param] * dtype_bytes(plan.params[g.param].grad_dtype); };
-    // destination offsets past a window boundary: the pack's output is only
-    // element aligned, the copy-in row 4-byte aligned
+    auto piece_bytes = [&](int32_t t, int32_t r) {
+        return shard_elements(plan, t, r) * dtype_bytes(plan.params[t].storage_dtype);
+    };
+    // ranks walked by the rank-dependent operations (a sample for large W)
+    std::vector<int32_t> ranks;
+    for (int32_t r = 0; r < plan.W; ++r)
+        if (plan.W <= 16 || r < 2 || r == plan.W / 2 || r >= plan.W - 2) ranks.push_back(r);
+    // destination offsets past a line boundary: the pack's output is only
+    // element aligned, the copy-in row 4-byte aligned (element aligned, flat)
     const int32_t kShiftUnits[] = {0, 1, 4, 27, 31};
     for (size_t bi = 0; bi < plan.buckets.size(); ++bi) {
         const BucketPlan &b = plan.buckets[bi];
         const int64_t out_bytes = W * b.S * dtype_bytes(b.dtype);
-        // the planner's row grouping, and every other one the world size allows
+        // the planner's row grouping, and every other one the rows allow
         for (int32_t glg = -1; glg <= 3; ++glg) {
-            if (glg >= 0 && (glg == b.pack.group_lg || W % (1 << glg) != 0)) continue;
+            if (glg >= 0 && (glg == b.pack.group_lg || b.pack.rows % (1 << glg) != 0)) continue;
             OpTable op = b.pack;
             if (glg >= 0) op.group_lg = glg;
             for (int32_t u : kShiftUnits) {
@@ -180,75 +208,59 @@ int main()
                 std::snprintf(name, sizeof name, "pack[%zu] rows/group %d shift %d", bi, 1 << op.group_lg, shift);
                 if (!check_op(name, op, plan.W, shift, n, [&](const RangeRef &) { return out_bytes; }, grad_bytes,
                               written) ||
-                    !tiles(written[0], out_bytes, name)) {
-                    std::printf("FAIL %s\n", g_fail.c_str());
-                    return 1;
-                }
+                    !tiles(written[0], out_bytes, name))
+                    return fail();
             }
         }
     }
-    for (int32_t u : kShiftUnits) {
-        const int32_t shift = (u * 4) % static_cast<int32_t>(kLineBytes);
-        std::vector<Intervals> written(1);
-        char name[64];
-        std::snprintf(name, sizeof name, "copy_in shift %d", shift);
-        auto shard_bytes = [&](const RangeRef &g) { return plan.P[g.param] * dtype_bytes(plan.params[g.param].storage_dtype); };
-        if (!check_op(name, plan.copy_in, plan.W, shift, n, [&](const RangeRef &) { return plan.B; }, shard_bytes,
-                      written) ||
-            !tiles(written[0], plan.B, name)) {
-            std::printf("FAIL %s\n", g_fail.c_str());
-            return 1;
+    const int64_t row_esz = flat ? dtype_bytes(plan.copy_in.reduce_dt) : 4;
+    for (int32_t r : flat ? ranks : std::vector<int32_t>{0}) {
+        for (int32_t u : kShiftUnits) {
+            const int32_t shift = static_cast<int32_t>((u * row_esz) % kLineBytes);
+            std::vector<Intervals> written(1);
+            char name[64];
+            std::snprintf(name, sizeof name, "copy_in rank %d shift %d", r, shift);
+            auto shard_bytes = [&](const RangeRef &g) {
+                return flat ? piece_bytes(g.param, r) : plan.P[g.param] * dtype_bytes(plan.params[g.param].storage_dtype);
+            };
+            if (!check_op(name, plan.copy_in, plan.W, shift, n, [&](const RangeRef &) { return plan.B; }, shard_bytes,
+                          written, r) ||
+                !tiles(written[0], plan.B, name))
+                return fail();
         }
     }
     {
         std::vector<Intervals> written(n);
         auto param_bytes = [&](const RangeRef &g) { return plan.numel[g.param] * dtype_bytes(plan.params[g.param].param_dtype); };
         if (!check_op("copy_out", plan.copy_out, plan.W, 0, n, param_bytes, [&](const RangeRef &) { return W * plan.B; },
-                      written)) {
-            std::printf("FAIL %s\n", g_fail.c_str());
-            return 1;
-        }
+                      written))
+            return fail();
         for (int32_t t = 0; t < n; ++t) {
             char name[64];
             std::snprintf(name, sizeof name, "copy_out param %d", t);
-            if (!tiles(written[t], plan.numel[t] * dtype_bytes(plan.params[t].param_dtype), name)) {
-                std::printf("FAIL %s\n", g_fail.c_str());
-                return 1;
-            }
+            if (!tiles(written[t], plan.numel[t] * dtype_bytes(plan.params[t].param_dtype), name)) return fail();
         }
     }
     for (size_t bi = 0; bi < plan.buckets.size(); ++bi) {
         const BucketPlan &b = plan.buckets[bi];
         const int64_t row_bytes = b.S * dtype_bytes(b.dtype);
-        std::vector<int32_t> ranks;
-        for (int32_t r = 0; r < plan.W; ++r)
-            if (plan.W <= 16 || r < 2 || r == plan.W / 2 || r >= plan.W - 2) ranks.push_back(r);
         for (int32_t r : ranks) {
             std::vector<Intervals> written(n);
             char name[64];
             std::snprintf(name, sizeof name, "write-back[%zu] rank %d", bi, r);
-            auto valid_bytes = [&](int32_t t, int64_t P) {
-                return std::max<int64_t>(0, std::min<int64_t>(P, plan.numel[t] - int64_t{r} * P)) *
-                       dtype_bytes(plan.params[t].storage_dtype);
-            };
             std::vector<int64_t> dst_limit(n, 0);
-            for (size_t k = 0; k < b.members.size(); ++k) dst_limit[b.members[k]] = valid_bytes(b.members[k], b.P[k]);
+            for (int32_t t : b.members) dst_limit[t] = piece_bytes(t, r);
             if (!check_op(name, b.write_back, plan.W, 0, n, [&](const RangeRef &g) { return dst_limit[g.param]; },
-                          [&](const RangeRef &) { return row_bytes; }, written, r)) {
-                std::printf("FAIL %s\n", g_fail.c_str());
-                return 1;
-            }
+                          [&](const RangeRef &) { return row_bytes; }, written, r))
+                return fail();
             for (int32_t t = 0; t < n; ++t) {
                 char tn[96];
                 std::snprintf(tn, sizeof tn, "%s param %d", name, t);
-                if (!tiles(written[t], dst_limit[t], tn)) {
-                    std::printf("FAIL %s\n", g_fail.c_str());
-                    return 1;
-                }
+                if (!tiles(written[t], dst_limit[t], tn)) return fail();
             }
         }
     }
-    std::printf("OK %zu buckets, windows:", plan.buckets.size());
+    std::printf("OK %s%zu buckets, windows:", flat ? "flat, " : "", plan.buckets.size());
     for (const BucketPlan &b : plan.buckets) std::printf(" %d (rows/group %d)", b.pack.n_windows, 1 << b.pack.group_lg);
     std::printf(" copy_in %d copy_out %d\n", plan.copy_in.n_windows, plan.copy_out.n_windows);
     return 0;

@@ -478,3 +478,93 @@ def test_rs_copy_out_pack_round_trip_with_divide():
             want = oracle.convert(oracle.convert(grads[i], t.grad_dtype, b.dtype), b.dtype, t.storage_dtype)
             assert np.array_equal(host_bytes(dst[i]), want[rank * P: rank * P + v].view(np.uint8)), i
     plan.destroy()
+
+
+# --------------------------------------------------------------------------- FSDP1 flat layout
+
+def _flat_of(w, reduce_dt=FP32, param_dt=BF16, W=None):
+    ts = w.tensors
+    return wl.custom([t.shape for t in ts], [t.grad_dtype for t in ts], [reduce_dt] * len(ts), W or w.world, w.seed,
+                     storage_dtypes=[t.storage_dtype for t in ts], param_dtypes=[param_dt] * len(ts))
+
+
+def check_flat(w, ranks, factors, seed=0, offsets=None):
+    """Pack, write-back, copy-in and copy-out of a flat plan vs the oracle."""
+    W = w.world
+    ref = oracle.plan_flat(w.descs(), W)
+    plan = fp.plan_buckets_flat(w.descs(), W)
+    assert plan.c == ref.c
+    rng = random.Random(seed)
+    off = (lambda i: rng.choice([0, 0, 1, 2, 3])) if offsets else (lambda i: 0)
+    # pack
+    grads = wl.make_grads(w)
+    wl.inject_specials(grads, [t.grad_dtype for t in w.tensors], seed=seed)
+    g_dev = [to_dev(g, t.grad_dtype, off(i)) for i, (g, t) in enumerate(zip(grads, w.tensors))]
+    packed = oracle.pack_flat(ref, grads)
+    if plan.buckets:
+        got = gpu_pack(plan, 0, g_dev, off(-1))
+        if not np.array_equal(got, packed.view(np.uint8).reshape(-1)):
+            bad = np.flatnonzero(got != packed.view(np.uint8).reshape(-1))
+            pytest.fail(f"{w.name}: flat pack differs in {bad.size} bytes, first at {bad[0]}")
+    # write-back of each rank's row (the packed row standing in for the reduced one)
+    for r in ranks:
+        for d in factors:
+            rs = to_dev(packed[r].copy(), ref.dtype, off(-2))
+            outs = [Guarded(oracle.piece_len(ref, i, r), t.storage_dtype, off(i)) if oracle.piece_len(ref, i, r)
+                    else None for i, t in enumerate(w.tensors)]
+            if plan.buckets:
+                fp.reduce_scatter_copy_out(plan, 0, r, rs, [o.t if o is not None else None for o in outs], d)
+                torch.cuda.synchronize()
+            wants = oracle.rs_copy_out_flat(ref, r, packed[r].copy(), d)
+            for i, (o, want) in enumerate(zip(outs, wants)):
+                if o is None:
+                    assert want.size == 0
+                elif not np.array_equal(o.result(), want.view(np.uint8)):
+                    pytest.fail(f"{w.name}: flat write-back rank {r} factor {d} param {i} differs")
+    # copy-in of every rank, then copy-out of the gathered flat parameter
+    params = wl.make_params(w)
+    ag = Guarded(W * ref.c, ref.param_dtype, off(-3))
+    rows = []
+    for r in range(W):
+        pieces = []
+        for i, (x, t) in enumerate(zip(params, w.tensors)):
+            lo, hi = oracle.flat_piece(ref, i, r)
+            pieces.append(x[max(0, lo - ref.F[i]): max(0, hi - ref.F[i])].copy() if hi > lo else np.zeros(0, x.dtype))
+        if plan.n:
+            fp.all_gather_copy_in(plan, r, [to_dev(p_, t.storage_dtype, off(i)) if p_.size else None
+                                            for i, (p_, t) in enumerate(zip(pieces, w.tensors))], ag.t)
+        rows.append(oracle.copy_in_flat(ref, r, pieces))
+    torch.cuda.synchronize()
+    flat = np.concatenate(rows) if rows else np.zeros(0, oracle.NP_DTYPE[ref.param_dtype])
+    if ref.c:
+        assert np.array_equal(ag.result(), flat.view(np.uint8)), f"{w.name}: flat copy-in rows differ"
+    outs = [Guarded(t.numel, ref.param_dtype, off(i)) for i, t in enumerate(w.tensors)]
+    if plan.n:
+        fp.all_gather_copy_out(plan, ag.t, [o.t for o in outs])
+        torch.cuda.synchronize()
+    for i, (o, want) in enumerate(zip(outs, oracle.copy_out_flat(ref, flat))):
+        assert np.array_equal(o.result(), want.view(np.uint8)), f"{w.name}: flat copy-out param {i} differs"
+    plan.destroy()
+
+
+@pytest.mark.parametrize("name", ["tiny", "mixed50m", "layout500", "hetero500"])
+def test_flat_layout_matches_oracle(name):
+    print(f"[flat parity] workload={name}", flush=True)
+    w = _flat_of(wl.get(name))
+    W = w.world
+    check_flat(w, ranks=range(W) if W <= 4 else [0, 1, W - 1], factors=[1.0, float(W)])
+
+
+def test_flat_layout_printed_units_and_random_misaligned():
+    # the page's units: two blocks of two Linear(6,6) on 4 (36 / 18 / 9 per rank), Linear(3,3) on 4
+    for k in (4, 2, 1):
+        print(f"[flat parity] {k} x Linear(6,6), W=4", flush=True)
+        check_flat(wl.custom([(6, 6)] * k, [FP32] * k, [FP32] * k, 4, seed=k), range(4), [1.0, 4.0])
+    check_flat(wl.custom([(3, 3)], [FP32], [FP32], 4, seed=9), range(4), [1.0, 2.0])
+    rng = random.Random(77)
+    for case in range(40):
+        base = _random_workload(rng, case)
+        w = _flat_of(base, rng.choice([BF16, FP32]), rng.choice([BF16, FP32]))
+        print(f"[flat random] case={case} W={w.world} n={len(w.tensors)}", flush=True)
+        check_flat(w, sorted({0, w.world - 1, rng.randrange(w.world)}), [1.0, rng.choice([2.0, 3.0, 0.5])],
+                   seed=case, offsets=True)

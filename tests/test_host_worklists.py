@@ -35,9 +35,9 @@ def checker(tmp_path_factory):
     return exe
 
 
-def _run(exe, descs, W):
+def _run(exe, descs, W, flat=False):
     text = f"{W} {len(descs)}\n" + "".join(" ".join(str(int(x)) for x in d) + "\n" for d in descs)
-    res = subprocess.run([exe], input=text, capture_output=True, text=True, timeout=600)
+    res = subprocess.run([exe] + (["flat"] if flat else []), input=text, capture_output=True, text=True, timeout=600)
     assert res.returncode == 0 and res.stdout.startswith("OK"), res.stdout + res.stderr[-3000:]
 
 
@@ -147,3 +147,76 @@ def test_compute_call_argument_errors_before_any_gpu_work():
     assert wb(None, 0, 0, 0x4000, 1.0, ptrs, None) == -5
     p.destroy()
     assert fp.counters()[0] == 0           # nothing was launched
+
+
+# --------------------------------------------------------------------------- FSDP1 flat layout
+
+def _flat_descs(descs, reduce_dt, param_dt):
+    """The same shapes as one flat parameter: one reduction and one param dtype."""
+    return [(d0, inner, g, reduce_dt, s_, param_dt) for d0, inner, g, _, s_, _ in descs]
+
+
+@pytest.mark.parametrize("name", list(wl.WORKLOADS))
+def test_flat_worklists_in_bounds_workloads(checker, name):
+    w = wl.get(name)
+    _run(checker, _flat_descs(w.descs(), FP32, BF16), w.world, flat=True)
+
+
+def test_flat_worklists_padding_past_a_map_stretch(checker):
+    # N a whole number of 2 KiB map stretches and padding that runs past the
+    # last one: the last rank's row must not look up a stretch beyond N
+    for n_el, W, dt in ((1536, 5, FP32), (2048, 3, BF16), (512, 3, FP32), (4096, 7, BF16)):
+        _run(checker, [(n_el, 1, dt, dt, dt, dt)], W, flat=True)
+        _run(checker, [(n_el - 8, 1, dt, dt, dt, dt), (8, 1, FP32, dt, BF16, dt)], W, flat=True)
+
+
+def test_flat_worklists_in_bounds_random(checker):
+    rng = random.Random(4321)
+    for _ in range(120):
+        descs, W = _random_layout(rng)
+        _run(checker, _flat_descs(descs, rng.choice([BF16, FP32]), rng.choice([BF16, FP32])), W, flat=True)
+
+
+def _flat_oracle_matches(descs, W):
+    p = fp.plan_buckets_flat(descs, W)
+    o = oracle.plan_flat(descs, W)
+    if not descs:
+        assert p.buckets == () and p.B == 0
+    else:
+        (b,) = p.buckets
+        assert (b.dtype, b.S, list(b.members), list(b.O), list(b.P)) == \
+               (o.dtype, o.c, list(range(len(descs))), o.F, [d.numel for d in o.params])
+        esz = oracle.ELEM_SIZE[o.param_dtype]
+        assert (p.B, list(p.A), list(p.P)) == (o.c * esz, [f * esz for f in o.F], [d.numel for d in o.params])
+        for r in range(W):
+            for i in range(len(descs)):
+                assert fp.valid_in_chunk(p, i, r) == oracle.piece_len(o, i, r)
+    p.destroy()
+
+
+def test_abi_flat_planner_matches_oracle():
+    rng = random.Random(7)
+    for _ in range(200):
+        descs, W = _random_layout(rng)
+        _flat_oracle_matches(_flat_descs(descs, rng.choice([BF16, FP32]), rng.choice([BF16, FP32])), W)
+    # the printed FSDP1 sizes: 36 / 18 / 9 per rank, and Linear(3,3) on 4
+    lin = (6, 6, FP32, 0, FP32, FP32)
+    for k, c in ((4, 36), (2, 18), (1, 9)):
+        p = fp.plan_buckets_flat([lin] * k, 4)
+        assert p.c == c
+        p.destroy()
+    p = fp.plan_buckets_flat([(3, 3, FP32, 0, FP32, FP32)], 4)
+    assert p.c == 3 and [fp.valid_in_chunk(p, 0, r) for r in range(4)] == [3, 3, 3, 0]
+    p.destroy()
+
+
+def test_flat_planner_errors():
+    with pytest.raises(fp.FsdpPackError) as e:       # two reduction dtypes
+        fp.plan_buckets_flat([(2, 2, FP32, 0, FP32, BF16), (2, 2, BF16, 0, FP32, BF16)], 2)
+    assert e.value.code == -2
+    with pytest.raises(fp.FsdpPackError) as e:       # two param dtypes
+        fp.plan_buckets_flat([(2, 2, FP32, 0, FP32, BF16), (2, 2, FP32, 0, FP32, FP32)], 2)
+    assert e.value.code == -2
+    empty = fp.plan_buckets_flat([], 3)
+    assert empty.buckets == () and empty.B == 0
+    empty.destroy()
