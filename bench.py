@@ -19,10 +19,13 @@ Prints ONE JSON line (rank 0):
                traffic from the committed rocprofv3 counter summary when it
                was taken on the current kernel source, else null
   cpu_baseline the CPU oracle's pack, single thread, on a bounded sample
-plus per-kernel times, the pre-cast-then-pack comparator and a plain-copy
-ceiling measured in the same run.
+plus, measured in the same run: per-kernel times, the pack's p10/p50/p90
+cold and warm, the pre-cast-then-pack comparator, a plain-copy ceiling, the
+reduce-scatter write-back of rank 0 (with the oracle's rate beside it) and
+the pack beside a stream of bf16 GEMMs.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--flat]
+(--flat: the workload's tensors as one FSDP1 flat parameter.)
 """
 from __future__ import annotations
 

@@ -1,13 +1,15 @@
 // fsdppack_internal.h -- plan tables and the window -> range mapping shared
 // by the host planner, the ABI layer and the HIP kernels of libfsdppack.
 //
-// Every operation of the library (reduce-scatter pack, all-gather copy-in,
-// all-gather copy-out) is the same primitive over *ranges*: a contiguous
+// Every operation of the library (reduce-scatter pack, reduce-scatter
+// write-back, all-gather copy-in and copy-out, in the per-parameter and the
+// FSDP1 flat layouts) is the same primitive over *ranges*: a contiguous
 // destination run whose first `valid` elements are the cast of a contiguous
 // source run and whose remaining elements are +0 (the right-hand padding of
 // a rank chunk, or the zero gap after an all-gather segment).  One side of
 // every range lives in a caller tensor reached through a per-call pointer
-// table; the other side is an offset into the call's single packed buffer.
+// table; the other side is an offset into the call's single packed buffer
+// (a range that is all +0 has no source).
 //
 // Work is cut into fixed *windows* of kWindowBytes of destination, one per
 // workgroup.  For the pack (per row) and the copy-in, window boundaries sit
@@ -17,15 +19,16 @@
 // reaches HBM as two partial writes.  A workgroup finds its ranges
 // arithmetically from its window index plus small per-plan tables: a map
 // with one entry per kWindowBytes of a row (pack, copy-in) or per group of
-// windows (copy-out) that names the records to visit, and the records.  The
+// windows (copy-out, write-back) or per kWindowBytes of flat positions (flat
+// layout) that names the records to visit, and the records.  The
 // tables are a few KB to a few hundred KB and every entry is read by many
 // workgroups, so they stay resident in the scalar cache and L2: no workgroup
 // waits on a cold record of its own before touching data (a per-workgroup
 // record, read cold, measured ~20 % slower on MI355X), and a wave makes two
 // rounds of table reads before its data (a binary search over hundreds of
-// records would make nine).  The mapping functions below are compiled both for the device
-// (the kernels) and for the host (the planner's bounds checker), so the
-// checker runs exactly the code the kernels run.
+// records would make nine).  The mapping functions below are compiled both
+// for the device (the kernels) and for the host (the planner's bounds
+// checker), so the checker runs exactly the code the kernels run.
 #pragma once
 
 #include <cstdint>
@@ -85,7 +88,8 @@ static_assert(sizeof(PackMember) == 32, "shared with the device");
 // first + count - 1.  Pack: the members overlapping columns [x*E, (x+1)*E)
 // of a row (E = kWindowBytes of elements), shared by all W rows.  Copy-in:
 // the members overlapping bytes [x*kWindowBytes, (x+1)*kWindowBytes) of the
-// row.  Copy-out: the tensors owning windows [j*64, (j+1)*64).
+// row.  Copy-out, write-back: the records owning windows [j*64, (j+1)*64).
+// Flat layout: the parameters overlapping flat positions [x*E, (x+1)*E).
 struct ColumnWindow {
     int32_t first;
     int32_t count;
@@ -122,8 +126,8 @@ static_assert(sizeof(CopyOutTensor) == 40, "shared with the device");
 
 // One parameter of an FSDP1 flat layout, for the flat write-back and copy-in:
 // flat positions [F, F + numel); its pieces (the part inside a rank's
-// positions) live in caller tensors of dtype dt reached through pointer-table
-// entry `slot`.
+// positions) live in caller tensors of dtype dt.  `slot` is the parameter
+// index; the pointer table of these operations is in record order.
 struct FlatMember {
     int64_t F;
     int64_t numel;
@@ -135,24 +139,25 @@ static_assert(sizeof(FlatMember) == 32, "shared with the device");
 
 // Arguments of one launch (every operation).
 struct WindowArgs {
-    int32_t op;              // kOpPack / kOpCopyIn / kOpCopyOut
+    int32_t op;              // kOpPack, kOpCopyIn, kOpCopyOut, kOpWriteBack, kOpWriteBackFlat, kOpCopyInFlat
     int32_t n;               // entries of `members`
     int32_t n_windows;       // workgroups
     int32_t gx;              // pack: entries of the column map (windows per row: gx + 1)
-    int32_t W;               // world size
-    int32_t reduce_dt;       // the bucket's reduction dtype (pack: destination; write-back: source)
+    int32_t W;               // pack: rows (the world size; 1 for a flat layout)
+    int32_t reduce_dt;       // pack: destination dtype, write-back: source dtype (the bucket's
+                             // reduction dtype); flat ops: the rank row's dtype
     int32_t shift;           // pack / copy-in: bytes the destination starts past a cache-line boundary
     int32_t group_lg;        // pack: rows interleaved per row group, log2 (W is a multiple of 2^group_lg)
     int32_t rank;            // write-back, flat copy-in: the rank
     float divisor;           // write-back: divide factor (1: no division)
     int64_t flat_n;          // flat layout: the flat parameter's real length N (its rows hold S = c each)
-    int64_t S;               // pack: row length in elements
+    int64_t S;               // pack: row length in elements; flat ops: c, a rank's row length
     int64_t B;               // copy-in row bytes / copy-out row stride
-    const void *members;     // PackMember / CopyInMember / CopyOutTensor array
+    const void *members;     // PackMember / CopyInMember / CopyOutTensor / FlatMember records
     const void *columns;     // ColumnWindow map: per kWindowBytes of a row (pack, copy-in), of flat
                              // positions (flat ops) or per group of windows (copy-out, write-back)
-    const uint64_t *table;   // device pointer table, indexed by slot
-    char *base;              // the call's packed buffer (destination or source)
+    const uint64_t *table;   // device pointer table (by record for the pack and flat ops, else by parameter)
+    char *base;              // the call's packed buffer or row (destination or source)
 };
 
 // One contiguous range for the copy primitive: elements [lo, hi) of a chunk
@@ -166,7 +171,7 @@ struct RangeRef {
     int64_t hi;
     int64_t valid;
     int32_t slot;            // pointer-table entry
-    int32_t param;           // parameter index (host-side checks)
+    int32_t param;           // parameter index (host-side checks; -1 for a range that is all +0)
     int32_t src_dt;
     int32_t dst_dt;
     int32_t table_side;

@@ -4,18 +4,21 @@
 // One launch moves a whole operation: the reduce-scatter pack of a bucket
 // (every (rank, tensor) chunk, cast to the reduction dtype and zero-padded:
 // "PyTorch adds per-parameter mixed precision to FSDP2", paragraph 2), the
+// write-back of a rank's reduced row into its sharded gradients ("The unit
+// you wrapped", the paragraphs on the collectives FSDP issues), the
 // all-gather copy-in of one rank (every shard cast to its compute dtype,
 // paragraph 1) or the all-gather copy-out (every gathered segment back into
-// its full parameter, padding dropped).
+// its full parameter, padding dropped); each in the per-parameter layout or
+// the FSDP1 flat layout.
 //
 // The work is pure data movement with a handful of integer operations per
-// element, so the design aims at HBM bandwidth, not at the matrix cores:
-//  * each workgroup (one wave64) owns one 2 KiB window of destination,
-//    finds the rank chunks it overlaps from its index and the plan's small
-//    tables (a column map for the pack), and walks them;
-//  * every destination byte is written by a 16-byte vector store from its
-//    16-byte aligned address (scalar stores only at a range's unaligned head
-//    and tail), 64-lane wavefronts covering 1 KiB per store instruction;
+// element (plus one division per element in a dividing write-back), so the
+// design aims at HBM bandwidth, not at the matrix cores:
+//  * each workgroup (one wave64) owns one 2 KiB window, finds the ranges it
+//    overlaps from its index and the plan's small tables, and walks them;
+//  * every whole 16-byte destination vector is written by one 16-byte vector
+//    store (element stores only at a range's unaligned head and tail),
+//    64-lane wavefronts covering 1 KiB per store instruction;
 //  * source vectors come from 8- or 16-byte loads that need only dword
 //    alignment; a bf16 source sitting 2 bytes past a dword boundary loads
 //    one extra dword and shifts adjacent dwords by 16 bits, so no load ever

@@ -14,6 +14,14 @@
 // 16-byte aligned byte offset, unit order, so that one all-gather carries
 // mixed target dtypes ("PyTorch adds per-parameter mixed precision to
 // FSDP2", paragraph 1).
+//
+// FSDP1 flat layout (build_plan_flat): the unit's parameters flattened and
+// concatenated in unit order into one flat parameter, padded to W*ceil(N/W),
+// one contiguous piece per rank -- "The unit you wrapped", the
+// auto_wrap_policy and padding paragraphs.
+//
+// Each operation also gets its launch tables here: records, the map from a
+// window to the records it touches, and the launch geometry.
 #include "fsdppack_plan.h"
 
 #include <algorithm>

@@ -3,8 +3,9 @@
 // The planner follows "PyTorch adds per-parameter mixed precision to FSDP2"
 // (ainewsletter.today), paragraph 2, for bucketing (one reduction buffer per
 // effective reduction dtype), and "The unit you wrapped" (kernels.rudrite.com),
-// padding paragraphs, for the equal right-padded rank pieces.  It also builds
-// the member tables the kernels search (one per operation).
+// padding paragraphs, for the equal right-padded rank pieces (or, for the
+// FSDP1 flat layout, one flat parameter split into equal pieces).  It also
+// builds the record tables and maps the kernels read (one per operation).
 #pragma once
 
 #include <cstdint>
