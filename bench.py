@@ -273,6 +273,7 @@ def main():
         torch.cuda.synchronize()
         copy_ms = c0.elapsed_time(c1) / K      # back-to-back copies, events around the batch
         extra["copy_ceiling_GBps"] = round(2 * (nbytes // 4) * 4 / (copy_ms * 1e-3) / 1e9, 1)
+        extra["pack_frac_of_copy_ceiling"] = round(pack_gbps / extra["copy_ceiling_GBps"], 4)
         del src, dst
 
         # ---- reduce-scatter write-back of rank 0 (the step after the
@@ -405,7 +406,14 @@ def main():
             t_cpu += time.perf_counter() - ta
             reps += 1
         cpu_gbps = reps * sum(pack_bytes) / t_cpu / 1e9
+        cpu_model = None
+        try:
+            with open("/proc/cpuinfo") as f:
+                cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+        except OSError:
+            pass
         cpu = {"value": round(cpu_gbps, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "host_cores_available": len(os.sched_getaffinity(0)), "cpu_model": cpu_model,
                "sample": f"oracle pack of every bucket of {args.workload}, full size, repeated {reps}x "
                          f"({t_cpu:.1f} s, single thread); GB/s under the same byte model",
                "ms_per_pack": round(t_cpu / reps * 1e3, 2)}
