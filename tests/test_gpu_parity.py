@@ -568,3 +568,68 @@ def test_flat_layout_printed_units_and_random_misaligned():
         print(f"[flat random] case={case} W={w.world} n={len(w.tensors)}", flush=True)
         check_flat(w, sorted({0, w.world - 1, rng.randrange(w.world)}), [1.0, rng.choice([2.0, 3.0, 0.5])],
                    seed=case, offsets=True)
+
+
+# --------------------------------------------------------------------------- beyond 2^31 elements
+
+def _pattern_bits(idx):
+    """bf16 bit pattern of element idx (int64 array or tensor): a hash of the
+    index, finite (|exponent| bits below 0x80), with a hashed sign."""
+    h = (idx * 2654435761) & 0xFFFFFFFF
+    return ((h >> 16) & 0x3FFF) | ((h >> 1) & 0x8000)
+
+
+def test_pack_and_write_back_beyond_2_31_elements():
+    """One bf16 gradient of 2^31 + 2^20 + 3 elements (4.3 GB) and a small fp32
+    one, W=2: the [2, S] fp32 pack (8.6 GB) and rank 1's write-back divided by 2
+    checked on sampled positions against the definition (element offsets past
+    2^31 exercise every 64-bit index path)."""
+    numel = (1 << 31) + (1 << 20) + 3
+    print(f"[beyond 2^31] numel={numel}", flush=True)
+    descs = [(numel, 1, BF16, FP32, FP32, BF16), (5, 3, FP32, FP32, FP32, BF16)]
+    plan = fp.plan_buckets(descs, 2)
+    b = plan.buckets[0]
+    P0, P1, S = b.P[0], b.P[1], b.S
+    assert (b.O[0], b.O[1]) == (0, P0) and P0 == (numel + 1) // 2
+    g0 = torch.empty(numel, dtype=torch.bfloat16, device=DEV)
+    bits0 = g0.view(torch.int16)
+    chunk = 1 << 28
+    for s in range(0, numel, chunk):
+        idx = torch.arange(s, min(numel, s + chunk), dtype=torch.int64, device=DEV)
+        bits0[s:s + idx.numel()] = _pattern_bits(idx).to(torch.int16)
+        del idx
+    g1_h = wl.random_array(15, FP32, seed=3)
+    g1 = to_dev(g1_h, FP32)
+    out = torch.empty(2 * S, dtype=torch.float32, device=DEV)
+    fp.pack_reduce_scatter_input(plan, 0, [g0, g1], out)
+    torch.cuda.synchronize()
+
+    rng = np.random.default_rng(31)
+    j = np.unique(np.concatenate([
+        rng.integers(0, P0, 20000),
+        np.arange(max(0, (1 << 31) - P0 - 4), min(P0, (1 << 31) - P0 + 4)),   # flat source index 2^31 on rank 1
+        np.arange(0, 4), np.arange(P0 - 4, P0)]))
+    for r in (0, 1):
+        src = r * P0 + j
+        want = np.where(src < numel, (_pattern_bits(src).astype(np.int64) & 0xFFFF) << 16, 0).astype(np.uint32)
+        got = out.view(torch.int32)[torch.from_numpy(r * S + j).to(DEV)].cpu().numpy().view(np.uint32)
+        assert np.array_equal(got, want), f"rank {r}: pack of the large tensor differs"
+        small = out[r * S + P0: r * S + P0 + P1].cpu().numpy()
+        v = max(0, min(P1, 15 - r * P1))
+        assert np.array_equal(small[:v].view(np.uint32), g1_h[r * P1: r * P1 + v].view(np.uint32))
+        assert not np.any(small[v:].view(np.uint32))
+
+    # write-back of rank 1 (its row of the pack standing in for the reduced row), divided by 2
+    v0 = numel - P0
+    dst0 = torch.empty(v0, dtype=torch.float32, device=DEV)
+    dst1 = torch.empty(max(0, min(P1, 15 - P1)), dtype=torch.float32, device=DEV)
+    fp.reduce_scatter_copy_out(plan, 0, 1, out[S:2 * S], [dst0, dst1], 2.0)
+    torch.cuda.synchronize()
+    jj = j[j < v0]
+    row1 = (_pattern_bits(P0 + jj).astype(np.int64) & 0xFFFF) << 16
+    want = (row1.astype(np.uint32).view(np.float32) / np.float32(2.0)).view(np.uint32)   # exact: a power of two
+    got = dst0.view(torch.int32)[torch.from_numpy(jj).to(DEV)].cpu().numpy().view(np.uint32)
+    assert np.array_equal(got, want), "write-back of the large tensor differs"
+    del g0, out, dst0
+    torch.cuda.empty_cache()
+    plan.destroy()
