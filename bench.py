@@ -68,11 +68,20 @@ def parse():
     return ap.parse_args()
 
 
+def _code_only(text):
+    """C/C++ source without comments and with whitespace runs collapsed, so
+    that editing a comment does not count as changing the kernel."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for path in KERNEL_SOURCES:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
