@@ -18,15 +18,15 @@
 // between two workgroups, possibly on different XCDs with separate L2s,
 // reaches HBM as two partial writes.  A workgroup finds its ranges
 // arithmetically from its window index plus small per-plan tables: a map
-// with one entry per kWindowBytes of a row (pack, copy-in) or per group of
-// windows (copy-out, write-back) or per kWindowBytes of flat positions (flat
-// layout) that names the records to visit, and the records.  The
-// tables are a few KB to a few hundred KB and every entry is read by many
-// workgroups, so they stay resident in the scalar cache and L2: no workgroup
-// waits on a cold record of its own before touching data (a per-workgroup
-// record, read cold, measured ~20 % slower on MI355X), and a wave makes two
-// rounds of table reads before its data (a binary search over hundreds of
-// records would make nine).  The mapping functions below are compiled both
+// with one entry per stretch of 2^map_lg bytes of a row (pack, copy-in, flat
+// layout; the planner sizes the stretch so the map has at most about a
+// thousand entries) or per group of windows (copy-out, write-back) that
+// names the records to visit, and the records.  The tables are a few KB and
+// every entry is read by many workgroups, so they stay resident in the
+// scalar cache and L2: no workgroup waits on a cold record of its own before
+// touching data (a per-workgroup record, read cold, measured ~20 % slower on
+// MI355X), and a wave makes two rounds of table reads before its data (a
+// binary search over hundreds of records would make nine).  The mapping functions below are compiled both
 // for the device (the kernels) and for the host (the planner's bounds
 // checker), so the checker runs exactly the code the kernels run.
 #pragma once
@@ -86,10 +86,10 @@ static_assert(sizeof(PackMember) == 32, "shared with the device");
 
 // The records a stretch of work touches: first, first + 1, ...,
 // first + count - 1.  Pack: the members overlapping columns [x*E, (x+1)*E)
-// of a row (E = kWindowBytes of elements), shared by all W rows.  Copy-in:
-// the members overlapping bytes [x*kWindowBytes, (x+1)*kWindowBytes) of the
-// row.  Copy-out, write-back: the records owning windows [j*64, (j+1)*64).
-// Flat layout: the parameters overlapping flat positions [x*E, (x+1)*E).
+// of a row (E = 2^map_lg bytes of elements), shared by all W rows.  Copy-in:
+// the members overlapping bytes [x*2^map_lg, (x+1)*2^map_lg) of the row.
+// Copy-out, write-back: the records owning windows [j*64, (j+1)*64).  Flat
+// layout: the parameters overlapping flat positions [x*E, (x+1)*E).
 struct ColumnWindow {
     int32_t first;
     int32_t count;
@@ -142,7 +142,7 @@ struct WindowArgs {
     int32_t op;              // kOpPack, kOpCopyIn, kOpCopyOut, kOpWriteBack, kOpWriteBackFlat, kOpCopyInFlat
     int32_t n;               // entries of `members`
     int32_t n_windows;       // workgroups
-    int32_t gx;              // pack: entries of the column map (windows per row: gx + 1)
+    int32_t gx;              // pack: windows per row, less the row's spare window
     int32_t W;               // pack: rows (the world size; 1 for a flat layout)
     int32_t reduce_dt;       // pack: destination dtype, write-back: source dtype (the bucket's
                              // reduction dtype); flat ops: the rank row's dtype
@@ -150,12 +150,13 @@ struct WindowArgs {
     int32_t group_lg;        // pack: rows interleaved per row group, log2 (W is a multiple of 2^group_lg)
     int32_t rank;            // write-back, flat copy-in: the rank
     float divisor;           // write-back: divide factor (1: no division)
+    int32_t map_lg;          // pack, copy-in, flat ops: log2 of the row bytes per entry of `columns`
     int64_t flat_n;          // flat layout: the flat parameter's real length N (its rows hold S = c each)
     int64_t S;               // pack: row length in elements; flat ops: c, a rank's row length
     int64_t B;               // copy-in row bytes / copy-out row stride
     const void *members;     // PackMember / CopyInMember / CopyOutTensor / FlatMember records
-    const void *columns;     // ColumnWindow map: per kWindowBytes of a row (pack, copy-in), of flat
-                             // positions (flat ops) or per group of windows (copy-out, write-back)
+    const void *columns;     // ColumnWindow map: per 2^map_lg bytes of a row (pack, copy-in) or of
+                             // flat positions (flat ops), or per group of windows (copy-out, write-back)
     const uint64_t *table;   // device pointer table (by record for the pack and flat ops, else by parameter)
     char *base;              // the call's packed buffer or row (destination or source)
 };
@@ -241,7 +242,7 @@ FSDPPACK_HD inline void pack_row_window(const WindowArgs &a, int32_t w, int32_t 
 // [k*kWindowBytes - s_r, (k+1)*kWindowBytes - s_r) of the row, clipped to it,
 // with s_r how far the row starts past a line boundary (a row's last window
 // is empty when its bytes fit in gx windows).  Its columns [c0, c1) lie in one
-// or two windows of the column map, whose entries name the members to visit:
+// or two stretches of the column map, whose entries name the members to visit:
 // a wave makes two rounds of table reads (the column entries, then each
 // member record with its pointer) before its data.
 template <typename F>
@@ -257,8 +258,8 @@ FSDPPACK_HD inline void pack_window(const WindowArgs &a, int32_t w, F &&f)
     window_span(k, s_r, rb, y0, y1);
     if (y1 <= y0) return;                                 // the row's spare window
     const int64_t c0 = y0 >> lg, c1 = y1 >> lg;
-    const int32_t x0 = static_cast<int32_t>(c0 >> (kWindowLog2 - lg));
-    const int32_t x1 = static_cast<int32_t>((c1 - 1) >> (kWindowLog2 - lg));
+    const int32_t x0 = static_cast<int32_t>(c0 >> (a.map_lg - lg));
+    const int32_t x1 = static_cast<int32_t>((c1 - 1) >> (a.map_lg - lg));
     const int32_t m0 = C[x0].first;
     const ColumnWindow last = C[x1];
     for (int32_t m = m0; m < last.first + last.count; ++m) {
@@ -282,8 +283,49 @@ FSDPPACK_HD inline void pack_window(const WindowArgs &a, int32_t w, F &&f)
     }
 }
 
+// A pack window that is one whole window of a single member's rank chunk,
+// every element real: the common case, which the kernel moves with a short
+// direct copy instead of the general range walk.  `src` is the address of
+// the window's first source element, `dst_off` the byte offset of its first
+// destination element in the packed buffer.
+struct DirectWindow {
+    uint64_t src;
+    int64_t dst_off;
+    int32_t src_dt;
+};
+
+// Whether pack window w is such a window (its stretches of the column map
+// name only the one member, whose chunk holds the whole window with no
+// padding, and both ends are aligned for whole 16-byte destination vectors
+// and dword source loads); fills `d` when it is.  The window then equals the
+// single range pack_window produces for it, with lo = c0 - O, hi = c1 - O
+// and every element below `valid`.
+FSDPPACK_HD inline bool pack_direct(const WindowArgs &a, int32_t w, DirectWindow &d)
+{
+    const FSDPPACK_TABLE ColumnWindow *C = (const FSDPPACK_TABLE ColumnWindow *)a.columns;
+    const int lg = a.reduce_dt == kBF16 ? 1 : 2;
+    int32_t r, k;
+    pack_row_window(a, w, r, k);
+    const int64_t rb = a.S << lg;
+    const int32_t s_r = static_cast<int32_t>((a.shift + r * rb) & (kLineBytes - 1));
+    int64_t y0, y1;
+    window_span(k, s_r, rb, y0, y1);
+    if (y1 - y0 != kWindowBytes) return false;
+    const int64_t c0 = y0 >> lg, c1 = y1 >> lg;
+    const ColumnWindow e0 = C[static_cast<int32_t>(c0 >> (a.map_lg - lg))];
+    const ColumnWindow e1 = C[static_cast<int32_t>((c1 - 1) >> (a.map_lg - lg))];
+    if (e0.count != 1 || e1.count != 1 || e1.first != e0.first) return false;
+    const uint64_t ptr = table_entry(a, e0.first);
+    const PackMember pm = read_record<PackMember>(a.members, e0.first);
+    if (c0 < pm.O || c1 > pm.O + pm.P || r * pm.P + (c1 - pm.O) > pm.numel) return false;
+    d.src = ptr + static_cast<uint64_t>((r * pm.P + (c0 - pm.O)) * dtype_bytes(pm.src_dt));
+    d.dst_off = (r * a.S + c0) << lg;
+    d.src_dt = pm.src_dt;
+    return (d.src & 3u) == 0 && ((a.shift + d.dst_off) & 15) == 0;
+}
+
 // Copy-in window w: bytes [y0, y1) of the row, which lie in one or two
-// kWindowBytes stretches of the member map.  Every member's span is a
+// stretches of the member map.  Every member's span is a
 // multiple of 16 bytes.
 template <typename F>
 FSDPPACK_HD inline void copy_in_window(const WindowArgs &a, int32_t w, F &&f)
@@ -291,8 +333,8 @@ FSDPPACK_HD inline void copy_in_window(const WindowArgs &a, int32_t w, F &&f)
     const FSDPPACK_TABLE ColumnWindow *C = (const FSDPPACK_TABLE ColumnWindow *)a.columns;
     int64_t y0, y1;
     window_span(w, a.shift, a.B, y0, y1);
-    const int32_t m0 = C[y0 >> kWindowLog2].first;
-    const ColumnWindow last = C[(y1 - 1) >> kWindowLog2];
+    const int32_t m0 = C[y0 >> a.map_lg].first;
+    const ColumnWindow last = C[(y1 - 1) >> a.map_lg];
     for (int32_t m = m0; m < last.first + last.count; ++m) {
         const CopyInMember cm = read_record<CopyInMember>(a.members, m);
         const int64_t b0 = imax(y0, cm.A), b1 = imin(y1, cm.A_next);
@@ -390,7 +432,7 @@ FSDPPACK_HD inline void write_back_window(const WindowArgs &a, int32_t w, F &&f)
 // window w of rank a.rank's row: S = c elements of dtype reduce_dt (the
 // reduction dtype for the write-back, the param dtype for the copy-in), flat
 // positions [rank*c, rank*c + c).  The window's row elements [e0, e1) lie in
-// one or two kWindowBytes stretches of the flat-position map, which names the
+// one or two stretches of the flat-position map, which names the
 // parameters there; each overlap is a range between the row and that
 // parameter's piece (its part inside the rank's positions, starting at flat
 // position max(F, rank*c)).  The copy-in also writes the row's padding
@@ -406,8 +448,8 @@ FSDPPACK_HD inline void flat_window(const WindowArgs &a, int32_t w, F &&f)
     const int64_t base = static_cast<int64_t>(a.rank) * a.S;   // flat position of row element 0
     const int64_t f0 = base + e0, f1 = imin(base + e1, a.flat_n);
     if (f0 < f1) {
-        const int32_t m0 = C[f0 >> (kWindowLog2 - lg)].first;
-        const ColumnWindow last = C[(f1 - 1) >> (kWindowLog2 - lg)];
+        const int32_t m0 = C[f0 >> (a.map_lg - lg)].first;
+        const ColumnWindow last = C[(f1 - 1) >> (a.map_lg - lg)];
         for (int32_t m = m0; m < last.first + last.count; ++m) {
             const uint64_t ptr = table_entry(a, m);      // pointer table in record order
             const FlatMember fm = read_record<FlatMember>(a.members, m);

@@ -15,7 +15,9 @@
 // element (plus one division per element in a dividing write-back), so the
 // design aims at HBM bandwidth, not at the matrix cores:
 //  * each workgroup (one wave64) owns one 2 KiB window, finds the ranges it
-//    overlaps from its index and the plan's small tables, and walks them;
+//    overlaps from its index and the plan's small tables, and walks them; a
+//    pack window inside a single member's chunk with no padding (nearly all
+//    of them in large layouts) skips the walk and copies directly;
 //  * every whole 16-byte destination vector is written by one 16-byte vector
 //    store (element stores only at a range's unaligned head and tail),
 //    64-lane wavefronts covering 1 KiB per store instruction;
@@ -41,10 +43,12 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // One wavefront per workgroup, two destination vectors per lane: a window
 // of kBlock * kUnroll * 16 = 2 KiB is one pass (loads issued, then stores),
 // and a launch has tens of thousands of short workgroups.  On MI355X this
-// shape kept the most bytes in flight once each wave's table reads are paid:
-// one vector per lane leaves too few bytes per wave behind those reads;
-// more vectors per lane, wider workgroups or persistent workgroups measured
-// no better.
+// shape kept the most bytes in flight once each wave's table reads are paid
+// (about a microsecond of dependent scalar loads and index arithmetic before
+// its first data load): one vector per lane, in one- to four-wave
+// workgroups, leaves too few bytes per wave behind those reads (25-35 %
+// slower even at full occupancy), and more vectors per lane, wider
+// workgroups or persistent workgroups measured no better.
 constexpr int kBlock = 64;    // threads per workgroup (one wave64)
 constexpr int kUnroll = 2;    // destination vectors per thread per pass
 static_assert(kBlock * kUnroll * 16 == kWindowBytes, "one window is one pass of the workgroup");
@@ -369,6 +373,35 @@ __device__ __forceinline__ void run_range(const RangeRef &g, char *base, float d
     }
 }
 
+// A whole window of one member's chunk (pack_direct): each lane loads its
+// kUnroll source vectors, converts them and stores them; no range walk.
+template <int S, int D>
+__device__ __forceinline__ void copy_window_direct(const char *src, char *dst)
+{
+    using P = Path<S, D>;
+    constexpr int64_t SV = P::V * static_cast<int64_t>(sizeof(typename P::ST));
+    const VecOut out(dst, kBlock * kUnroll);
+    const int tid = threadIdx.x;
+    uint32_t w[kUnroll][P::NSRC];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) load_dwords<P::NSRC, false>(src + (tid + u * kBlock) * SV, w[u]);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) out.put(tid + u * kBlock, convert_vec<S, D>(w[u]));
+}
+
+__device__ __forceinline__ void run_direct(const DirectWindow &d, int32_t dst_dt, char *base)
+{
+    const char *src = reinterpret_cast<const char *>(d.src);
+    char *dst = base + d.dst_off;
+    switch (d.src_dt * 4 + dst_dt) {
+    case kBF16 * 4 + kFP32: copy_window_direct<kBF16, kFP32>(src, dst); break;
+    case kFP32 * 4 + kFP32: copy_window_direct<kFP32, kFP32>(src, dst); break;
+    case kFP32 * 4 + kBF16: copy_window_direct<kFP32, kBF16>(src, dst); break;
+    case kBF16 * 4 + kBF16: copy_window_direct<kBF16, kBF16>(src, dst); break;
+    default: break;
+    }
+}
+
 // One workgroup per window; the window's ranges come from its index and the
 // plan's (cache-resident) record tables.
 template <int OP>
@@ -376,7 +409,11 @@ __global__ void __launch_bounds__(kBlock) window_kernel(WindowArgs a)
 {
     const int32_t w = static_cast<int32_t>(blockIdx.x);
     auto body = [&](const RangeRef &g) { run_range<OP != kOpPack, false>(g, a.base, 1.0f); };
-    if constexpr (OP == kOpPack) pack_window(a, w, body);
+    if constexpr (OP == kOpPack) {
+        DirectWindow d;
+        if (pack_direct(a, w, d)) run_direct(d, a.reduce_dt, a.base);
+        else pack_window(a, w, body);
+    }
     else if constexpr (OP == kOpCopyIn) copy_in_window(a, w, body);
     else if constexpr (OP == kOpCopyOut) copy_out_window(a, w, body);
     else if constexpr (OP == kOpCopyInFlat) flat_window<true>(a, w, body);

@@ -23,11 +23,13 @@ namespace fsdppack {
 struct OpTable {
     int32_t op = kOpPack;
     std::vector<unsigned char> members;   // PackMember / CopyInMember / CopyOutTensor records
-    std::vector<ColumnWindow> columns;    // record map (pack, copy-in: per kWindowBytes of a row; copy-out: per window group)
+    std::vector<ColumnWindow> columns;    // record map (pack, copy-in, flat ops: per 2^map_lg bytes of a row;
+                                          // copy-out, write-back: per window group)
     std::vector<int32_t> table_params;    // pointer-table entry -> parameter index
     int32_t n = 0;                        // records
     int32_t n_windows = 0;                // workgroups per launch (pack / copy-in: destination window-aligned)
-    int32_t gx = 0;                       // pack: column-map entries
+    int32_t gx = 0;                       // pack: windows per row, less the spare one
+    int32_t map_lg = kWindowLog2;         // pack, copy-in, flat ops: log2 of the bytes per map entry
     int32_t group_lg = 0;                 // pack: log2 of the rows interleaved per row group
     int32_t rows = 1;                     // pack: rows of the launch (W; 1 for a flat layout)
     int64_t flat_n = 0;                   // flat ops: the flat parameter's real length N
@@ -69,6 +71,7 @@ struct OpTable {
         a.n_windows = static_cast<int32_t>(windows(a.shift));
         a.gx = gx;
         a.group_lg = group_lg;
+        a.map_lg = map_lg;
         a.reduce_dt = reduce_dt;
         a.S = S;
         a.B = B;

@@ -15,8 +15,9 @@
 //    ends with its row, for several offsets of the destination past a line
 //    boundary; only the pack's spare window at the end of a row may have no
 //    range;
-//  * the record maps have one entry per kWindowBytes of a row (pack,
-//    copy-in) or per group of windows (copy-out, write-back);
+//  * the record maps have one entry per 2^map_lg bytes of a row (pack,
+//    copy-in, flat ops; at least a window) or per group of windows
+//    (copy-out, write-back);
 //  * the reduce-scatter write-back of every rank (a sample of ranks for large
 //    W) writes each member's real rank-chunk elements exactly once and reads
 //    only the rank's reduced row.
@@ -35,6 +36,7 @@
 using namespace fsdppack;
 
 static std::string g_fail;
+static int64_t g_direct = 0;   // pack windows taking the direct copy
 
 #define CHECK(cond, ...)                                                  \
     do {                                                                  \
@@ -99,13 +101,16 @@ static bool check_op(const char *name, const OpTable &op, int32_t W, int32_t shi
                                                                                   : sizeof(CopyOutTensor);
     CHECK(op.members.size() == static_cast<size_t>(op.n) * rec, "%s: member table size", name);
     CHECK(op.n_windows == 0 || op.n > 0, "%s: windows without members", name);
-    CHECK(op.op != kOpPack || (op.columns.size() == static_cast<size_t>(op.gx) &&
-                               op.table_params.size() == static_cast<size_t>(op.n)), "%s: column map size", name);
-    CHECK(op.op != kOpCopyIn || op.columns.size() == static_cast<size_t>((op.B + kWindowBytes - 1) / kWindowBytes),
+    // maps over a row: one entry per 2^map_lg bytes, at least a window's worth
+    const int64_t stretch = int64_t{1} << op.map_lg;
+    CHECK(op.map_lg >= kWindowLog2 && op.map_lg < 48, "%s: map stretch 2^%d bytes", name, op.map_lg);
+    CHECK(op.op != kOpPack ||
+              (op.columns.size() == static_cast<size_t>((op.S * dtype_bytes(op.reduce_dt) + stretch - 1) / stretch) &&
+               op.table_params.size() == static_cast<size_t>(op.n)), "%s: column map size", name);
+    CHECK(op.op != kOpCopyIn || op.columns.size() == static_cast<size_t>((op.B + stretch - 1) / stretch),
           "%s: member map size", name);
     CHECK((op.op != kOpCopyInFlat && op.op != kOpWriteBackFlat) ||
-              op.columns.size() == static_cast<size_t>((op.flat_n * dtype_bytes(op.reduce_dt) + kWindowBytes - 1) /
-                                                       kWindowBytes),
+              op.columns.size() == static_cast<size_t>((op.flat_n * dtype_bytes(op.reduce_dt) + stretch - 1) / stretch),
           "%s: flat map size", name);
     CHECK((op.op != kOpCopyOut && op.op != kOpWriteBack) ||
               op.columns.size() == static_cast<size_t>((op.n_windows + (1 << kGroupLog2) - 1) >> kGroupLog2),
@@ -122,6 +127,24 @@ static bool check_op(const char *name, const OpTable &op, int32_t W, int32_t shi
             ++ranges;
         });
         if (!ok) return false;
+        if (op.op == kOpPack) {
+            // the kernel's direct copy of a whole single-member window must
+            // be exactly the one range the general walk gives for it
+            DirectWindow d{};
+            if (pack_direct(a, w, d)) {
+                int n_rng = 0;
+                bool same = false;
+                for_each_range(a, w, [&](const RangeRef &g) {
+                    ++n_rng;
+                    const int64_t ssz = dtype_bytes(g.src_dt), dsz = dtype_bytes(g.dst_dt);
+                    same = g.hi - g.lo == kWindowBytes / dsz && g.valid >= g.hi && g.src_dt == d.src_dt &&
+                           static_cast<int64_t>(d.src) == g.src_off + g.lo * ssz &&
+                           d.dst_off == g.dst_off + g.lo * dsz && (a.shift + d.dst_off) % 16 == 0;
+                });
+                CHECK(n_rng == 1 && same, "%s: window %d (shift %d): direct copy differs from its range", name, w, shift);
+                ++g_direct;
+            }
+        }
         int64_t row0 = shift, row1 = shift + op.B;        // the window's row, from the aligned origin
         if (op.op == kOpPack) {
             // window k of row r is empty exactly when the row ends before it
@@ -262,6 +285,7 @@ int main(int argc, char **argv)
     }
     std::printf("OK %s%zu buckets, windows:", flat ? "flat, " : "", plan.buckets.size());
     for (const BucketPlan &b : plan.buckets) std::printf(" %d (rows/group %d)", b.pack.n_windows, 1 << b.pack.group_lg);
-    std::printf(" copy_in %d copy_out %d\n", plan.copy_in.n_windows, plan.copy_out.n_windows);
+    std::printf(" copy_in %d copy_out %d; direct pack windows %lld\n", plan.copy_in.n_windows,
+                plan.copy_out.n_windows, static_cast<long long>(g_direct));
     return 0;
 }
