@@ -213,16 +213,13 @@ int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdp
         op.dst_bytes = W * b.S * dsz;
         op.n_windows = static_cast<int32_t>(op.windows(0));
         // Row order: rows in pairs (window k of rows 2i and 2i+1, then window
-        // k + 1) when W is even and the rank chunks average at most 512 KiB
-        // of source, one row at a time otherwise.  Measured on MI355X over
-        // groups of 1, 2, 4 and 8 rows: pairs gained 2-4 % on layouts of
-        // ~100-400 KB chunks (445 tensors, or 32 tensors at W=8) and lost
-        // nothing at W=128; larger groups were slower when the pack follows
-        // another kernel, and any grouping slowed multi-MB chunks (up to 8 %
-        // at 8 rows).
-        if (!mem.empty() && W % 2 == 0 &&
-            static_cast<double>(op.src_bytes) <= 524288.0 * static_cast<double>(mem.size()) * W)
-            op.group_lg = 1;
+        // k + 1) when W is even, one row at a time otherwise.  Measured on
+        // MI355X over groups of 1, 2 and 4 rows: pairs gained 2-4 % on
+        // layouts of ~100-400 KB chunks (445 tensors, or 32 tensors at W=8)
+        // and 2.5 % on multi-MB chunks (12 tensors of a 218M-element block),
+        // and lost nothing at W=128; groups of 4 were no better than pairs
+        // and slower at W=128.
+        if (!mem.empty() && W % 2 == 0) op.group_lg = 1;
 
         // reduce-scatter write-back: each member's rank chunk (P elements in
         // its storage dtype) cut into windows from its first byte; a launch
