@@ -286,8 +286,9 @@ FSDPPACK_HD inline void pack_window(const WindowArgs &a, int32_t w, F &&f)
 // A pack window that is one whole window of a single member's rank chunk,
 // every element real: the common case, which the kernel moves with a short
 // direct copy instead of the general range walk.  `src` is the address of
-// the window's first source element, `dst_off` the byte offset of its first
-// destination element in the packed buffer.
+// the window's first source element (dword aligned, or 2 bytes past a dword
+// for a bf16 source), `dst_off` the byte offset of its first destination
+// element in the packed buffer (16-byte aligned in memory).
 struct DirectWindow {
     uint64_t src;
     int64_t dst_off;
@@ -295,11 +296,12 @@ struct DirectWindow {
 };
 
 // Whether pack window w is such a window (its stretches of the column map
-// name only the one member, whose chunk holds the whole window with no
-// padding, and both ends are aligned for whole 16-byte destination vectors
-// and dword source loads); fills `d` when it is.  The window then equals the
-// single range pack_window produces for it, with lo = c0 - O, hi = c1 - O
-// and every element below `valid`.
+// name one or two members, one of whose chunks holds the whole window with
+// no padding, and both ends are aligned for whole 16-byte destination
+// vectors and dword source loads); fills `d` when it is.  Both candidate
+// records and pointers are read in the same round trip.  The window then
+// equals the single range pack_window produces for it, with lo = c0 - O,
+// hi = c1 - O and every element below `valid`.
 FSDPPACK_HD inline bool pack_direct(const WindowArgs &a, int32_t w, DirectWindow &d)
 {
     const FSDPPACK_TABLE ColumnWindow *C = (const FSDPPACK_TABLE ColumnWindow *)a.columns;
@@ -314,14 +316,21 @@ FSDPPACK_HD inline bool pack_direct(const WindowArgs &a, int32_t w, DirectWindow
     const int64_t c0 = y0 >> lg, c1 = y1 >> lg;
     const ColumnWindow e0 = C[static_cast<int32_t>(c0 >> (a.map_lg - lg))];
     const ColumnWindow e1 = C[static_cast<int32_t>((c1 - 1) >> (a.map_lg - lg))];
-    if (e0.count != 1 || e1.count != 1 || e1.first != e0.first) return false;
-    const uint64_t ptr = table_entry(a, e0.first);
-    const PackMember pm = read_record<PackMember>(a.members, e0.first);
+    const int32_t m0 = e0.first, n = e1.first + e1.count - m0;   // candidates m0, m0 + 1
+    if (n < 1 || n > 2) return false;
+    const int32_t m1 = m0 + n - 1;
+    const uint64_t ptr0 = table_entry(a, m0), ptr1 = table_entry(a, m1);
+    const PackMember pm0 = read_record<PackMember>(a.members, m0);
+    const PackMember pm1 = read_record<PackMember>(a.members, m1);
+    const bool second = c0 >= pm1.O;                     // members tile the columns in order
+    const PackMember pm = second ? pm1 : pm0;
+    const uint64_t ptr = second ? ptr1 : ptr0;
     if (c0 < pm.O || c1 > pm.O + pm.P || r * pm.P + (c1 - pm.O) > pm.numel) return false;
     d.src = ptr + static_cast<uint64_t>((r * pm.P + (c0 - pm.O)) * dtype_bytes(pm.src_dt));
     d.dst_off = (r * a.S + c0) << lg;
     d.src_dt = pm.src_dt;
-    return (d.src & 3u) == 0 && ((a.shift + d.dst_off) & 15) == 0;
+    // a bf16 source may start 2 bytes past a dword (the kernel then shifts)
+    return (d.src & (pm.src_dt == kBF16 ? 1u : 3u)) == 0 && ((a.shift + d.dst_off) & 15) == 0;
 }
 
 // Copy-in window w: bytes [y0, y1) of the row, which lie in one or two

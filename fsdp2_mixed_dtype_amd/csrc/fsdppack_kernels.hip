@@ -374,7 +374,8 @@ __device__ __forceinline__ void run_range(const RangeRef &g, char *base, float d
 }
 
 // A whole window of one member's chunk (pack_direct): each lane loads its
-// kUnroll source vectors, converts them and stores them; no range walk.
+// kUnroll source vectors, converts them and stores them; no range walk.  A
+// bf16 source 2 bytes past a dword boundary loads through the shifted path.
 template <int S, int D>
 __device__ __forceinline__ void copy_window_direct(const char *src, char *dst)
 {
@@ -383,8 +384,13 @@ __device__ __forceinline__ void copy_window_direct(const char *src, char *dst)
     const VecOut out(dst, kBlock * kUnroll);
     const int tid = threadIdx.x;
     uint32_t w[kUnroll][P::NSRC];
+    if (S != kBF16 || (reinterpret_cast<uintptr_t>(src) & 3u) == 0) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) load_dwords<P::NSRC, false>(src + (tid + u * kBlock) * SV, w[u]);
+        for (int u = 0; u < kUnroll; ++u) load_dwords<P::NSRC, false>(src + (tid + u * kBlock) * SV, w[u]);
+    } else {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) load_half_shifted<P::NSRC, false>(src - 2 + (tid + u * kBlock) * SV, w[u]);
+    }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) out.put(tid + u * kBlock, convert_vec<S, D>(w[u]));
 }
