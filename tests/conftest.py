@@ -24,3 +24,17 @@ def golden(name):
             key, *vals = line.split()
             rows[key] = vals
     return rows
+
+
+def direct_window_layout():
+    """A W=4 layout whose pack windows mostly lie inside one rank chunk (the
+    kernel's direct copy): bf16 and fp32 gradients into both reduction
+    dtypes, bf16 rank chunks that start at odd elements (2 bytes past a
+    dword), and small tensors between large ones (two members in one map
+    stretch).  Returns (shapes, grad dtypes, reduce dtypes, W)."""
+    BF16, FP32 = 1, 2
+    shapes = [(4 * 3001, 1), (8, 5), (4 * 1537, 3), (3,), (4 * 4096, 2), (4 * 2049, 1), (5, 7), (4 * 1025, 8),
+              (4 * 777, 11)]
+    gdt = [BF16, BF16, FP32, FP32, BF16, FP32, BF16, BF16, BF16]
+    rdt = [FP32, FP32, FP32, BF16, BF16, BF16, 0, FP32, BF16]
+    return shapes, gdt, rdt, 4

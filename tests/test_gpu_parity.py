@@ -119,6 +119,20 @@ def test_pack_special_values_heterogeneous():
     check_pack(w, grads)
 
 
+def test_pack_direct_windows_every_dtype_pair_and_shift():
+    """Windows inside one rank chunk take the kernel's direct copy: all four
+    dtype pairs, bf16 chunks at odd elements, two members per map stretch,
+    sources shifted by an element and outputs off a 16-byte boundary."""
+    from conftest import direct_window_layout
+    shapes, gdt, rdt, W = direct_window_layout()
+    w = wl.custom(shapes, gdt, rdt, W, seed=11)
+    grads = wl.make_grads(w)
+    wl.inject_specials(grads, gdt, seed=11)
+    for src_shift, out_off in ((0, 0), (1, 0), (0, 6), (1, 2)):
+        print(f"[pack direct] src_shift={src_shift} out_off={out_off}", flush=True)
+        check_pack(w, grads, [src_shift] * len(grads), out_off)
+
+
 def _random_workload(rng, seed):
     W = rng.choice([1, 2, 3, 4, 5, 8, 16, 33, 128])
     n = rng.randint(1, 9)

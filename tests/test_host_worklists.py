@@ -59,6 +59,19 @@ def test_worklists_in_bounds_workloads(checker, name):
     _run(checker, w.descs(), w.world)
 
 
+def test_direct_windows_are_exercised(checker):
+    """The direct-copy layout of the GPU tests really produces direct pack
+    windows (and the checker finds each equal to its general range)."""
+    from conftest import direct_window_layout
+    shapes, gdt, rdt, W = direct_window_layout()
+    w = wl.custom(shapes, gdt, rdt, W)
+    text = f"{W} {len(w.descs())}\n" + "".join(" ".join(str(int(x)) for x in d) + "\n" for d in w.descs())
+    res = subprocess.run([checker], input=text, capture_output=True, text=True, timeout=600)
+    assert res.returncode == 0 and res.stdout.startswith("OK"), res.stdout + res.stderr[-3000:]
+    direct = int(res.stdout.rsplit("direct pack windows", 1)[1].split()[0])
+    assert direct > 100, res.stdout
+
+
 def test_worklists_in_bounds_random(checker):
     rng = random.Random(1234)
     for _ in range(150):
