@@ -51,9 +51,11 @@ constexpr int64_t kMaxBytes = INT64_MAX / 4;
 // stretch is the coarsest power of two bytes, from one window up, that gives
 // at most kMapEntries entries, made finer (down to one window) while its
 // stretches list too many records on average (a window walks every record
-// of its stretches, skipping those it does not overlap).  A map with one
-// entry per 2 KiB window measured ~5 % slower on MI355X for a 25 MB row,
-// whose ~100 KB map keeps missing those caches under streaming traffic.
+// of its stretches, skipping those it does not overlap).  On MI355X a plain
+// cast kernel that reads one entry of a ~100 KB table per workgroup (the
+// size of a one-entry-per-window map for a 25 MB row) ran up to 8 % slower
+// than with a table of a few KB when its waves move one vector per lane;
+// with the pack's two vectors per lane the difference was within noise.
 constexpr int64_t kMapEntries = 1024;
 constexpr double kMapMeanRecords = 2.0;
 constexpr int64_t kMapMaxRecords = 32;
