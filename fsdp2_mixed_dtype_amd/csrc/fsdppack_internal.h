@@ -293,6 +293,7 @@ struct DirectWindow {
     uint64_t src;
     int64_t dst_off;
     int32_t src_dt;
+    int32_t dst_dt;
 };
 
 // Whether pack window w is such a window (its stretches of the column map
@@ -329,6 +330,7 @@ FSDPPACK_HD inline bool pack_direct(const WindowArgs &a, int32_t w, DirectWindow
     d.src = ptr + static_cast<uint64_t>((r * pm.P + (c0 - pm.O)) * dtype_bytes(pm.src_dt));
     d.dst_off = (r * a.S + c0) << lg;
     d.src_dt = pm.src_dt;
+    d.dst_dt = a.reduce_dt;
     // a bf16 source may start 2 bytes past a dword (the kernel then shifts)
     return (d.src & (pm.src_dt == kBF16 ? 1u : 3u)) == 0 && ((a.shift + d.dst_off) & 15) == 0;
 }
@@ -363,6 +365,34 @@ FSDPPACK_HD inline void copy_in_window(const WindowArgs &a, int32_t w, F &&f)
         g.table_side = kTableIsSource;
         f(g);
     }
+}
+
+// The copy-in counterpart of pack_direct: window w is one whole window of a
+// single parameter's segment [A, A_next) that lies inside its shard's P
+// elements (no zero gap), the destination on 16-byte vectors in memory and
+// the source on dwords (or 2 bytes past one for bf16).  With one or two
+// candidate records in its map stretches, both are read in one round trip;
+// the pointer table is indexed by parameter, so the pointer follows.  The
+// window then equals the single range copy_in_window produces for it.
+FSDPPACK_HD inline bool copy_in_direct(const WindowArgs &a, int32_t w, DirectWindow &d)
+{
+    const FSDPPACK_TABLE ColumnWindow *C = (const FSDPPACK_TABLE ColumnWindow *)a.columns;
+    int64_t y0, y1;
+    window_span(w, a.shift, a.B, y0, y1);
+    if (y1 - y0 != kWindowBytes) return false;
+    const ColumnWindow e0 = C[y0 >> a.map_lg], e1 = C[(y1 - 1) >> a.map_lg];
+    const int32_t m0 = e0.first, n = e1.first + e1.count - m0;
+    if (n < 1 || n > 2) return false;
+    const CopyInMember c0 = read_record<CopyInMember>(a.members, m0);
+    const CopyInMember c1 = read_record<CopyInMember>(a.members, m0 + n - 1);
+    const CopyInMember cm = y0 >= c1.A ? c1 : c0;        // members tile the row in order
+    const int64_t esz = dtype_bytes(cm.dst_dt);
+    if (y0 < cm.A || y1 > cm.A_next || (y1 - cm.A) / esz > cm.P) return false;
+    d.src = table_entry(a, cm.slot) + static_cast<uint64_t>((y0 - cm.A) / esz * dtype_bytes(cm.src_dt));
+    d.dst_off = y0;
+    d.src_dt = cm.src_dt;
+    d.dst_dt = cm.dst_dt;
+    return (d.src & (cm.src_dt == kBF16 ? 1u : 3u)) == 0 && ((a.shift + y0) & 15) == 0;
 }
 
 // The tensor record whose windows contain window w: a binary search on win0

@@ -16,8 +16,9 @@
 // design aims at HBM bandwidth, not at the matrix cores:
 //  * each workgroup (one wave64) owns one 2 KiB window, finds the ranges it
 //    overlaps from its index and the plan's small tables, and walks them; a
-//    pack window inside a single member's chunk with no padding (nearly all
-//    of them in large layouts) skips the walk and copies directly;
+//    pack or copy-in window inside a single member's chunk with no padding
+//    (nearly all of them in large layouts) skips the walk and copies
+//    directly;
 //  * every whole 16-byte destination vector is written by one 16-byte vector
 //    store (element stores only at a range's unaligned head and tail),
 //    64-lane wavefronts covering 1 KiB per store instruction;
@@ -383,7 +384,9 @@ __device__ __forceinline__ void run_range(const RangeRef &g, char *base, float d
 // with the neighbouring windows and plain loads let the cache serve the
 // second read (non-temporal loads there cost 8 % on rows that start off a
 // line).
-template <int S, int D>
+// COPY: a source read exactly once whatever its alignment (the all-gather
+// copy-in), loaded non-temporally everywhere.
+template <int S, int D, bool COPY>
 __device__ __forceinline__ void copy_window_direct(const char *src, char *dst)
 {
     using P = Path<S, D>;
@@ -391,9 +394,15 @@ __device__ __forceinline__ void copy_window_direct(const char *src, char *dst)
     const VecOut out(dst, kBlock * kUnroll);
     const int tid = threadIdx.x;
     uint32_t w[kUnroll][P::NSRC];
-    if ((reinterpret_cast<uintptr_t>(src) & (kLineBytes - 1)) == 0) {
+    if (COPY || (reinterpret_cast<uintptr_t>(src) & (kLineBytes - 1)) == 0) {
+        if (S != kBF16 || (reinterpret_cast<uintptr_t>(src) & 3u) == 0) {
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) load_dwords<P::NSRC, true>(src + (tid + u * kBlock) * SV, w[u]);
+            for (int u = 0; u < kUnroll; ++u) load_dwords<P::NSRC, true>(src + (tid + u * kBlock) * SV, w[u]);
+        } else {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+                load_half_shifted<P::NSRC, true>(src - 2 + (tid + u * kBlock) * SV, w[u]);
+        }
     } else if (S != kBF16 || (reinterpret_cast<uintptr_t>(src) & 3u) == 0) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) load_dwords<P::NSRC, false>(src + (tid + u * kBlock) * SV, w[u]);
@@ -405,15 +414,16 @@ __device__ __forceinline__ void copy_window_direct(const char *src, char *dst)
     for (int u = 0; u < kUnroll; ++u) out.put(tid + u * kBlock, convert_vec<S, D>(w[u]));
 }
 
-__device__ __forceinline__ void run_direct(const DirectWindow &d, int32_t dst_dt, char *base)
+template <bool COPY>
+__device__ __forceinline__ void run_direct(const DirectWindow &d, char *base)
 {
     const char *src = reinterpret_cast<const char *>(d.src);
     char *dst = base + d.dst_off;
-    switch (d.src_dt * 4 + dst_dt) {
-    case kBF16 * 4 + kFP32: copy_window_direct<kBF16, kFP32>(src, dst); break;
-    case kFP32 * 4 + kFP32: copy_window_direct<kFP32, kFP32>(src, dst); break;
-    case kFP32 * 4 + kBF16: copy_window_direct<kFP32, kBF16>(src, dst); break;
-    case kBF16 * 4 + kBF16: copy_window_direct<kBF16, kBF16>(src, dst); break;
+    switch (d.src_dt * 4 + d.dst_dt) {
+    case kBF16 * 4 + kFP32: copy_window_direct<kBF16, kFP32, COPY>(src, dst); break;
+    case kFP32 * 4 + kFP32: copy_window_direct<kFP32, kFP32, COPY>(src, dst); break;
+    case kFP32 * 4 + kBF16: copy_window_direct<kFP32, kBF16, COPY>(src, dst); break;
+    case kBF16 * 4 + kBF16: copy_window_direct<kBF16, kBF16, COPY>(src, dst); break;
     default: break;
     }
 }
@@ -427,13 +437,17 @@ __global__ void __launch_bounds__(kBlock) window_kernel(WindowArgs a)
     auto body = [&](const RangeRef &g) { run_range<OP != kOpPack, false>(g, a.base, 1.0f); };
     if constexpr (OP == kOpPack) {
         DirectWindow d;
-        if (pack_direct(a, w, d)) run_direct(d, a.reduce_dt, a.base);
+        if (pack_direct(a, w, d)) run_direct<false>(d, a.base);
         else pack_window(a, w, body);
-    }
-    else if constexpr (OP == kOpCopyIn) copy_in_window(a, w, body);
-    else if constexpr (OP == kOpCopyOut) copy_out_window(a, w, body);
-    else if constexpr (OP == kOpCopyInFlat) flat_window<true>(a, w, body);
-    else if constexpr (OP == kOpWriteBackFlat) {
+    } else if constexpr (OP == kOpCopyIn) {
+        DirectWindow d;
+        if (copy_in_direct(a, w, d)) run_direct<true>(d, a.base);
+        else copy_in_window(a, w, body);
+    } else if constexpr (OP == kOpCopyOut) {
+        copy_out_window(a, w, body);
+    } else if constexpr (OP == kOpCopyInFlat) {
+        flat_window<true>(a, w, body);
+    } else if constexpr (OP == kOpWriteBackFlat) {
         if (a.divisor != 1.0f)     // uniform across the launch
             flat_window<false>(a, w, [&](const RangeRef &g) { run_range<true, true>(g, a.base, a.divisor); });
         else

@@ -36,7 +36,8 @@
 using namespace fsdppack;
 
 static std::string g_fail;
-static int64_t g_direct = 0;   // pack windows taking the direct copy
+static int64_t g_direct = 0;      // pack windows taking the direct copy
+static int64_t g_direct_in = 0;   // copy-in windows taking it
 
 #define CHECK(cond, ...)                                                  \
     do {                                                                  \
@@ -138,11 +139,29 @@ static bool check_op(const char *name, const OpTable &op, int32_t W, int32_t shi
                     ++n_rng;
                     const int64_t ssz = dtype_bytes(g.src_dt), dsz = dtype_bytes(g.dst_dt);
                     same = g.hi - g.lo == kWindowBytes / dsz && g.valid >= g.hi && g.src_dt == d.src_dt &&
-                           static_cast<int64_t>(d.src) == g.src_off + g.lo * ssz &&
+                           g.dst_dt == d.dst_dt && static_cast<int64_t>(d.src) == g.src_off + g.lo * ssz &&
                            d.dst_off == g.dst_off + g.lo * dsz && (a.shift + d.dst_off) % 16 == 0;
                 });
                 CHECK(n_rng == 1 && same, "%s: window %d (shift %d): direct copy differs from its range", name, w, shift);
                 ++g_direct;
+            }
+        }
+        if (op.op == kOpCopyIn) {
+            // likewise the copy-in's direct copy of a whole window of one segment
+            DirectWindow d{};
+            if (copy_in_direct(a, w, d)) {
+                int n_rng = 0;
+                bool same = false;
+                for_each_range(a, w, [&](const RangeRef &g) {
+                    ++n_rng;
+                    const int64_t ssz = dtype_bytes(g.src_dt), dsz = dtype_bytes(g.dst_dt);
+                    same = g.hi - g.lo == kWindowBytes / dsz && g.valid >= g.hi && g.src_dt == d.src_dt &&
+                           g.dst_dt == d.dst_dt && static_cast<int64_t>(d.src) == g.src_off + g.lo * ssz &&
+                           d.dst_off == g.dst_off + g.lo * dsz && (a.shift + d.dst_off) % 16 == 0;
+                });
+                CHECK(n_rng == 1 && same, "%s: window %d (shift %d): direct copy-in differs from its range", name, w,
+                      shift);
+                ++g_direct_in;
             }
         }
         int64_t row0 = shift, row1 = shift + op.B;        // the window's row, from the aligned origin
@@ -285,7 +304,8 @@ int main(int argc, char **argv)
     }
     std::printf("OK %s%zu buckets, windows:", flat ? "flat, " : "", plan.buckets.size());
     for (const BucketPlan &b : plan.buckets) std::printf(" %d (rows/group %d)", b.pack.n_windows, 1 << b.pack.group_lg);
-    std::printf(" copy_in %d copy_out %d; direct pack windows %lld\n", plan.copy_in.n_windows,
-                plan.copy_out.n_windows, static_cast<long long>(g_direct));
+    std::printf(" copy_in %d copy_out %d; direct pack windows %lld, direct copy-in windows %lld\n",
+                plan.copy_in.n_windows, plan.copy_out.n_windows, static_cast<long long>(g_direct),
+                static_cast<long long>(g_direct_in));
     return 0;
 }
