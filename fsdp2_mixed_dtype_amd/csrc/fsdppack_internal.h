@@ -409,18 +409,47 @@ FSDPPACK_HD inline CopyOutTensor find_tensor(const WindowArgs &a, int32_t w)
     return T[lo];
 }
 
-// Copy-out window w: bytes [x*kWindowBytes, ...) of the tensor owning w
-// (windows start at each tensor's own first byte; `shift` is unused), split
-// at rank-chunk boundaries; chunk r comes from byte r*B + A of the gathered
-// buffer.
-template <typename F>
-FSDPPACK_HD inline void copy_out_window(const WindowArgs &a, int32_t w, F &&f)
+// Elements [e0, e1) of tensor t that copy-out window w covers: bytes
+// [x*kWindowBytes, ...) of the tensor (windows start at each tensor's own
+// first byte; `shift` is unused).
+FSDPPACK_HD inline void copy_out_span(const CopyOutTensor &t, int32_t w, int64_t &e0, int64_t &e1)
 {
-    const CopyOutTensor t = find_tensor(a, w);
+    const int64_t per = kWindowBytes / dtype_bytes(t.dt);
+    e0 = (w - t.win0) * per;
+    e1 = imin(t.numel, e0 + per);
+}
+
+// Byte offset in the gathered buffer of element i of tensor t: element
+// i - r*P of rank r's chunk, r = i / P, which sits at byte r*B + A.  For
+// tensors of fewer than 2^32 elements (P <= numel), in 32-bit division.
+FSDPPACK_HD inline int64_t copy_out_source(const WindowArgs &a, const CopyOutTensor &t, uint32_t i)
+{
+    const uint32_t P = static_cast<uint32_t>(t.P), r = i / P;
+    return static_cast<int64_t>(r) * a.B + t.A + static_cast<int64_t>(i - r * P) * dtype_bytes(t.dt);
+}
+
+// Rank chunks above which a copy-out window is gathered element by element
+// in one pass (copy_out_source per element) instead of walked chunk by
+// chunk.  A parameter with fewer rows than ranks has chunks of a few
+// elements, and a window over them meets dozens; walking them costs a full
+// round trip of loads and stores per chunk, since a wave's wait for its
+// loads also waits for its earlier stores.
+constexpr int64_t kGatherChunks = 2;
+
+FSDPPACK_HD inline bool copy_out_gathered(const CopyOutTensor &t, int64_t e0, int64_t e1)
+{
+    return (t.numel >> 32) == 0 && udiv(e1 - 1, t.P) - udiv(e0, t.P) >= kGatherChunks;
+}
+
+// Copy-out window w of tensor t, split at rank-chunk boundaries; chunk r
+// comes from byte r*B + A of the gathered buffer.
+template <typename F>
+FSDPPACK_HD inline void copy_out_chunks(const WindowArgs &a, const CopyOutTensor &t, int32_t w, F &&f)
+{
     const uint64_t ptr = table_entry(a, t.slot);
     const int64_t esz = dtype_bytes(t.dt);
-    const int64_t e0 = (w - t.win0) * (kWindowBytes / esz);
-    const int64_t e1 = imin(t.numel, e0 + kWindowBytes / esz);
+    int64_t e0, e1;
+    copy_out_span(t, w, e0, e1);
     for (int64_t r = udiv(e0, t.P); r * t.P < e1; ++r) {
         const int64_t b0 = imax(e0, r * t.P), b1 = imin(e1, (r + 1) * t.P);
         RangeRef g;
@@ -437,6 +466,13 @@ FSDPPACK_HD inline void copy_out_window(const WindowArgs &a, int32_t w, F &&f)
         g.table_side = kTableIsDest;
         f(g);
     }
+}
+
+// Copy-out window w: the chunks of the tensor owning it.
+template <typename F>
+FSDPPACK_HD inline void copy_out_window(const WindowArgs &a, int32_t w, F &&f)
+{
+    copy_out_chunks(a, find_tensor(a, w), w, f);
 }
 
 // Reduce-scatter write-back window w: bytes [x*kWindowBytes, ...) of the

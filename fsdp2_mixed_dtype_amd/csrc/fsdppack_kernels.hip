@@ -358,7 +358,9 @@ __device__ void copy_range(const char *__restrict__ src, char *__restrict__ dst,
 // and the write-back (sources read once).  On MI355X non-temporal loads sped
 // the copies up by 2-6 %, but moved the pack by -3 % to +5 % depending on the
 // layout.  DIV: divide every element by d before the cast (write-back only).
-template <bool NT, bool DIV>
+// SAME: the range never casts (the copy-out moves a parameter's own dtype),
+// so only the two plain copies are compiled in.
+template <bool NT, bool DIV, bool SAME = false>
 __device__ __forceinline__ void run_range(const RangeRef &g, char *base, float d)
 {
     char *tp = reinterpret_cast<char *>(g.ptr);
@@ -366,6 +368,11 @@ __device__ __forceinline__ void run_range(const RangeRef &g, char *base, float d
     char *dst;
     if (g.table_side == kTableIsSource) { src = tp + g.src_off; dst = base + g.dst_off; }
     else { src = base + g.src_off; dst = tp + g.dst_off; }
+    if constexpr (SAME) {
+        if (g.dst_dt == kBF16) copy_range<kBF16, kBF16, NT, DIV>(src, dst, g.lo, g.hi, g.valid, d);
+        else copy_range<kFP32, kFP32, NT, DIV>(src, dst, g.lo, g.hi, g.valid, d);
+        return;
+    }
     switch (g.src_dt * 4 + g.dst_dt) {
     case kBF16 * 4 + kFP32: copy_range<kBF16, kFP32, NT, DIV>(src, dst, g.lo, g.hi, g.valid, d); break;
     case kFP32 * 4 + kFP32: copy_range<kFP32, kFP32, NT, DIV>(src, dst, g.lo, g.hi, g.valid, d); break;
@@ -428,6 +435,30 @@ __device__ __forceinline__ void run_direct(const DirectWindow &d, char *base)
     }
 }
 
+// A copy-out window over many small rank chunks (copy_out_gathered): each
+// lane fetches its elements one by one from wherever their chunks sit in the
+// gathered buffer, so the whole window is one round of loads and one of
+// stores.  Copy-out moves bits (same dtype on both sides); lanes take
+// consecutive elements, so each load and store instruction touches one or
+// two short contiguous runs.
+template <typename T>
+__device__ __forceinline__ void copy_out_gather(const WindowArgs &a, const CopyOutTensor &t, int64_t e0, int64_t e1)
+{
+    constexpr int kPerLane = static_cast<int>(kWindowBytes / sizeof(T)) / kBlock;
+    FSDPPACK_GLOBAL T *dst = gout<T>(reinterpret_cast<char *>(table_entry(a, t.slot)));
+    // the tensor has fewer than 2^32 elements (copy_out_gathered); element
+    // i0 + j*kBlock is the lane's j-th, present while j*kBlock < left
+    const uint32_t i0 = static_cast<uint32_t>(e0) + threadIdx.x;
+    const int32_t left = static_cast<int32_t>(e1 - e0) - static_cast<int32_t>(threadIdx.x);
+    T v[kPerLane];
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j)
+        if (j * kBlock < left) v[j] = __builtin_nontemporal_load(gin<T>(a.base + copy_out_source(a, t, i0 + j * kBlock)));
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j)
+        if (j * kBlock < left) dst[i0 + j * kBlock] = v[j];
+}
+
 // One workgroup per window; the window's ranges come from its index and the
 // plan's (cache-resident) record tables.
 template <int OP>
@@ -444,7 +475,13 @@ __global__ void __launch_bounds__(kBlock) window_kernel(WindowArgs a)
         if (copy_in_direct(a, w, d)) run_direct<true>(d, a.base);
         else copy_in_window(a, w, body);
     } else if constexpr (OP == kOpCopyOut) {
-        copy_out_window(a, w, body);
+        const CopyOutTensor t = find_tensor(a, w);
+        int64_t e0, e1;
+        copy_out_span(t, w, e0, e1);
+        if (!copy_out_gathered(t, e0, e1))
+            copy_out_chunks(a, t, w, [&](const RangeRef &g) { run_range<true, false, true>(g, a.base, 1.0f); });
+        else if (t.dt == kBF16) copy_out_gather<uint16_t>(a, t, e0, e1);
+        else copy_out_gather<uint32_t>(a, t, e0, e1);
     } else if constexpr (OP == kOpCopyInFlat) {
         flat_window<true>(a, w, body);
     } else if constexpr (OP == kOpWriteBackFlat) {

@@ -38,3 +38,18 @@ def direct_window_layout():
     gdt = [BF16, BF16, FP32, FP32, BF16, FP32, BF16, BF16, BF16]
     rdt = [FP32, FP32, FP32, BF16, BF16, BF16, 0, FP32, BF16]
     return shapes, gdt, rdt, 4
+
+
+def gathered_copy_out_layout():
+    """Layouts whose copy-out windows span many small rank chunks (the
+    kernel's element-by-element gather): parameters with fewer rows than
+    ranks or a handful of rows per rank, in bf16 and fp32, next to ordinary
+    ones.  Returns a list of (shapes, param dtypes, W)."""
+    BF16, FP32 = 1, 2
+    return [
+        ([(100, 1), (16 * 188 - 5, 1), (40, 3), (17, 7), (3001, 1), (33, 5), (16 * 64, 64), (7,)],
+         [BF16, FP32, BF16, FP32, BF16, FP32, BF16, FP32], 16),
+        ([(5000, 1), (129, 1), (4999, 1), (1, 1), (300, 3), (1000, 64)],
+         [BF16, FP32, FP32, BF16, BF16, FP32], 128),
+        ([(2000, 1), (513, 2), (64, 9)], [FP32, BF16, BF16], 3),
+    ]

@@ -15,6 +15,10 @@
 //    ends with its row, for several offsets of the destination past a line
 //    boundary; only the pack's spare window at the end of a row may have no
 //    range;
+//  * a pack or copy-in window that takes the kernel's direct copy is exactly
+//    the one range the general walk gives for it, and a copy-out window the
+//    kernel gathers element by element reads, for every element, the byte
+//    the chunk walk reads for it;
 //  * the record maps have one entry per 2^map_lg bytes of a row (pack,
 //    copy-in, flat ops; at least a window) or per group of windows
 //    (copy-out, write-back);
@@ -38,6 +42,7 @@ using namespace fsdppack;
 static std::string g_fail;
 static int64_t g_direct = 0;      // pack windows taking the direct copy
 static int64_t g_direct_in = 0;   // copy-in windows taking it
+static int64_t g_gather = 0;      // copy-out windows gathered element by element
 
 #define CHECK(cond, ...)                                                  \
     do {                                                                  \
@@ -162,6 +167,29 @@ static bool check_op(const char *name, const OpTable &op, int32_t W, int32_t shi
                 CHECK(n_rng == 1 && same, "%s: window %d (shift %d): direct copy-in differs from its range", name, w,
                       shift);
                 ++g_direct_in;
+            }
+        }
+        if (op.op == kOpCopyOut) {
+            // a gathered copy-out window reads, for each of its elements, the
+            // very byte the chunk walk reads for it, and covers the same elements
+            const CopyOutTensor t = find_tensor(a, w);
+            int64_t e0, e1;
+            copy_out_span(t, w, e0, e1);
+            if (copy_out_gathered(t, e0, e1)) {
+                int64_t covered = 0;
+                bool same = true;
+                for_each_range(a, w, [&](const RangeRef &g) {
+                    const int64_t esz = dtype_bytes(g.dst_dt);
+                    for (int64_t j = g.lo; j < g.hi && same; ++j) {
+                        const int64_t i = g.dst_off / esz + j;
+                        same = i >= e0 && i < e1 && g.src_dt == t.dt && g.dst_dt == t.dt &&
+                               copy_out_source(a, t, static_cast<uint32_t>(i)) == g.src_off + j * esz;
+                    }
+                    covered += g.hi - g.lo;
+                });
+                CHECK(same && covered == e1 - e0 && (t.numel >> 32) == 0,
+                      "%s: window %d: gathered copy differs from its chunk ranges", name, w);
+                ++g_gather;
             }
         }
         int64_t row0 = shift, row1 = shift + op.B;        // the window's row, from the aligned origin
@@ -304,8 +332,9 @@ int main(int argc, char **argv)
     }
     std::printf("OK %s%zu buckets, windows:", flat ? "flat, " : "", plan.buckets.size());
     for (const BucketPlan &b : plan.buckets) std::printf(" %d (rows/group %d)", b.pack.n_windows, 1 << b.pack.group_lg);
-    std::printf(" copy_in %d copy_out %d; direct pack windows %lld, direct copy-in windows %lld\n",
+    std::printf(" copy_in %d copy_out %d; direct pack windows %lld, direct copy-in windows %lld, "
+                "gathered copy-out windows %lld\n",
                 plan.copy_in.n_windows, plan.copy_out.n_windows, static_cast<long long>(g_direct),
-                static_cast<long long>(g_direct_in));
+                static_cast<long long>(g_direct_in), static_cast<long long>(g_gather));
     return 0;
 }

@@ -373,6 +373,28 @@ def test_copy_out_matches_oracle(name):
     plan.destroy()
 
 
+def test_copy_out_gathered_windows():
+    """Copy-out windows over many small rank chunks (gathered element by
+    element by the kernel), bf16 and fp32, outputs at element offsets 0-2."""
+    from conftest import gathered_copy_out_layout
+    for k, (shapes, pdt, W) in enumerate(gathered_copy_out_layout()):
+        print(f"[copy-out gathered] layout {k} W={W}", flush=True)
+        n = len(shapes)
+        w = wl.custom(shapes, [FP32] * n, [0] * n, W, storage_dtypes=[FP32] * n, param_dtypes=pdt)
+        ref = oracle.plan(w.descs(), W)
+        plan = fp.plan_buckets(w.descs(), W)
+        gathered = np.random.default_rng(k).integers(0, 256, size=W * ref.B, dtype=np.uint8)
+        ag = torch.from_numpy(gathered.copy()).to(DEV)
+        for shift in range(3):
+            outs = [Guarded(t.numel, t.param_dtype, (i + shift) % 3) for i, t in enumerate(w.tensors)]
+            fp.all_gather_copy_out(plan, ag, [o.t for o in outs])
+            torch.cuda.synchronize()
+            wants = oracle.copy_out(ref, gathered)
+            for i, (o, want) in enumerate(zip(outs, wants)):
+                assert np.array_equal(o.result(), want.view(np.uint8)), f"layout {k} shift {shift}: param {i} differs"
+        plan.destroy()
+
+
 @pytest.mark.parametrize("name", ["tiny", "mixed50m", "hetero500"])
 def test_copy_in_all_gather_copy_out_round_trip(name):
     """copy-out(all-gather(copy-in(shards of X))) == cast(X), storage -> param dtype."""

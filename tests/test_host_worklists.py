@@ -72,6 +72,21 @@ def test_direct_windows_are_exercised(checker):
     assert direct > 100, res.stdout
 
 
+def test_gathered_copy_out_windows_are_exercised(checker):
+    """The gathered copy-out layouts of the GPU tests really produce copy-out
+    windows that the kernel gathers element by element (and the checker finds
+    each element read from the byte the chunk walk reads)."""
+    from conftest import gathered_copy_out_layout
+    for shapes, pdt, W in gathered_copy_out_layout():
+        w = wl.custom(shapes, [FP32] * len(shapes), [0] * len(shapes), W, storage_dtypes=[FP32] * len(shapes),
+                      param_dtypes=pdt)
+        text = f"{W} {len(w.descs())}\n" + "".join(" ".join(str(int(x)) for x in d) + "\n" for d in w.descs())
+        res = subprocess.run([checker], input=text, capture_output=True, text=True, timeout=600)
+        assert res.returncode == 0 and res.stdout.startswith("OK"), res.stdout + res.stderr[-3000:]
+        gathered = int(res.stdout.rsplit("gathered copy-out windows", 1)[1].split()[0])
+        assert gathered >= 2, res.stdout
+
+
 def test_worklists_in_bounds_random(checker):
     rng = random.Random(1234)
     for _ in range(150):
