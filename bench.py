@@ -391,9 +391,12 @@ def main():
     try:
         with open(TRAFFIC_SUMMARY) as f:
             summ = json.load(f).get(args.workload)
-        # counter figures only stand while the kernel they were taken on does
-        if summ and summ.get("kernel_source_sha256_16") == kernel_source_hash() and nb == 1:
-            traffic = summ.get("traffic_bytes_per_launch")
+        # counter figures only stand while the kernel they were taken on does;
+        # a layout with several buckets has them per bucket
+        if summ and summ.get("kernel_source_sha256_16") == kernel_source_hash():
+            rec = summ if nb == 1 else summ.get("buckets", {}).get(str(dom))
+            if rec:
+                traffic = rec.get("traffic_bytes_per_launch")
     except (OSError, ValueError):
         pass
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
