@@ -240,6 +240,11 @@ struct VecOut {
     {
         __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, static_cast<int>(q * 16), 0, kStorePolicy);
     }
+    // half vector p (8 bytes) of the span
+    __device__ __forceinline__ void put8(int64_t p, u32x2 v) const
+    {
+        __builtin_amdgcn_raw_buffer_store_b64(v, rsrc, static_cast<int>(p * 8), 0, kStorePolicy);
+    }
 };
 
 // One element: dst[i] = i < valid ? cast(src[i]) : +0.
@@ -393,6 +398,12 @@ __device__ __forceinline__ void run_range(const RangeRef &g, char *base, float d
 // line).
 // COPY: a source read exactly once whatever its alignment (the all-gather
 // copy-in), loaded non-temporally everywhere.
+// fp32 -> bf16 reads 32 source bytes per 16-byte destination vector; rather
+// than two 16-byte loads per lane 32 bytes apart (each wave instruction then
+// touching half of every line it spans), each lane converts four 16-byte
+// source pieces into four 8-byte halves, so every load instruction reads
+// 1 KiB and every store writes 512 B contiguously (on MI355X the copy-in of
+// the 218M-element block 5 % faster; the pack unchanged).
 template <int S, int D, bool COPY>
 __device__ __forceinline__ void copy_window_direct(const char *src, char *dst)
 {
@@ -400,6 +411,24 @@ __device__ __forceinline__ void copy_window_direct(const char *src, char *dst)
     constexpr int64_t SV = P::V * static_cast<int64_t>(sizeof(typename P::ST));
     const VecOut out(dst, kBlock * kUnroll);
     const int tid = threadIdx.x;
+    if constexpr (S == kFP32 && D == kBF16) {
+        uint32_t h[2 * kUnroll][4];
+        if (COPY || (reinterpret_cast<uintptr_t>(src) & (kLineBytes - 1)) == 0) {
+#pragma unroll
+            for (int u = 0; u < 2 * kUnroll; ++u) load_dwords<4, true>(src + (tid + u * kBlock) * 16, h[u]);
+        } else {
+#pragma unroll
+            for (int u = 0; u < 2 * kUnroll; ++u) load_dwords<4, false>(src + (tid + u * kBlock) * 16, h[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < 2 * kUnroll; ++u) {
+            u32x2 r;
+            r.x = f32_to_bf16(h[u][0]) | (f32_to_bf16(h[u][1]) << 16);
+            r.y = f32_to_bf16(h[u][2]) | (f32_to_bf16(h[u][3]) << 16);
+            out.put8(tid + u * kBlock, r);
+        }
+        return;
+    }
     uint32_t w[kUnroll][P::NSRC];
     if (COPY || (reinterpret_cast<uintptr_t>(src) & (kLineBytes - 1)) == 0) {
         if (S != kBF16 || (reinterpret_cast<uintptr_t>(src) & 3u) == 0) {
