@@ -395,6 +395,61 @@ FSDPPACK_HD inline bool copy_in_direct(const WindowArgs &a, int32_t w, DirectWin
     return (d.src & (cm.src_dt == kBF16 ? 1u : 3u)) == 0 && ((a.shift + y0) & 15) == 0;
 }
 
+// Candidate records above which a copy-in window is gathered vector by
+// vector in one pass instead of walked segment by segment (each segment a
+// full round trip of loads and stores).  Segments start on 16-byte
+// boundaries of the row and span whole 16-byte vectors, so when the row
+// itself starts on a 16-byte boundary of memory every destination vector
+// lies in a single segment.
+constexpr int32_t kCopyInGatherRecords = 3;
+
+// Whether copy-in window w is gathered: the row 16-byte aligned in memory
+// and at least kCopyInGatherRecords segments overlapping the window's bytes
+// [y0, y1) (multiples of 16 from the row's start), which are those of
+// records m0 ... m0 + n - 1.
+FSDPPACK_HD inline bool copy_in_gathered(const WindowArgs &a, int32_t w, int64_t &y0, int64_t &y1, int32_t &m0,
+                                         int32_t &n)
+{
+    if ((a.shift & 15) != 0) return false;
+    const FSDPPACK_TABLE ColumnWindow *C = (const FSDPPACK_TABLE ColumnWindow *)a.columns;
+    window_span(w, a.shift, a.B, y0, y1);
+    const int32_t c0 = C[y0 >> a.map_lg].first;
+    const ColumnWindow last = C[(y1 - 1) >> a.map_lg];
+    const int32_t nc = last.first + last.count - c0;
+    if (nc < kCopyInGatherRecords) return false;
+    int32_t k0 = 0, k1 = 0;                  // the records owning bytes y0 and y1 - 1
+    for (int32_t k = 0; k < nc; ++k) {
+        const int64_t A = read_record<CopyInMember>(a.members, c0 + k).A;
+        if (A <= y0) k0 = k;
+        if (A < y1) k1 = k;
+    }
+    m0 = c0 + k0;
+    n = k1 - k0 + 1;
+    return n >= kCopyInGatherRecords;
+}
+
+// The copy-in record owning row byte y among the candidates m0 ... m0+n-1
+// (the last whose segment starts at or before y: members tile the row in
+// order), with its shard's pointer.  Called per lane with a wave-uniform
+// candidate list, so the records are read by scalar loads and each lane
+// keeps its own pick.
+struct CopyInPick {
+    CopyInMember m;
+    uint64_t ptr;
+};
+FSDPPACK_HD inline CopyInPick copy_in_member_at(const WindowArgs &a, int32_t m0, int32_t n, int64_t y)
+{
+    CopyInPick p;
+    p.m = read_record<CopyInMember>(a.members, m0);
+    p.ptr = table_entry(a, p.m.slot);
+    for (int32_t k = 1; k < n; ++k) {
+        const CopyInMember cm = read_record<CopyInMember>(a.members, m0 + k);
+        const uint64_t ptr = table_entry(a, cm.slot);
+        if (y >= cm.A) { p.m = cm; p.ptr = ptr; }
+    }
+    return p;
+}
+
 // The tensor record whose windows contain window w: a binary search on win0
 // among the few records the group map names for w's group (usually one).
 FSDPPACK_HD inline CopyOutTensor find_tensor(const WindowArgs &a, int32_t w)

@@ -464,6 +464,60 @@ __device__ __forceinline__ void run_direct(const DirectWindow &d, char *base)
     }
 }
 
+// A copy-in window over many small segments (copy_in_gathered): each lane
+// takes its destination vectors, finds the segment holding each one among
+// the window's candidate records, and loads that segment's source elements
+// one by one (the dtype pair changes from segment to segment); then it
+// converts and stores the vectors, so the whole window is one round of
+// loads and one of stores.  Elements past a shard's P are the zero gap.
+__device__ __forceinline__ void copy_in_gather(const WindowArgs &a, int64_t y0, int64_t y1, int32_t m0, int32_t n)
+{
+    const VecOut out(a.base + y0, (y1 - y0) >> 4);
+    const int tid = threadIdx.x;
+    uint32_t e[kUnroll][8];
+    int32_t kind[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const int64_t y = y0 + static_cast<int64_t>(tid + u * kBlock) * 16;
+        kind[u] = -1;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) e[u][k] = 0;
+        if (y < y1) {
+            const CopyInPick p = copy_in_member_at(a, m0, n, y);
+            const int dlg = p.m.dst_dt == kBF16 ? 1 : 2;              // log2 of the destination element size
+            const int64_t first = (y - p.m.A) >> dlg;
+            const char *src = reinterpret_cast<const char *>(p.ptr);
+            kind[u] = p.m.src_dt * 4 + p.m.dst_dt;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                if (k < (16 >> dlg) && first + k < p.m.P) {
+                    if (p.m.src_dt == kBF16) e[u][k] = __builtin_nontemporal_load(gin<uint16_t>(src) + first + k);
+                    else e[u][k] = __builtin_nontemporal_load(gin<uint32_t>(src) + first + k);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        if (kind[u] < 0) continue;
+        const uint32_t *x = e[u];
+        u32x4 r;
+        if (kind[u] == kBF16 * 4 + kBF16) {
+            r.x = x[0] | (x[1] << 16); r.y = x[2] | (x[3] << 16); r.z = x[4] | (x[5] << 16); r.w = x[6] | (x[7] << 16);
+        } else if (kind[u] == kFP32 * 4 + kBF16) {
+            r.x = f32_to_bf16(x[0]) | (f32_to_bf16(x[1]) << 16);
+            r.y = f32_to_bf16(x[2]) | (f32_to_bf16(x[3]) << 16);
+            r.z = f32_to_bf16(x[4]) | (f32_to_bf16(x[5]) << 16);
+            r.w = f32_to_bf16(x[6]) | (f32_to_bf16(x[7]) << 16);
+        } else if (kind[u] == kBF16 * 4 + kFP32) {
+            r.x = x[0] << 16; r.y = x[1] << 16; r.z = x[2] << 16; r.w = x[3] << 16;
+        } else {
+            r.x = x[0]; r.y = x[1]; r.z = x[2]; r.w = x[3];
+        }
+        out.put(tid + u * kBlock, r);
+    }
+}
+
 // A copy-out window over many small rank chunks (copy_out_gathered): each
 // lane fetches its elements one by one from wherever their chunks sit in the
 // gathered buffer, so the whole window is one round of loads and one of
@@ -501,7 +555,10 @@ __global__ void __launch_bounds__(kBlock) window_kernel(WindowArgs a)
         else pack_window(a, w, body);
     } else if constexpr (OP == kOpCopyIn) {
         DirectWindow d;
+        int64_t y0, y1;
+        int32_t m0, n;
         if (copy_in_direct(a, w, d)) run_direct<true>(d, a.base);
+        else if (copy_in_gathered(a, w, y0, y1, m0, n)) copy_in_gather(a, y0, y1, m0, n);
         else copy_in_window(a, w, body);
     } else if constexpr (OP == kOpCopyOut) {
         const CopyOutTensor t = find_tensor(a, w);

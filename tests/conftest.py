@@ -53,3 +53,15 @@ def gathered_copy_out_layout():
          [BF16, FP32, FP32, BF16, BF16, FP32], 128),
         ([(2000, 1), (513, 2), (64, 9)], [FP32, BF16, BF16], 3),
     ]
+
+
+def gathered_copy_in_layout():
+    """A W=4 layout of 40 small parameters (1-12 rows of 1-9 columns) whose
+    all-gather segments are a few vectors long, so that copy-in windows span
+    many segments (the kernel's vector-by-vector gather); storage -> param
+    dtypes cycle through all four pairs.  Returns (shapes, storage dtypes,
+    param dtypes, W)."""
+    BF16, FP32 = 1, 2
+    pairs = [(BF16, BF16), (FP32, BF16), (BF16, FP32), (FP32, FP32)]
+    shapes = [(1 + (i * 7) % 12, 1 + (i * 5) % 9) for i in range(40)]
+    return shapes, [pairs[i % 4][0] for i in range(40)], [pairs[i % 4][1] for i in range(40)], 4

@@ -18,7 +18,8 @@
 //  * a pack or copy-in window that takes the kernel's direct copy is exactly
 //    the one range the general walk gives for it, and a copy-out window the
 //    kernel gathers element by element reads, for every element, the byte
-//    the chunk walk reads for it;
+//    the chunk walk reads for it, and a copy-in window it gathers vector by
+//    vector takes each vector from the record the walk takes it from;
 //  * the record maps have one entry per 2^map_lg bytes of a row (pack,
 //    copy-in, flat ops; at least a window) or per group of windows
 //    (copy-out, write-back);
@@ -43,6 +44,7 @@ static std::string g_fail;
 static int64_t g_direct = 0;      // pack windows taking the direct copy
 static int64_t g_direct_in = 0;   // copy-in windows taking it
 static int64_t g_gather = 0;      // copy-out windows gathered element by element
+static int64_t g_gather_in = 0;   // copy-in windows gathered vector by vector
 
 #define CHECK(cond, ...)                                                  \
     do {                                                                  \
@@ -167,6 +169,31 @@ static bool check_op(const char *name, const OpTable &op, int32_t W, int32_t shi
                 CHECK(n_rng == 1 && same, "%s: window %d (shift %d): direct copy-in differs from its range", name, w,
                       shift);
                 ++g_direct_in;
+            }
+            // a gathered copy-in window: every 16-byte vector lies inside the
+            // segment of the record picked for it, which is the record whose
+            // range the walk writes those bytes from, with the same dtypes
+            int64_t y0, y1;
+            int32_t m0, ncand;
+            if (!copy_in_direct(a, w, d) && copy_in_gathered(a, w, y0, y1, m0, ncand)) {
+                std::vector<RangeRef> rs;
+                for_each_range(a, w, [&](const RangeRef &g) { rs.push_back(g); });
+                CHECK(y0 % 16 == 0 && y1 % 16 == 0, "%s: window %d (shift %d): gathered window off 16 bytes", name, w,
+                      shift);
+                for (int64_t y = y0; y < y1; y += 16) {
+                    const CopyInPick p = copy_in_member_at(a, m0, ncand, y);
+                    bool found = false;
+                    for (const RangeRef &g : rs) {
+                        const int64_t esz = dtype_bytes(g.dst_dt);
+                        if (g.dst_off + g.lo * esz <= y && y + 16 <= g.dst_off + g.hi * esz)
+                            found = g.slot == p.m.slot && g.src_dt == p.m.src_dt && g.dst_dt == p.m.dst_dt &&
+                                    g.valid == p.m.P && g.dst_off == p.m.A;
+                    }
+                    CHECK(found && p.m.A <= y && y + 16 <= p.m.A_next,
+                          "%s: window %d (shift %d): gathered vector at byte %lld differs from the walk", name, w, shift,
+                          (long long)y);
+                }
+                ++g_gather_in;
             }
         }
         if (op.op == kOpCopyOut) {
@@ -333,8 +360,8 @@ int main(int argc, char **argv)
     std::printf("OK %s%zu buckets, windows:", flat ? "flat, " : "", plan.buckets.size());
     for (const BucketPlan &b : plan.buckets) std::printf(" %d (rows/group %d)", b.pack.n_windows, 1 << b.pack.group_lg);
     std::printf(" copy_in %d copy_out %d; direct pack windows %lld, direct copy-in windows %lld, "
-                "gathered copy-out windows %lld\n",
+                "gathered copy-in windows %lld, gathered copy-out windows %lld\n",
                 plan.copy_in.n_windows, plan.copy_out.n_windows, static_cast<long long>(g_direct),
-                static_cast<long long>(g_direct_in), static_cast<long long>(g_gather));
+                static_cast<long long>(g_direct_in), static_cast<long long>(g_gather_in), static_cast<long long>(g_gather));
     return 0;
 }

@@ -395,6 +395,34 @@ def test_copy_out_gathered_windows():
         plan.destroy()
 
 
+def test_copy_in_gathered_segments_every_dtype_pair():
+    """Copy-in windows over many small segments in all four storage -> param
+    dtype pairs: gathered vector by vector when the all-gather buffer is
+    16-byte aligned, walked segment by segment when it starts 4, 8 or 12 bytes
+    past a 16-byte boundary; shards at element offsets 0-2."""
+    from conftest import gathered_copy_in_layout
+    shapes, sdt, pdt, W = gathered_copy_in_layout()
+    n = len(shapes)
+    w = wl.custom(shapes, [FP32] * n, [0] * n, W, storage_dtypes=sdt, param_dtypes=pdt)
+    ref = oracle.plan(w.descs(), W)
+    plan = fp.plan_buckets(w.descs(), W)
+    for row_off in (0, 4, 8, 12):
+        print(f"[copy-in gathered] all-gather buffer at +{row_off} bytes", flush=True)
+        ag = Guarded(W * plan.B, None, row_off)
+        ag_ref = np.full((W, ref.B), POISON, np.uint8)
+        for r in range(W):
+            shards = _shards_random(w, ref, r)
+            wl.inject_specials(shards, sdt, seed=r)
+            offs = [(i + r) % 3 for i in range(n)]
+            fp.all_gather_copy_in(plan, r, [to_dev(s_, t.storage_dtype, o) for s_, t, o in
+                                            zip(shards, w.tensors, offs)], ag.t)
+            oracle.copy_in(ref, r, shards, ag_ref)
+        torch.cuda.synchronize()
+        got = ag.result().reshape(W, -1)
+        assert np.array_equal(got, ag_ref), f"copy-in rows differ (buffer at +{row_off} bytes)"
+    plan.destroy()
+
+
 @pytest.mark.parametrize("name", ["tiny", "mixed50m", "hetero500"])
 def test_copy_in_all_gather_copy_out_round_trip(name):
     """copy-out(all-gather(copy-in(shards of X))) == cast(X), storage -> param dtype."""
