@@ -423,6 +423,56 @@ def test_copy_in_gathered_segments_every_dtype_pair():
     plan.destroy()
 
 
+def _edge_layouts():
+    """The pack's edge layouts plus a crowded one: tiny parameters with
+    zero-size ones between them, so that gathered copy-in and copy-out
+    windows meet empty segments and empty rank chunks."""
+    return [
+        wl.custom([(0, 4), (0, 1)], [FP32, BF16], [FP32, FP32], 4),
+        wl.custom([(1,)], [BF16], [FP32], 8, param_dtypes=[FP32]),
+        wl.custom([(5, 3)], [FP32], [BF16], 1),
+        wl.custom([(3, 1), (2, 5), (7, 2)], [BF16, FP32, BF16], [FP32, FP32, FP32], 1000),
+        wl.custom([(0, 3), (4, 4), (0, 9)], [FP32, FP32, BF16], [0, 0, 0], 3),
+        wl.custom([(8, 0), (2, 2)], [BF16, BF16], [0, 0], 2),
+        wl.custom([(3, 1), (0, 4), (2, 1), (0, 1), (5, 1), (1, 3), (0, 2), (7, 1), (900, 1), (13, 7)],
+                  [BF16, FP32] * 5, [0] * 10, 4, storage_dtypes=[BF16, FP32, FP32, BF16, FP32] * 2,
+                  param_dtypes=[BF16, BF16, FP32, FP32, BF16] * 2),
+    ]
+
+
+def test_copy_paths_edge_cases():
+    """Copy-in (every rank, or a sample for large W), copy-out and the
+    divided write-back on the edge layouts, against the oracle."""
+    for ci, w in enumerate(_edge_layouts()):
+        print(f"[copy edge] case={ci} W={w.world}", flush=True)
+        W = w.world
+        ref = oracle.plan(w.descs(), W)
+        plan = fp.plan_buckets(w.descs(), W)
+        ranks = range(W) if W <= 8 else [0, 1, W - 1]
+        if ref.B:
+            ag = Guarded(W * plan.B, None)
+            ag_ref = np.full((W, ref.B), POISON, np.uint8)
+            for r in ranks:
+                shards = _shards_random(w, ref, r)
+                fp.all_gather_copy_in(plan, r, [to_dev(s_, t.storage_dtype, (i + r) % 3) if s_.size else None
+                                                for i, (s_, t) in enumerate(zip(shards, w.tensors))], ag.t)
+                oracle.copy_in(ref, r, shards, ag_ref)
+            torch.cuda.synchronize()
+            assert np.array_equal(ag.result().reshape(W, -1), ag_ref), f"case {ci}: copy-in rows differ"
+        gathered = np.random.default_rng(ci).integers(0, 256, size=W * ref.B, dtype=np.uint8)
+        outs = [Guarded(t.numel, t.param_dtype, i % 3) if t.numel else None for i, t in enumerate(w.tensors)]
+        fp.all_gather_copy_out(plan, torch.from_numpy(gathered.copy()).to(DEV), [o.t if o else None for o in outs])
+        torch.cuda.synchronize()
+        for i, (o, want) in enumerate(zip(outs, oracle.copy_out(ref, gathered))):
+            if o is not None:
+                assert np.array_equal(o.result(), want.view(np.uint8)), f"case {ci}: copy-out param {i} differs"
+        for bi, b in enumerate(ref.buckets):
+            for r in sorted({0, W - 1}):
+                row = wl.random_array(b.S, b.dtype, seed=ci * 10 + bi)
+                check_rs_copy_out(w, ref, plan, bi, r, row, float(W))
+        plan.destroy()
+
+
 @pytest.mark.parametrize("name", ["tiny", "mixed50m", "hetero500"])
 def test_copy_in_all_gather_copy_out_round_trip(name):
     """copy-out(all-gather(copy-in(shards of X))) == cast(X), storage -> param dtype."""
