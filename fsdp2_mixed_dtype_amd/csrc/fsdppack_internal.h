@@ -26,9 +26,10 @@
 // scalar cache and L2: no workgroup waits on a cold record of its own before
 // touching data (a per-workgroup record, read cold, measured ~20 % slower on
 // MI355X), and a wave makes two rounds of table reads before its data (a
-// binary search over hundreds of records would make nine).  The mapping functions below are compiled both
-// for the device (the kernels) and for the host (the planner's bounds
-// checker), so the checker runs exactly the code the kernels run.
+// binary search over hundreds of records would make nine).  The mapping
+// functions below are compiled both for the device (the kernels) and for
+// the host (the planner's bounds checker), so the checker runs exactly the
+// code the kernels run.
 #pragma once
 
 #include <cstdint>

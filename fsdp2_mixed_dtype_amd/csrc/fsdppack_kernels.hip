@@ -18,7 +18,9 @@
 //    overlaps from its index and the plan's small tables, and walks them; a
 //    pack or copy-in window inside a single member's chunk with no padding
 //    (nearly all of them in large layouts) skips the walk and copies
-//    directly;
+//    directly, and a copy-in or copy-out window over many small segments or
+//    rank chunks gathers its elements in one pass instead of one round trip
+//    of loads and stores per piece;
 //  * every whole 16-byte destination vector is written by one 16-byte vector
 //    store (element stores only at a range's unaligned head and tail),
 //    64-lane wavefronts covering 1 KiB per store instruction;
