@@ -524,8 +524,9 @@ __device__ __forceinline__ void copy_in_gather(const WindowArgs &a, int64_t y0, 
 // lane fetches its elements one by one from wherever their chunks sit in the
 // gathered buffer, so the whole window is one round of loads and one of
 // stores.  Copy-out moves bits (same dtype on both sides); lanes take
-// consecutive elements, so each load and store instruction touches one or
-// two short contiguous runs.
+// consecutive elements, so every store instruction writes one contiguous
+// run, and a load instruction reads one contiguous run per rank chunk its
+// elements fall in.
 template <typename T>
 __device__ __forceinline__ void copy_out_gather(const WindowArgs &a, const CopyOutTensor &t, int64_t e0, int64_t e1)
 {
