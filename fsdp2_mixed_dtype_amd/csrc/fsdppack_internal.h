@@ -396,9 +396,9 @@ FSDPPACK_HD inline bool copy_in_direct(const WindowArgs &a, int32_t w, DirectWin
     return (d.src & (cm.src_dt == kBF16 ? 1u : 3u)) == 0 && ((a.shift + y0) & 15) == 0;
 }
 
-// Candidate records above which a copy-in window is gathered vector by
-// vector in one pass instead of walked segment by segment (each segment a
-// full round trip of loads and stores).  Segments start on 16-byte
+// Segments a copy-in window must overlap to be gathered vector by vector in
+// one pass instead of walked segment by segment (each segment a full round
+// trip of loads and stores).  Segments start on 16-byte
 // boundaries of the row and span whole 16-byte vectors, so when the row
 // itself starts on a 16-byte boundary of memory every destination vector
 // lies in a single segment.
