@@ -279,7 +279,10 @@ def test_pack_on_side_stream():
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     out = torch.empty(w.world * plan.buckets[0].S, dtype=torch.float32, device=DEV)
+    # the binding launches on the stream torch reports as current
+    assert fp._stream(None) == torch.cuda.current_stream().cuda_stream
     with torch.cuda.stream(s):
+        assert fp._stream(None) == s.cuda_stream
         fp.pack_reduce_scatter_input(plan, 0, g_dev, out)
     fp.pack_reduce_scatter_input(plan, 0, g_dev, out, stream=s)      # same table, explicit stream
     s.synchronize()
