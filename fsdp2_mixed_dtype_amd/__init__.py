@@ -193,7 +193,7 @@ def _ptr(t, dtype: int | None, numel: int | None, what: str):
         return 0
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{what}: expected a torch.Tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:             # (cheaper than building t.device; HIP tensors report is_cuda)
         raise ValueError(f"{what}: tensor must live on the GPU")
     if not t.is_contiguous():
         raise ValueError(f"{what}: tensor must be contiguous")
