@@ -24,7 +24,10 @@ namespace {
 thread_local std::string g_error;
 thread_local void *g_next_start = nullptr;   // events for the next launch on this thread
 thread_local void *g_next_stop = nullptr;
-std::atomic<int64_t> g_counters[4];   // launches, table uploads, table reuses, plan uploads
+// launches, table uploads, table reuses, plan uploads, table evictions,
+// cross-stream waits at an eviction
+constexpr int kCounters = 6;
+std::atomic<int64_t> g_counters[kCounters];
 
 int fail(int code, const std::string &msg)
 {
@@ -94,9 +97,21 @@ int ensure_device(fsdppack_plan *p)
     return FSDPPACK_OK;
 }
 
-// Find or stage the device pointer table for `key` in cache `c`, ordered
-// before work enqueued next on `stream`.  Caller holds plan->mu.
-int acquire_table(PtrCache &c, const std::vector<uint64_t> &key, hipStream_t stream, PtrSlot **out)
+// Find or stage the device table for pointer set `key` in cache `c` (for a
+// narrow pack, the stretch records built from the pointers, then the
+// pointers), ordered before work enqueued next on `stream`.  Caller holds
+// plan->mu.
+//
+// Replacing a cached table needs no device-wide synchronisation:
+//  * the slot's previous upload read its pinned staging buffer, so that one
+//    copy (issued at least kPtrSlots distinct pointer sets ago) must be done
+//    before the buffer is rewritten: a host wait on its event;
+//  * kernels that read the old table on `stream` itself precede the new
+//    upload in stream order, and those on any other stream that used the slot
+//    are waited for on the device (an event recorded on that stream now,
+//    waited on by `stream`).
+int acquire_table(const OpTable &op, PtrCache &c, const std::vector<uint64_t> &key, hipStream_t stream,
+                  PtrSlot **out)
 {
     hipError_t e;
     for (PtrSlot &s : c.slots) {
@@ -122,11 +137,27 @@ int acquire_table(PtrCache &c, const std::vector<uint64_t> &key, hipStream_t str
         victim = &c.slots[0];
         for (PtrSlot &s : c.slots)
             if (s.last_use < victim->last_use) victim = &s;
-        // kernels still reading the evicted table (on any stream) and its
-        // staging upload must be done before either is overwritten
-        if ((e = hipDeviceSynchronize()) != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+        if ((e = hipEventSynchronize(static_cast<hipEvent_t>(victim->ready))) != hipSuccess)
+            return hip_fail(e, "hipEventSynchronize(previous upload)");
+        size_t used = 0;
+        for (void *st : victim->streams) {
+            if (st == stream) continue;
+            if (used == victim->drain.size()) {
+                hipEvent_t ev;
+                if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess)
+                    return hip_fail(e, "hipEventCreate");
+                victim->drain.push_back(ev);
+            }
+            hipEvent_t ev = static_cast<hipEvent_t>(victim->drain[used++]);
+            if ((e = hipEventRecord(ev, static_cast<hipStream_t>(st))) != hipSuccess)
+                return hip_fail(e, "hipEventRecord(other stream)");
+            if ((e = hipStreamWaitEvent(stream, ev, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+            g_counters[5]++;
+        }
+        victim->live = false;
+        g_counters[4]++;
     }
-    const size_t bytes = key.size() * sizeof(uint64_t);
+    const size_t bytes = static_cast<size_t>(op.table_bytes(key.size()));
     if (victim->d_table == nullptr) {
         if ((e = hipMalloc(reinterpret_cast<void **>(&victim->d_table), bytes)) != hipSuccess) return hip_fail(e, "hipMalloc(pointer table)");
         if ((e = hipHostMalloc(reinterpret_cast<void **>(&victim->h_stage), bytes, hipHostMallocDefault)) != hipSuccess) return hip_fail(e, "hipHostMalloc(pointer table)");
@@ -134,7 +165,9 @@ int acquire_table(PtrCache &c, const std::vector<uint64_t> &key, hipStream_t str
         if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) return hip_fail(e, "hipEventCreate");
         victim->ready = ev;
     }
-    std::memcpy(victim->h_stage, key.data(), bytes);
+    const int64_t ns = op.stretch_count();
+    if (ns > 0) build_pack_stretches(op, key.data(), reinterpret_cast<PackStretch *>(victim->h_stage));
+    std::memcpy(victim->h_stage + ns * static_cast<int64_t>(sizeof(PackStretch) / 8), key.data(), key.size() * 8);
     if ((e = hipMemcpyAsync(victim->d_table, victim->h_stage, bytes, hipMemcpyHostToDevice, stream)) != hipSuccess)
         return hip_fail(e, "hipMemcpyAsync(pointer table)");
     if ((e = hipEventRecord(static_cast<hipEvent_t>(victim->ready), stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -151,6 +184,10 @@ int acquire_table(PtrCache &c, const std::vector<uint64_t> &key, hipStream_t str
 int run_op(fsdppack_plan *p, const OpTable &op, size_t cache_index, const std::vector<uint64_t> &key, char *base,
            void *stream, const char *what, int32_t rank = 0, float divisor = 1.0f)
 {
+    // timing events armed for the next launch are taken by this call, also
+    // when it has nothing to launch
+    void *ev0 = g_next_start, *ev1 = g_next_stop;
+    g_next_start = g_next_stop = nullptr;
     // window boundaries follow the cache lines of memory, not the buffer's start
     const int32_t shift = static_cast<int32_t>(reinterpret_cast<uintptr_t>(base) & (kLineBytes - 1));
     if (op.windows(shift) <= 0) return FSDPPACK_OK;
@@ -158,15 +195,15 @@ int run_op(fsdppack_plan *p, const OpTable &op, size_t cache_index, const std::v
     if (int rc = ensure_device(p)) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     PtrSlot *slot = nullptr;
-    if (int rc = acquire_table(p->caches[cache_index], key, s, &slot)) return rc;
+    if (int rc = acquire_table(op, p->caches[cache_index], key, s, &slot)) return rc;
     WindowArgs args = op.args(true, shift);
 
-    args.table = slot->d_table;
+    const int64_t ns = op.stretch_count();
+    args.stretches = ns > 0 ? reinterpret_cast<const PackStretch *>(slot->d_table) : nullptr;
+    args.table = slot->d_table + ns * static_cast<int64_t>(sizeof(PackStretch) / 8);
     args.base = base;
     args.rank = rank;
     args.divisor = divisor;
-    void *ev0 = g_next_start, *ev1 = g_next_stop;
-    g_next_start = g_next_stop = nullptr;
     const int le = launch_windows(args, stream, ev0, ev1);
     if (le != 0) return hip_fail(static_cast<hipError_t>(le), what);
     g_counters[0]++;
@@ -399,6 +436,7 @@ void fsdppack_plan_destroy(fsdppack_plan *plan)
         for (PtrCache &c : plan->caches) {
             for (PtrSlot &s : c.slots) {
                 if (s.ready) (void)hipEventDestroy(static_cast<hipEvent_t>(s.ready));
+                for (void *ev : s.drain) (void)hipEventDestroy(static_cast<hipEvent_t>(ev));
                 if (s.d_table) (void)hipFree(s.d_table);
                 if (s.h_stage) (void)hipHostFree(s.h_stage);
             }
@@ -432,7 +470,7 @@ int fsdppack_time_next_launch(void *start_event, void *stop_event)
 int fsdppack_counters(int64_t *counters, int32_t n)
 {
     if (counters == nullptr || n < 0) return fail(FSDPPACK_EINVAL, "counters: bad arguments");
-    for (int32_t i = 0; i < n && i < 4; ++i) counters[i] = g_counters[i].load();
+    for (int32_t i = 0; i < n && i < kCounters; ++i) counters[i] = g_counters[i].load();
     return FSDPPACK_OK;
 }
 

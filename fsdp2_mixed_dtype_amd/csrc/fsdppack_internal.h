@@ -138,6 +138,33 @@ struct FlatMember {
 };
 static_assert(sizeof(FlatMember) == 32, "shared with the device");
 
+// One candidate member of a pack stretch, with the member's gradient pointer
+// folded in (these records are rebuilt for every pointer set).  Column
+// offsets and counts are 32-bit: stretch records are only built for buckets
+// whose rows hold fewer than 2^31 bytes and whose members' rank chunks
+// hold fewer than 2^32 source bytes (pack_narrow).
+//   source of row r, column c (O <= c < OP):  base + r*Pss + c*size(dt)
+//   row r's real columns: [O, OP) for r < full, [O, OT) for r == full, none after
+struct PackCand {
+    uint64_t base;           // gradient address - O*size(dt), modulo 2^64
+    uint32_t Pss;            // P*size(dt): source bytes between consecutive rank chunks
+    uint32_t O;              // first column
+    uint32_t OP;             // O + P
+    uint32_t full;           // ranks whose chunk is all real: numel / P
+    uint32_t OT;             // O + numel - full*P
+    uint32_t dt;             // source dtype; 0 = no candidate
+};
+static_assert(sizeof(PackCand) == 32, "shared with the device");
+
+// The members a pack window may lie in, for the windows whose last byte falls
+// in one stretch of 2^map_lg bytes of a row: the members overlapping the
+// stretch extended one window to the left (so the window's first byte is
+// covered too), in column order, when there are at most two of them.
+struct PackStretch {
+    PackCand c[2];
+};
+static_assert(sizeof(PackStretch) == 64, "one scalar load");
+
 // Arguments of one launch (every operation).
 struct WindowArgs {
     int32_t op;              // kOpPack, kOpCopyIn, kOpCopyOut, kOpWriteBack, kOpWriteBackFlat, kOpCopyInFlat
@@ -160,6 +187,7 @@ struct WindowArgs {
                              // flat positions (flat ops), or per group of windows (copy-out, write-back)
     const uint64_t *table;   // device pointer table (by record for the pack and flat ops, else by parameter)
     char *base;              // the call's packed buffer or row (destination or source)
+    const PackStretch *stretches;   // pack: one record per map stretch (null: no direct windows)
 };
 
 // One contiguous range for the copy primitive: elements [lo, hi) of a chunk
@@ -238,21 +266,29 @@ FSDPPACK_HD inline void pack_row_window(const WindowArgs &a, int32_t w, int32_t 
     r = (g << a.group_lg) + (within & ((1 << a.group_lg) - 1));
 }
 
-// Pack window w: window k of row r (pack_row_window).  The row's window
-// boundaries sit on line boundaries of memory: window k covers bytes
-// [k*kWindowBytes - s_r, (k+1)*kWindowBytes - s_r) of the row, clipped to it,
-// with s_r how far the row starts past a line boundary (a row's last window
-// is empty when its bytes fit in gx windows).  Its columns [c0, c1) lie in one
-// or two stretches of the column map, whose entries name the members to visit:
-// a wave makes two rounds of table reads (the column entries, then each
-// member record with its pointer) before its data.
+// Row r and window k of the pack window at (x, g) of the launch's 2-D grid:
+// g is the row group, x runs over its windows (window k of each of the
+// group's 2^group_lg rows in turn) -- the same (r, k) as pack_row_window for
+// w = g * (gx + 1) * 2^group_lg + x, without a division.
+FSDPPACK_HD inline void pack_row_window_2d(const WindowArgs &a, uint32_t x, uint32_t g, int32_t &r, int32_t &k)
+{
+    k = static_cast<int32_t>(x >> a.group_lg);
+    r = static_cast<int32_t>((g << a.group_lg) + (x & ((1u << a.group_lg) - 1)));
+}
+
+// Pack window k of row r.  The row's window boundaries sit on line boundaries
+// of memory: window k covers bytes [k*kWindowBytes - s_r, (k+1)*kWindowBytes
+// - s_r) of the row, clipped to it, with s_r how far the row starts past a
+// line boundary (a row's last window is empty when its bytes fit in gx
+// windows).  Its columns [c0, c1) lie in one or two stretches of the column
+// map, whose entries name the members to visit: a wave makes two rounds of
+// table reads (the column entries, then each member record with its pointer)
+// before its data.
 template <typename F>
-FSDPPACK_HD inline void pack_window(const WindowArgs &a, int32_t w, F &&f)
+FSDPPACK_HD inline void pack_window_rk(const WindowArgs &a, int32_t r, int32_t k, F &&f)
 {
     const FSDPPACK_TABLE ColumnWindow *C = (const FSDPPACK_TABLE ColumnWindow *)a.columns;
     const int lg = a.reduce_dt == kBF16 ? 1 : 2;            // log2 of the element size
-    int32_t r, k;
-    pack_row_window(a, w, r, k);
     const int64_t rb = a.S << lg;                         // bytes per row
     const int32_t s_r = static_cast<int32_t>((a.shift + r * rb) & (kLineBytes - 1));
     int64_t y0, y1;
@@ -284,6 +320,15 @@ FSDPPACK_HD inline void pack_window(const WindowArgs &a, int32_t w, F &&f)
     }
 }
 
+// Pack window w (linear index, pack_row_window).
+template <typename F>
+FSDPPACK_HD inline void pack_window(const WindowArgs &a, int32_t w, F &&f)
+{
+    int32_t r, k;
+    pack_row_window(a, w, r, k);
+    pack_window_rk(a, r, k, f);
+}
+
 // A pack window that is one whole window of a single member's rank chunk,
 // every element real: the common case, which the kernel moves with a short
 // direct copy instead of the general range walk.  `src` is the address of
@@ -297,19 +342,17 @@ struct DirectWindow {
     int32_t dst_dt;
 };
 
-// Whether pack window w is such a window (its stretches of the column map
+// Whether window k of row r is such a window (its stretches of the column map
 // name one or two members, one of whose chunks holds the whole window with
 // no padding, and both ends are aligned for whole 16-byte destination
 // vectors and dword source loads); fills `d` when it is.  Both candidate
 // records and pointers are read in the same round trip.  The window then
 // equals the single range pack_window produces for it, with lo = c0 - O,
 // hi = c1 - O and every element below `valid`.
-FSDPPACK_HD inline bool pack_direct(const WindowArgs &a, int32_t w, DirectWindow &d)
+FSDPPACK_HD inline bool pack_direct_rk(const WindowArgs &a, int32_t r, int32_t k, DirectWindow &d)
 {
     const FSDPPACK_TABLE ColumnWindow *C = (const FSDPPACK_TABLE ColumnWindow *)a.columns;
     const int lg = a.reduce_dt == kBF16 ? 1 : 2;
-    int32_t r, k;
-    pack_row_window(a, w, r, k);
     const int64_t rb = a.S << lg;
     const int32_t s_r = static_cast<int32_t>((a.shift + r * rb) & (kLineBytes - 1));
     int64_t y0, y1;
@@ -334,6 +377,64 @@ FSDPPACK_HD inline bool pack_direct(const WindowArgs &a, int32_t w, DirectWindow
     d.dst_dt = a.reduce_dt;
     // a bf16 source may start 2 bytes past a dword (the kernel then shifts)
     return (d.src & (pm.src_dt == kBF16 ? 1u : 3u)) == 0 && ((a.shift + d.dst_off) & 15) == 0;
+}
+
+// pack_direct_rk for pack window w (linear index, pack_row_window).
+FSDPPACK_HD inline bool pack_direct(const WindowArgs &a, int32_t w, DirectWindow &d)
+{
+    int32_t r, k;
+    pack_row_window(a, w, r, k);
+    return pack_direct_rk(a, r, k, d);
+}
+
+// Whether window k of row r is a direct window according to the stretch
+// records (a.stretches, built for the call's pointer set by
+// build_pack_stretches): one whole window inside one member's rank chunk,
+// every element real.  One scalar load of 64 bytes (the stretch record of
+// the window's last byte) stands between the launch arguments and the data;
+// the index arithmetic is 32-bit (rows of fewer than 2^31 bytes).  Fills `d`
+// as pack_direct does; the window then equals the single range
+// pack_window_rk produces for it.
+// (The launch's fields the test reads are passed one by one: the kernel takes
+// them as leading scalar arguments, which the hardware can place in scalar
+// registers before the wave starts.)  rb: row bytes; lg: log2 of the
+// reduction dtype's size.
+FSDPPACK_HD inline bool pack_direct_stretch_s(const PackStretch *stretches, uint32_t rb, uint32_t shift,
+                                              uint32_t map_lg, uint32_t lg, int32_t reduce_dt, int32_t r, int32_t k,
+                                              DirectWindow &d)
+{
+    const uint32_t s_r = (shift + static_cast<uint32_t>(r) * rb) & (kLineBytes - 1);
+    const uint32_t kb = static_cast<uint32_t>(k) << kWindowLog2;
+    if (kb < s_r) return false;                                         // the row's first, partial window
+    const uint32_t y0 = kb - s_r, y1 = y0 + kWindowBytes;
+    if (y1 > rb) return false;                                          // the row's last, partial window
+    const uint32_t c0 = y0 >> lg, c1 = y1 >> lg;
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
+    const u32x16 v = ((const FSDPPACK_TABLE u32x16 *)stretches)[(y1 - 1) >> map_lg];
+    PackStretch e;
+    __builtin_memcpy(&e, &v, sizeof e);
+#else
+    const PackStretch e = stretches[(y1 - 1) >> map_lg];
+#endif
+    const PackCand &c = (e.c[1].dt != 0 && c0 >= e.c[1].O) ? e.c[1] : e.c[0];
+    if (c.dt == 0 || c0 < c.O || c1 > c.OP) return false;
+    const uint32_t ur = static_cast<uint32_t>(r);
+    if (ur > c.full || (ur == c.full && c1 > c.OT)) return false;       // padding in the window
+    const uint32_t ssz = c.dt == kBF16 ? 2u : 4u;
+    d.src = c.base + static_cast<uint64_t>(ur) * c.Pss + static_cast<uint64_t>(c0) * ssz;
+    d.dst_off = static_cast<int64_t>(static_cast<uint64_t>(ur) * rb + y0);
+    d.src_dt = static_cast<int32_t>(c.dt);
+    d.dst_dt = reduce_dt;
+    // a bf16 source may start 2 bytes past a dword (the kernel then shifts)
+    return (d.src & (ssz - 1)) == 0 && ((shift + d.dst_off) & 15) == 0;
+}
+
+FSDPPACK_HD inline bool pack_direct_stretch(const WindowArgs &a, int32_t r, int32_t k, DirectWindow &d)
+{
+    const uint32_t lg = a.reduce_dt == kBF16 ? 1u : 2u;
+    return pack_direct_stretch_s(a.stretches, static_cast<uint32_t>(a.S) << lg, static_cast<uint32_t>(a.shift),
+                                 static_cast<uint32_t>(a.map_lg), lg, a.reduce_dt, r, k, d);
 }
 
 // Copy-in window w: bytes [y0, y1) of the row, which lie in one or two

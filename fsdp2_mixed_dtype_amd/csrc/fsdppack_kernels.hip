@@ -55,6 +55,15 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kBlock = 64;    // threads per workgroup (one wave64)
 constexpr int kUnroll = 2;    // destination vectors per thread per pass
 static_assert(kBlock * kUnroll * 16 == kWindowBytes, "one window is one pass of the workgroup");
+// The pack's workgroup shape.  A plain bf16 -> fp32 cast of the 50.3M-element
+// layout's bytes streams faster on MI355X as 128-thread workgroups of one
+// vector per lane (44.9-45.2 us) than as one wave of two (46.7-47.3 us), but
+// the pack in that shape took 59.8 us against 48.1 us: every wave still pays
+// its launch-argument and stretch-record reads before its first data load,
+// behind half the bytes.
+constexpr int kPackBlock = 64;
+constexpr int kPackUnroll = 2;
+static_assert(kPackBlock * kPackUnroll * 16 == kWindowBytes, "one window is one pass of the workgroup");
 
 template <int DT> struct ElemT;
 template <> struct ElemT<kBF16> { using T = uint16_t; };
@@ -284,7 +293,7 @@ __device__ __forceinline__ void copy_straddle(const char *src, const VecOut &out
 // workgroup take part; no two threads write the same byte.  NT: the whole
 // source vectors are loaded non-temporally.  DIV: every element is divided
 // by d (in S) before the cast.
-template <int S, int D, bool NT, bool DIV>
+template <int S, int D, bool NT, bool DIV, int BLK = kBlock, int UNR = kUnroll>
 __device__ void copy_range(const char *__restrict__ src, char *__restrict__ dst, int64_t lo,
                            int64_t hi, int64_t valid, float d)
 {
@@ -310,16 +319,16 @@ __device__ void copy_range(const char *__restrict__ src, char *__restrict__ dst,
         // element alignment makes the source 4-byte aligned, or 2 bytes past
         // a dword boundary for a bf16 source at an odd element offset
         if ((reinterpret_cast<uintptr_t>(s0) & 3u) == 0) {
-            for (int64_t q = tid; q < nfull; q += kBlock * kUnroll) {
-                uint32_t w[kUnroll][P::NSRC];
+            for (int64_t q = tid; q < nfull; q += BLK * UNR) {
+                uint32_t w[UNR][P::NSRC];
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
-                    const int64_t qq = q + u * kBlock;
+                for (int u = 0; u < UNR; ++u) {
+                    const int64_t qq = q + u * BLK;
                     if (qq < nfull) load_dwords<P::NSRC, NT>(s0 + qq * SV, w[u]);
                 }
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
-                    const int64_t qq = q + u * kBlock;
+                for (int u = 0; u < UNR; ++u) {
+                    const int64_t qq = q + u * BLK;
                     if (qq < nfull) {
                         if constexpr (DIV) divide_words<S>(w[u], d);
                         out.put(qq, convert_vec<S, D>(w[u]));
@@ -328,16 +337,16 @@ __device__ void copy_range(const char *__restrict__ src, char *__restrict__ dst,
             }
         } else if constexpr (S == kBF16) {
             const char *a0 = s0 - 2;
-            for (int64_t q = tid; q < nfull; q += kBlock * kUnroll) {
-                uint32_t w[kUnroll][P::NSRC];
+            for (int64_t q = tid; q < nfull; q += BLK * UNR) {
+                uint32_t w[UNR][P::NSRC];
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
-                    const int64_t qq = q + u * kBlock;
+                for (int u = 0; u < UNR; ++u) {
+                    const int64_t qq = q + u * BLK;
                     if (qq < nfull) load_half_shifted<P::NSRC, NT>(a0 + qq * SV, w[u]);
                 }
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
-                    const int64_t qq = q + u * kBlock;
+                for (int u = 0; u < UNR; ++u) {
+                    const int64_t qq = q + u * BLK;
                     if (qq < nfull) {
                         if constexpr (DIV) divide_words<S>(w[u], d);
                         out.put(qq, convert_vec<S, D>(w[u]));
@@ -349,7 +358,7 @@ __device__ void copy_range(const char *__restrict__ src, char *__restrict__ dst,
 
     // the straddling vector (if any) and the all-padding vectors
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    for (int64_t q = nfull + tid; q < nvec; q += kBlock) {
+    for (int64_t q = nfull + tid; q < nvec; q += BLK) {
         const int64_t i0 = v0 + q * P::V;
         if (i0 >= valid) out.put(q, zero);
         else copy_straddle<S, D, DIV>(src, out, q, i0, valid, d);
@@ -367,7 +376,7 @@ __device__ void copy_range(const char *__restrict__ src, char *__restrict__ dst,
 // layout.  DIV: divide every element by d before the cast (write-back only).
 // SAME: the range never casts (the copy-out moves a parameter's own dtype),
 // so only the two plain copies are compiled in.
-template <bool NT, bool DIV, bool SAME = false>
+template <bool NT, bool DIV, bool SAME = false, int BLK = kBlock, int UNR = kUnroll>
 __device__ __forceinline__ void run_range(const RangeRef &g, char *base, float d)
 {
     char *tp = reinterpret_cast<char *>(g.ptr);
@@ -376,15 +385,15 @@ __device__ __forceinline__ void run_range(const RangeRef &g, char *base, float d
     if (g.table_side == kTableIsSource) { src = tp + g.src_off; dst = base + g.dst_off; }
     else { src = base + g.src_off; dst = tp + g.dst_off; }
     if constexpr (SAME) {
-        if (g.dst_dt == kBF16) copy_range<kBF16, kBF16, NT, DIV>(src, dst, g.lo, g.hi, g.valid, d);
-        else copy_range<kFP32, kFP32, NT, DIV>(src, dst, g.lo, g.hi, g.valid, d);
+        if (g.dst_dt == kBF16) copy_range<kBF16, kBF16, NT, DIV, BLK, UNR>(src, dst, g.lo, g.hi, g.valid, d);
+        else copy_range<kFP32, kFP32, NT, DIV, BLK, UNR>(src, dst, g.lo, g.hi, g.valid, d);
         return;
     }
     switch (g.src_dt * 4 + g.dst_dt) {
-    case kBF16 * 4 + kFP32: copy_range<kBF16, kFP32, NT, DIV>(src, dst, g.lo, g.hi, g.valid, d); break;
-    case kFP32 * 4 + kFP32: copy_range<kFP32, kFP32, NT, DIV>(src, dst, g.lo, g.hi, g.valid, d); break;
-    case kFP32 * 4 + kBF16: copy_range<kFP32, kBF16, NT, DIV>(src, dst, g.lo, g.hi, g.valid, d); break;
-    case kBF16 * 4 + kBF16: copy_range<kBF16, kBF16, NT, DIV>(src, dst, g.lo, g.hi, g.valid, d); break;
+    case kBF16 * 4 + kFP32: copy_range<kBF16, kFP32, NT, DIV, BLK, UNR>(src, dst, g.lo, g.hi, g.valid, d); break;
+    case kFP32 * 4 + kFP32: copy_range<kFP32, kFP32, NT, DIV, BLK, UNR>(src, dst, g.lo, g.hi, g.valid, d); break;
+    case kFP32 * 4 + kBF16: copy_range<kFP32, kBF16, NT, DIV, BLK, UNR>(src, dst, g.lo, g.hi, g.valid, d); break;
+    case kBF16 * 4 + kBF16: copy_range<kBF16, kBF16, NT, DIV, BLK, UNR>(src, dst, g.lo, g.hi, g.valid, d); break;
     default: break;   // the planner only emits the four pairs above
     }
 }
@@ -406,62 +415,62 @@ __device__ __forceinline__ void run_range(const RangeRef &g, char *base, float d
 // source pieces into four 8-byte halves, so every load instruction reads
 // 1 KiB and every store writes 512 B contiguously (on MI355X the copy-in of
 // the 218M-element block 5 % faster; the pack unchanged).
-template <int S, int D, bool COPY>
+template <int S, int D, bool COPY, int BLK = kBlock, int UNR = kUnroll>
 __device__ __forceinline__ void copy_window_direct(const char *src, char *dst)
 {
     using P = Path<S, D>;
     constexpr int64_t SV = P::V * static_cast<int64_t>(sizeof(typename P::ST));
-    const VecOut out(dst, kBlock * kUnroll);
+    const VecOut out(dst, BLK * UNR);
     const int tid = threadIdx.x;
     if constexpr (S == kFP32 && D == kBF16) {
-        uint32_t h[2 * kUnroll][4];
+        uint32_t h[2 * UNR][4];
         if (COPY || (reinterpret_cast<uintptr_t>(src) & (kLineBytes - 1)) == 0) {
 #pragma unroll
-            for (int u = 0; u < 2 * kUnroll; ++u) load_dwords<4, true>(src + (tid + u * kBlock) * 16, h[u]);
+            for (int u = 0; u < 2 * UNR; ++u) load_dwords<4, true>(src + (tid + u * BLK) * 16, h[u]);
         } else {
 #pragma unroll
-            for (int u = 0; u < 2 * kUnroll; ++u) load_dwords<4, false>(src + (tid + u * kBlock) * 16, h[u]);
+            for (int u = 0; u < 2 * UNR; ++u) load_dwords<4, false>(src + (tid + u * BLK) * 16, h[u]);
         }
 #pragma unroll
-        for (int u = 0; u < 2 * kUnroll; ++u) {
+        for (int u = 0; u < 2 * UNR; ++u) {
             u32x2 r;
             r.x = f32_to_bf16(h[u][0]) | (f32_to_bf16(h[u][1]) << 16);
             r.y = f32_to_bf16(h[u][2]) | (f32_to_bf16(h[u][3]) << 16);
-            out.put8(tid + u * kBlock, r);
+            out.put8(tid + u * BLK, r);
         }
         return;
     }
-    uint32_t w[kUnroll][P::NSRC];
+    uint32_t w[UNR][P::NSRC];
     if (COPY || (reinterpret_cast<uintptr_t>(src) & (kLineBytes - 1)) == 0) {
         if (S != kBF16 || (reinterpret_cast<uintptr_t>(src) & 3u) == 0) {
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) load_dwords<P::NSRC, true>(src + (tid + u * kBlock) * SV, w[u]);
+            for (int u = 0; u < UNR; ++u) load_dwords<P::NSRC, true>(src + (tid + u * BLK) * SV, w[u]);
         } else {
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
-                load_half_shifted<P::NSRC, true>(src - 2 + (tid + u * kBlock) * SV, w[u]);
+            for (int u = 0; u < UNR; ++u)
+                load_half_shifted<P::NSRC, true>(src - 2 + (tid + u * BLK) * SV, w[u]);
         }
     } else if (S != kBF16 || (reinterpret_cast<uintptr_t>(src) & 3u) == 0) {
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) load_dwords<P::NSRC, false>(src + (tid + u * kBlock) * SV, w[u]);
+        for (int u = 0; u < UNR; ++u) load_dwords<P::NSRC, false>(src + (tid + u * BLK) * SV, w[u]);
     } else {
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) load_half_shifted<P::NSRC, false>(src - 2 + (tid + u * kBlock) * SV, w[u]);
+        for (int u = 0; u < UNR; ++u) load_half_shifted<P::NSRC, false>(src - 2 + (tid + u * BLK) * SV, w[u]);
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) out.put(tid + u * kBlock, convert_vec<S, D>(w[u]));
+    for (int u = 0; u < UNR; ++u) out.put(tid + u * BLK, convert_vec<S, D>(w[u]));
 }
 
-template <bool COPY>
+template <bool COPY, int BLK = kBlock, int UNR = kUnroll>
 __device__ __forceinline__ void run_direct(const DirectWindow &d, char *base)
 {
     const char *src = reinterpret_cast<const char *>(d.src);
     char *dst = base + d.dst_off;
     switch (d.src_dt * 4 + d.dst_dt) {
-    case kBF16 * 4 + kFP32: copy_window_direct<kBF16, kFP32, COPY>(src, dst); break;
-    case kFP32 * 4 + kFP32: copy_window_direct<kFP32, kFP32, COPY>(src, dst); break;
-    case kFP32 * 4 + kBF16: copy_window_direct<kFP32, kBF16, COPY>(src, dst); break;
-    case kBF16 * 4 + kBF16: copy_window_direct<kBF16, kBF16, COPY>(src, dst); break;
+    case kBF16 * 4 + kFP32: copy_window_direct<kBF16, kFP32, COPY, BLK, UNR>(src, dst); break;
+    case kFP32 * 4 + kFP32: copy_window_direct<kFP32, kFP32, COPY, BLK, UNR>(src, dst); break;
+    case kFP32 * 4 + kBF16: copy_window_direct<kFP32, kBF16, COPY, BLK, UNR>(src, dst); break;
+    case kBF16 * 4 + kBF16: copy_window_direct<kBF16, kBF16, COPY, BLK, UNR>(src, dst); break;
     default: break;
     }
 }
@@ -545,18 +554,42 @@ __device__ __forceinline__ void copy_out_gather(const WindowArgs &a, const CopyO
         if (j * kBlock < left) dst[i0 + j * kBlock] = v[j];
 }
 
+// The reduce-scatter pack: one workgroup of kPackBlock threads per window,
+// on a 2-D grid (x: the windows of a row group, y: the row group).  A window
+// the stretch records (or, in a bucket without them, the column map) show to
+// lie inside one member's rank chunk is copied directly; any other window
+// walks its ranges.
+// The direct test's inputs come first, as scalar arguments (st: the stretch
+// records; rb: row bytes; meta: reduction dtype | log2 of its size << 8 |
+// group_lg << 16), so that they can be preloaded into scalar registers.
+__global__ void __launch_bounds__(kPackBlock) pack_kernel(const PackStretch *st, uint32_t rb, uint32_t shift,
+                                                          uint32_t map_lg, uint32_t meta, WindowArgs a)
+{
+    const uint32_t glg = meta >> 16, lg = (meta >> 8) & 0xFFu;
+    const int32_t k = static_cast<int32_t>(blockIdx.x >> glg);
+    const int32_t r = static_cast<int32_t>((blockIdx.y << glg) + (blockIdx.x & ((1u << glg) - 1)));
+    DirectWindow d;
+    if (st != nullptr) {
+        if (pack_direct_stretch_s(st, rb, shift, map_lg, lg, static_cast<int32_t>(meta & 0xFFu), r, k, d)) {
+            run_direct<false, kPackBlock, kPackUnroll>(d, a.base);
+            return;
+        }
+    } else if (pack_direct_rk(a, r, k, d)) {
+        run_direct<false, kPackBlock, kPackUnroll>(d, a.base);
+        return;
+    }
+    pack_window_rk(a, r, k,
+                   [&](const RangeRef &g) { run_range<false, false, false, kPackBlock, kPackUnroll>(g, a.base, 1.0f); });
+}
+
 // One workgroup per window; the window's ranges come from its index and the
 // plan's (cache-resident) record tables.
 template <int OP>
 __global__ void __launch_bounds__(kBlock) window_kernel(WindowArgs a)
 {
     const int32_t w = static_cast<int32_t>(blockIdx.x);
-    auto body = [&](const RangeRef &g) { run_range<OP != kOpPack, false>(g, a.base, 1.0f); };
-    if constexpr (OP == kOpPack) {
-        DirectWindow d;
-        if (pack_direct(a, w, d)) run_direct<false>(d, a.base);
-        else pack_window(a, w, body);
-    } else if constexpr (OP == kOpCopyIn) {
+    auto body = [&](const RangeRef &g) { run_range<true, false>(g, a.base, 1.0f); };
+    if constexpr (OP == kOpCopyIn) {
         DirectWindow d;
         int64_t y0, y1;
         int32_t m0, n;
@@ -594,8 +627,16 @@ int launch_windows(const WindowArgs &args, void *stream, void *start_event, void
     hipEvent_t e0 = static_cast<hipEvent_t>(start_event), e1 = static_cast<hipEvent_t>(stop_event);
     // hipExtLaunchKernelGGL: when events are given they are stamped by the
     // dispatch itself, so they bracket exactly this kernel's execution
-    if (args.op == kOpPack) hipExtLaunchKernelGGL(window_kernel<kOpPack>, grid, block, 0, st, e0, e1, 0, args);
-    else if (args.op == kOpCopyIn) hipExtLaunchKernelGGL(window_kernel<kOpCopyIn>, grid, block, 0, st, e0, e1, 0, args);
+    if (args.op == kOpPack) {
+        // x: the windows of a row group, y: the row groups
+        const dim3 grid2(static_cast<uint32_t>((args.gx + 1) << args.group_lg),
+                         static_cast<uint32_t>(args.W >> args.group_lg));
+        const uint32_t lg = args.reduce_dt == kBF16 ? 1u : 2u;
+        const uint32_t rb = args.stretches ? static_cast<uint32_t>(args.S) << lg : 0u;
+        const uint32_t meta = static_cast<uint32_t>(args.reduce_dt) | (lg << 8) | (static_cast<uint32_t>(args.group_lg) << 16);
+        hipExtLaunchKernelGGL(pack_kernel, grid2, dim3(kPackBlock), 0, st, e0, e1, 0, args.stretches, rb,
+                              static_cast<uint32_t>(args.shift), static_cast<uint32_t>(args.map_lg), meta, args);
+    } else if (args.op == kOpCopyIn) hipExtLaunchKernelGGL(window_kernel<kOpCopyIn>, grid, block, 0, st, e0, e1, 0, args);
     else if (args.op == kOpCopyOut) hipExtLaunchKernelGGL(window_kernel<kOpCopyOut>, grid, block, 0, st, e0, e1, 0, args);
     else if (args.op == kOpWriteBack) hipExtLaunchKernelGGL(window_kernel<kOpWriteBack>, grid, block, 0, st, e0, e1, 0, args);
     else if (args.op == kOpWriteBackFlat)

@@ -86,6 +86,17 @@ static int32_t build_record_map(std::vector<ColumnWindow> &map, int64_t total, i
     }
 }
 
+// Whether a pack table gets stretch records: the kernel's direct test works
+// in 32-bit column and row-byte arithmetic (rows of fewer than 2^31 bytes)
+// and steps between a member's rank chunks by a 32-bit byte count.
+static bool pack_narrow(const OpTable &op, const std::vector<PackMember> &mem)
+{
+    if (mem.empty() || (op.S * dtype_bytes(op.reduce_dt)) >= (int64_t{1} << 31)) return false;
+    for (const PackMember &m : mem)
+        if (m.P * dtype_bytes(m.src_dt) >= (int64_t{1} << 32) || m.numel >= (int64_t{1} << 32)) return false;
+    return true;
+}
+
 // Group map of a table of CopyOutTensor records whose windows are
 // consecutive (record t owns windows [win0_t, win0_{t+1})): for each group of
 // 2^kGroupLog2 windows, the records owning its first and last windows.
@@ -255,6 +266,7 @@ int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdp
         op.map_lg = build_record_map(op.columns, b.S, dsz == 2 ? 1 : 2, mem.size(), [&](size_t i) {
             return std::make_pair(mem[i].O, mem[i].O + mem[i].P);
         });
+        op.narrow = pack_narrow(op, mem);
     }
 
     {   // all-gather copy-in: each parameter owns bytes [A_t, A_{t+1}) of the
@@ -313,6 +325,40 @@ int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdp
         build_group_map(op);
     }
     return FSDPPACK_OK;
+}
+
+void build_pack_stretches(const OpTable &op, const uint64_t *ptrs, PackStretch *out)
+{
+    const PackMember *M = reinterpret_cast<const PackMember *>(op.members.data());
+    const int lg = op.reduce_dt == kBF16 ? 1 : 2;
+    const int64_t rb = op.S << lg, E = int64_t{1} << op.map_lg;
+    const int64_t nx = op.stretch_count();
+    int32_t first = 0;
+    for (int64_t x = 0; x < nx; ++x) {
+        // the columns of row bytes [x*E - window, (x+1)*E), clipped to the row:
+        // every window whose last byte lies in stretch x starts in there
+        const int64_t b0 = std::max<int64_t>(0, x * E - kWindowBytes), b1 = std::min(rb, (x + 1) * E);
+        const int64_t c0 = b0 >> lg, c1 = (b1 + (int64_t{1} << lg) - 1) >> lg;
+        while (first < op.n && M[first].O + M[first].P <= c0) ++first;
+        int32_t last = first;
+        while (last < op.n && M[last].O < c1) ++last;
+        PackStretch s{};                                   // dt 0: no candidate
+        if (last - first >= 1 && last - first <= 2) {
+            for (int32_t i = first; i < last; ++i) {
+                const PackMember &m = M[i];
+                const int64_t ssz = dtype_bytes(m.src_dt), full = m.numel / m.P;
+                PackCand &c = s.c[i - first];
+                c.base = ptrs[i] - static_cast<uint64_t>(m.O * ssz);
+                c.Pss = static_cast<uint32_t>(m.P * ssz);
+                c.O = static_cast<uint32_t>(m.O);
+                c.OP = static_cast<uint32_t>(m.O + m.P);
+                c.full = static_cast<uint32_t>(full);
+                c.OT = static_cast<uint32_t>(m.O + m.numel - full * m.P);
+                c.dt = static_cast<uint32_t>(m.src_dt);
+            }
+        }
+        out[x] = s;
+    }
 }
 
 int64_t shard_elements(const fsdppack_plan &plan, int32_t t, int32_t r)
@@ -408,6 +454,7 @@ int build_plan_flat(const fsdppack_param_desc *params, int32_t n, int32_t world,
         op.map_lg = build_record_map(op.columns, op.S, bsz == 2 ? 1 : 2, mem.size(), [&](size_t i) {
             return std::make_pair(mem[i].O, mem[i].O + mem[i].P);
         });
+        op.narrow = pack_narrow(op, mem);
     }
 
     // write-back and copy-in: windows over a rank's row, records by flat offset

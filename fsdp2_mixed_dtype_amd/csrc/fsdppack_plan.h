@@ -38,6 +38,9 @@ struct OpTable {
     int64_t B = 0;                        // all-gather row bytes
     int64_t dst_bytes = 0;                // bytes the operation writes
     int64_t src_bytes = 0;                // bytes it reads
+    bool narrow = false;                  // pack: rows of fewer than 2^31 bytes and rank chunks of fewer
+                                          // than 2^32 source bytes, so every pointer set also gets stretch
+                                          // records (one per column-map entry) for the direct windows
     void *d_members = nullptr;            // device copies (owned by the plan)
     void *d_columns = nullptr;
 
@@ -58,6 +61,14 @@ struct OpTable {
         if (dst_bytes == 0) return 0;
         if (op == kOpPack) return (static_cast<int64_t>(gx) + 1) * (dst_bytes / (S * dtype_bytes(reduce_dt)));
         return (shift + dst_bytes + kWindowBytes - 1) >> kWindowLog2;
+    }
+    // stretch records in a pointer set's device table (placed before its pointers)
+    int64_t stretch_count() const { return narrow ? static_cast<int64_t>(columns.size()) : 0; }
+    // bytes of a pointer set's device table: the stretch records, then one
+    // pointer per table entry
+    int64_t table_bytes(size_t entries) const
+    {
+        return stretch_count() * static_cast<int64_t>(sizeof(PackStretch)) + static_cast<int64_t>(entries) * 8;
     }
     // launch arguments against host (`device == false`) or device members
     WindowArgs args(bool device, int32_t shift) const
@@ -101,16 +112,18 @@ struct FlatLayout {
 // Per-call pointer tables, cached on the device by content: the same grads /
 // shards / params pointers (the usual case from step to step) reuse an
 // uploaded table; a new set is staged through pinned host memory and copied
-// on the caller's stream.  A steady-state call records no event: a slot is
-// only rewritten after a device-wide synchronisation (eviction is rare), and
-// a stream that first uses a slot uploaded on another stream waits once for
-// the upload.
+// on the caller's stream.  A steady-state call records no event; a stream
+// that first uses a slot uploaded on another stream waits once for the
+// upload.  Rewriting a slot for a new set waits on the host for the slot's
+// previous upload only, and on the device for the other streams that used it
+// (acquire_table), never for the whole device.
 struct PtrSlot {
     std::vector<uint64_t> key;
     uint64_t *d_table = nullptr;
     uint64_t *h_stage = nullptr;      // pinned host staging of this slot
     void *ready = nullptr;            // hipEvent_t: upload finished
     std::vector<void *> streams;      // streams ordered after the upload
+    std::vector<void *> drain;        // hipEvent_t pool: other streams' work, at an eviction
     uint64_t last_use = 0;
     bool live = false;
 };
@@ -159,5 +172,11 @@ int build_plan_flat(const fsdppack_param_desc *params, int32_t n, int32_t world,
 // Real elements of parameter t on rank r: the rank chunk's (per-parameter
 // layout) or the piece inside the rank's flat positions (flat layout).
 int64_t shard_elements(const fsdppack_plan &plan, int32_t t, int32_t r);
+
+// The stretch records of a narrow pack table for one pointer set (`ptrs`: the
+// gradients in member order, the pack's pointer-table order): for each
+// column-map stretch, the members overlapping its bytes extended one window to
+// the left, when there are one or two of them (else none).
+void build_pack_stretches(const OpTable &op, const uint64_t *ptrs, PackStretch *out);
 
 }  // namespace fsdppack

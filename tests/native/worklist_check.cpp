@@ -15,8 +15,10 @@
 //    ends with its row, for several offsets of the destination past a line
 //    boundary; only the pack's spare window at the end of a row may have no
 //    range;
-//  * a pack or copy-in window that takes the kernel's direct copy is exactly
-//    the one range the general walk gives for it, and a copy-out window the
+//  * a pack or copy-in window that takes the kernel's direct copy (for the
+//    pack also through the stretch records of a made-up pointer set) is
+//    exactly the one range the general walk gives for it, the pack's 2-D
+//    grid maps every workgroup to the window the linear index names, and a copy-out window the
 //    kernel gathers element by element reads, for every element, the byte
 //    the chunk walk reads for it, and a copy-in window it gathers vector by
 //    vector takes each vector from the record the walk takes it from;
@@ -41,7 +43,8 @@
 using namespace fsdppack;
 
 static std::string g_fail;
-static int64_t g_direct = 0;      // pack windows taking the direct copy
+static int64_t g_direct = 0;      // pack windows taking the direct copy (column map)
+static int64_t g_direct_st = 0;   // pack windows taking it through the stretch records
 static int64_t g_direct_in = 0;   // copy-in windows taking it
 static int64_t g_gather = 0;      // copy-out windows gathered element by element
 static int64_t g_gather_in = 0;   // copy-in windows gathered vector by vector
@@ -123,6 +126,19 @@ static bool check_op(const char *name, const OpTable &op, int32_t W, int32_t shi
     CHECK((op.op != kOpCopyOut && op.op != kOpWriteBack) ||
               op.columns.size() == static_cast<size_t>((op.n_windows + (1 << kGroupLog2) - 1) >> kGroupLog2),
           "%s: group map size", name);
+    // stretch records of a narrow pack for a made-up pointer set: member m's
+    // gradient at 2^32 * (m + 1), plus one element for odd m (bf16 sources
+    // then start 2 bytes past a dword)
+    std::vector<uint64_t> ptrs(static_cast<size_t>(op.n));
+    std::vector<PackStretch> stretches(static_cast<size_t>(op.stretch_count()));
+    if (op.op == kOpPack) {
+        const PackMember *M = reinterpret_cast<const PackMember *>(op.members.data());
+        for (int32_t m = 0; m < op.n; ++m)
+            ptrs[m] = (static_cast<uint64_t>(m + 1) << 32) + ((m & 1) ? dtype_bytes(M[m].src_dt) : 0);
+        CHECK(op.narrow == (op.stretch_count() > 0) && (!op.narrow || op.stretch_count() == static_cast<int64_t>(op.columns.size())),
+              "%s: stretch records", name);
+        if (op.narrow) build_pack_stretches(op, ptrs.data(), stretches.data());
+    }
     for (int32_t w = 0; w < a.n_windows; ++w) {
         int ranges = 0;
         bool ok = true;
@@ -151,6 +167,34 @@ static bool check_op(const char *name, const OpTable &op, int32_t W, int32_t shi
                 });
                 CHECK(n_rng == 1 && same, "%s: window %d (shift %d): direct copy differs from its range", name, w, shift);
                 ++g_direct;
+            }
+            // the launch's 2-D grid gives the same row and window
+            int32_t r, k, r2, k2;
+            pack_row_window(a, w, r, k);
+            const int32_t span = (a.gx + 1) << a.group_lg;
+            pack_row_window_2d(a, static_cast<uint32_t>(w % span), static_cast<uint32_t>(w / span), r2, k2);
+            CHECK(r == r2 && k == k2, "%s: window %d: 2-D grid maps to row %d window %d, not %d / %d", name, w, r2, k2,
+                  r, k);
+            // the direct copy through the stretch records is likewise the one
+            // range of the walk, read from the member's own pointer
+            if (op.narrow) {
+                WindowArgs as = a;
+                as.stretches = stretches.data();
+                DirectWindow ds{};
+                if (pack_direct_stretch(as, r, k, ds)) {
+                    int n_rng = 0;
+                    bool same = false;
+                    for_each_range(a, w, [&](const RangeRef &g) {
+                        ++n_rng;
+                        const int64_t ssz = dtype_bytes(g.src_dt), dsz = dtype_bytes(g.dst_dt);
+                        same = g.hi - g.lo == kWindowBytes / dsz && g.valid >= g.hi && g.src_dt == ds.src_dt &&
+                               g.dst_dt == ds.dst_dt && ds.src == ptrs[g.slot] + static_cast<uint64_t>(g.src_off + g.lo * ssz) &&
+                               ds.dst_off == g.dst_off + g.lo * dsz && (a.shift + ds.dst_off) % 16 == 0;
+                    });
+                    CHECK(n_rng == 1 && same, "%s: window %d (shift %d): stretch-direct copy differs from its range",
+                          name, w, shift);
+                    ++g_direct_st;
+                }
             }
         }
         if (op.op == kOpCopyIn) {
@@ -359,9 +403,10 @@ int main(int argc, char **argv)
     }
     std::printf("OK %s%zu buckets, windows:", flat ? "flat, " : "", plan.buckets.size());
     for (const BucketPlan &b : plan.buckets) std::printf(" %d (rows/group %d)", b.pack.n_windows, 1 << b.pack.group_lg);
-    std::printf(" copy_in %d copy_out %d; direct pack windows %lld, direct copy-in windows %lld, "
-                "gathered copy-in windows %lld, gathered copy-out windows %lld\n",
+    std::printf(" copy_in %d copy_out %d; direct pack windows %lld, stretch-direct pack windows %lld, "
+                "direct copy-in windows %lld, gathered copy-in windows %lld, gathered copy-out windows %lld\n",
                 plan.copy_in.n_windows, plan.copy_out.n_windows, static_cast<long long>(g_direct),
+                static_cast<long long>(g_direct_st),
                 static_cast<long long>(g_direct_in), static_cast<long long>(g_gather_in), static_cast<long long>(g_gather));
     return 0;
 }
