@@ -11,18 +11,26 @@ Prints ONE JSON line (rank 0):
   value        whole-step algorithmic bytes / step time  (GB/s)
   ms_per_step  wall time per step over the K timed steps (launched as a
                caller would, nothing between the kernels)
-  roofline     the pack kernel: algorithmic bytes per launch / mean launch
-               time vs 8 TB/s HBM peak.  Launch times come from K further
-               steps in which HIP events are stamped by each kernel's own
+  ms_per_pack  the metric's quantity: mean time of the fused pack (all
+               buckets), from HIP events stamped by each pack kernel's own
                dispatch at its start and end (hipExtLaunchKernelGGL on the
-               launch stream);
-               traffic from the committed rocprofv3 counter summary when it
-               was taken on the current kernel source, else null
-  cpu_baseline the CPU oracle's pack, single thread, on a bounded sample
-plus, measured in the same run: per-kernel times, the pack's p10/p50/p90
-cold and warm, the pre-cast-then-pack comparator, a plain-copy ceiling, the
-reduce-scatter write-back of rank 0 (with the oracle's rate beside it) and
-the pack beside a stream of bf16 GEMMs.
+               launch stream), over K further steps
+  roofline     the pack kernel of the largest bucket: algorithmic bytes per
+               launch / mean launch time vs 8 TB/s HBM peak; traffic from the
+               committed rocprofv3 counter summary when it was taken on the
+               current kernel source, else null
+  targets      the pack of both target layouts (the 50.3M-element layout and
+               one block of the 1.75B KDA-style model), measured in this run
+  cpu_baseline the CPU oracle's pack, unchanged, on all host cores (one task
+               per member and block of ranks) with the single-thread figure
+               beside it; median of 5 after one warm-up, repeated for a few
+               seconds of CPU work
+plus, measured in the same run: per-kernel times, the pack's p10/p50/p90 cold
+and warm, the pre-cast-then-pack comparator (its output checked equal to the
+fused pack's), a plain-copy ceiling, the reduce-scatter write-back of rank 0
+(with the oracle's rate beside it), the launch floor of every launch of the
+step (an empty kernel of the same grid), a pointer-churn leg (new gradient
+pointers on every call) and the pack beside a stream of bf16 GEMMs.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--flat]
 (--flat: the workload's tensors as one FSDP1 flat parameter.)
@@ -45,6 +53,8 @@ METRIC = "ms per fused mixed-dtype pack + achieved HBM GB/s (% of MI355X peak)"
 HBM_PEAK_GBPS = 8000.0
 PAGES_H100_FUSED_MS = 0.1888      # isolated H100 test, 50.3M-element layout (context only)
 PAGES_H100_PRECAST_MS = 0.3582
+TARGET_WORKLOADS = ("mixed50m", "kda_block")     # the layouts the >= 80 % target names
+WINDOW_BYTES = 2048                               # destination bytes per workgroup of the library's kernels
 # the sources that decide what a pack launch reads and writes
 KERNEL_SOURCES = [os.path.join(ROOT, "fsdp2_mixed_dtype_amd", "csrc", f)
                   for f in ("fsdppack_kernels.hip", "fsdppack_internal.h", "fsdppack_plan.cpp")]
@@ -58,8 +68,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixed50m")
     ap.add_argument("--rotate-bytes", type=float, default=2.0, help="GiB of buffers rotated across steps")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="bound on the CPU-oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=4.0,
+                    help="minimum seconds of each CPU-oracle timing (single thread, all cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-targets", action="store_true", help="skip the other target layout's pack")
     ap.add_argument("--pack-only", action="store_true",
                     help="run only pack launches (for counter collection under rocprofv3)")
     ap.add_argument("--flat", action="store_true",
@@ -86,6 +98,177 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+def pct(v, q):
+    v = sorted(v)
+    return v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
+
+
+def median(v):
+    return pct(v, 0.5)
+
+
+class Bench:
+    """Device-side helpers shared by the legs (torch only for memory, streams
+    and events; every step of the work runs in the library's kernels)."""
+
+    def __init__(self, args):
+        import numpy as np
+        import torch
+
+        import fsdp2_mixed_dtype_amd as fp
+        import workloads as wl
+        self.np, self.torch, self.fp, self.wl = np, torch, fp, wl
+        self.args = args
+        self.dev = torch.device("cuda:0")
+        torch.cuda.set_device(self.dev)
+        self.stream = torch.cuda.current_stream()
+
+    def new_event(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)          # creates the underlying HIP event
+        return e
+
+    def to_dev(self, a, dt):
+        t = self.torch.from_numpy(self.np.ascontiguousarray(a))
+        if dt == self.fp.BF16:
+            t = t.view(self.torch.bfloat16)
+        return t.to(self.dev)
+
+    def esz(self, dt):
+        return self.fp.ELEM_SIZE[dt]
+
+    def pack_bytes(self, w, plan):
+        W = w.world
+        out = []
+        for b in plan.buckets:
+            rd = sum(plan.numel[i] * self.esz(w.tensors[i].grad_dtype) for i in b.members)
+            out.append(rd + W * b.S * self.esz(b.dtype))
+        return out
+
+    def grad_sets(self, w, plan, grads_h, R):
+        """R independent sets of device gradients and packed outputs."""
+        sets = []
+        for _ in range(R):
+            g = [self.to_dev(a, t.grad_dtype) for a, t in zip(grads_h, w.tensors)]
+            outs = [self.torch.empty(w.world * b.S, dtype=self.fp.TORCH_DTYPE[b.dtype], device=self.dev)
+                    for b in plan.buckets]
+            sets.append((self.fp.prepare_grads(plan, g), outs, g))
+        return sets
+
+    def time_packs(self, plan, sets, K, warmup):
+        """Per-bucket kernel times (ms) of K packs over the rotated sets, each
+        stamped by its own dispatch; returns [K][nb]."""
+        fp = self.fp
+        nb = len(plan.buckets)
+        for i in range(len(sets) + warmup):
+            g, outs, _ = sets[i % len(sets)]
+            for bi in range(nb):
+                fp.pack_reduce_scatter_input(plan, bi, g, outs[bi], self.stream)
+        ev = [[(self.new_event(), self.new_event()) for _ in range(nb)] for _ in range(K)]
+        self.torch.cuda.synchronize()
+        for i in range(K):
+            g, outs, _ = sets[i % len(sets)]
+            for bi in range(nb):
+                fp.time_next_launch(*ev[i][bi])
+                fp.pack_reduce_scatter_input(plan, bi, g, outs[bi], self.stream)
+        self.torch.cuda.synchronize()
+        return [[a.elapsed_time(b) for a, b in e] for e in ev]
+
+    def time_empty(self, workgroups, K):
+        """Mean time (ms) of an empty kernel of `workgroups` 64-thread workgroups."""
+        fp = self.fp
+        for _ in range(3):
+            fp.empty_launch(workgroups, 64, self.stream)
+        ev = [(self.new_event(), self.new_event()) for _ in range(K)]
+        self.torch.cuda.synchronize()
+        for e in ev:
+            fp.time_next_launch(*e)
+            fp.empty_launch(workgroups, 64, self.stream)
+        self.torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev) / K
+
+
+def pack_target(B, name, K, warmup, rotate_bytes):
+    """The pack of workload `name` alone (the per-parameter layout), timed like
+    the main workload's: rotated buffer sets, kernel-stamped events."""
+    w = B.wl.get(name)
+    plan = B.fp.plan_buckets(w.descs(), w.world)
+    pb = B.pack_bytes(w, plan)
+    R = min(16, max(2, math.ceil(rotate_bytes * 2**30 / sum(pb))))
+    sets = B.grad_sets(w, plan, B.wl.make_grads(w), R)
+    per = B.time_packs(plan, sets, K, warmup)
+    dom = max(range(len(pb)), key=lambda i: pb[i])
+    ms = [sum(x) for x in per]
+    dom_ms = sum(x[dom] for x in per) / K
+    res = {"ms_per_pack": round(sum(ms) / K, 5), "pack_bytes": sum(pb),
+           "GBps": round(sum(pb) / (sum(ms) / K * 1e-3) / 1e9, 1),
+           "frac_of_peak": round(pb[dom] / (dom_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+           "ms_p10_p50_p90": [round(pct(ms, q), 5) for q in (0.1, 0.5, 0.9)],
+           "buckets": len(pb), "rotated_sets": R}
+    del sets
+    plan.destroy()
+    return res
+
+
+def cpu_oracle_pack(ref, grads_h, threads, seconds):
+    """Time the oracle's pack of every bucket (the unchanged C routine) on
+    `threads` host threads: each task packs one member's rows [r0, r1) (the
+    routine called on that sub-layout: W = r1 - r0 rows, the gradient from
+    element r0*P, the output from row r0).  Tasks write disjoint bytes, and the
+    routine releases the interpreter lock while it runs.  Returns the per-pack
+    times (s) after one warm-up, at least 5 and at least `seconds` in all."""
+    import ctypes
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
+    lib = oracle._load()
+    outs = [np.empty((ref.W, b.S), dtype=oracle.NP_DTYPE[b.dtype]) for b in ref.buckets]
+    gs = [np.ascontiguousarray(g).reshape(-1) for g in grads_h]
+    total = sum(ref.W * P for b in ref.buckets for P in b.P)
+    chunk = max(1, total // (threads * 8))          # elements per task, roughly
+    tasks = []
+    for bi, b in enumerate(ref.buckets):
+        osz = oracle.ELEM_SIZE[b.dtype]
+        for k, i in enumerate(b.members):
+            P, O = b.P[k], b.O[k]
+            if P == 0:
+                continue
+            d = ref.params[i]
+            gsz = oracle.ELEM_SIZE[d.grad_dtype]
+            rows = max(1, min(ref.W, chunk // P))
+            for r0 in range(0, ref.W, rows):
+                r1 = min(ref.W, r0 + rows)
+                valid = max(0, d.numel - r0 * P)
+                src = gs[i].ctypes.data + (r0 * P * gsz if valid else 0)
+                tasks.append((r1 - r0, src, d.grad_dtype, valid, P, O, b.S, b.dtype,
+                              outs[bi].ctypes.data + r0 * b.S * osz, (r1 - r0) * P))
+    tasks.sort(key=lambda t: -t[-1])
+    args = [(W_, (ctypes.c_void_p * 1)(src), np.array([gdt], np.int32), np.array([valid], np.int64),
+             np.array([P], np.int64), np.array([O], np.int64), S, dt, dst)
+            for W_, src, gdt, valid, P, O, S, dt, dst, _ in tasks]
+
+    def run(a):
+        W_, src, gdt, valid, P, O, S, dt, dst = a
+        rc = lib.oracle_pack(W_, 1, src, gdt.ctypes.data, valid.ctypes.data, P.ctypes.data, O.ctypes.data, S, dt, dst)
+        if rc:
+            raise RuntimeError("oracle_pack: bad layout")
+
+    times = []
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        t_all = time.perf_counter()
+        while len(times) < 6 or (time.perf_counter() - t_all < seconds and len(times) < 200):
+            t0 = time.perf_counter()
+            if threads == 1:
+                for a in args:
+                    run(a)
+            else:
+                list(ex.map(run, args))
+            times.append(time.perf_counter() - t0)
+    return times[1:], outs
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -93,14 +276,9 @@ def main():
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
-    import torch
-
-    import fsdp2_mixed_dtype_amd as fp
-    import workloads as wl
-
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
+    B = Bench(args)
+    np, torch, fp, wl = B.np, B.torch, B.fp, B.wl
+    dev = B.dev
     w = wl.get(args.workload)
     if args.flat:
         # one flat parameter per unit: one reduction and one param dtype
@@ -128,12 +306,8 @@ def main():
     plan_us = min(plan_times) * 1e6
 
     # ---- algorithmic bytes (read + write) per launch
-    def esz(dt):
-        return fp.ELEM_SIZE[dt]
-    pack_bytes = []
-    for b in plan.buckets:
-        rd = sum(plan.numel[i] * esz(w.tensors[i].grad_dtype) for i in b.members)
-        pack_bytes.append(rd + W * b.S * esz(b.dtype))
+    esz = B.esz
+    pack_bytes = B.pack_bytes(w, plan)
     if args.flat:   # rank 0's pieces read, its whole row (padding included) written
         copy_in_bytes = sum(fp.valid_in_chunk(plan, i, 0) * esz(t.storage_dtype) for i, t in enumerate(w.tensors)) \
             + plan.B
@@ -144,33 +318,25 @@ def main():
 
     # ---- inputs: seeded host draws, uploaded once per rotation set
     grads_h = wl.make_grads(w)
-
-    def to_dev(a, dt):
-        t = torch.from_numpy(np.ascontiguousarray(a))
-        if dt == fp.BF16:
-            t = t.view(torch.bfloat16)
-        return t.to(dev)
-
     set_bytes = step_bytes
     # enough sets that a step never finds its data in the last-level cache,
     # capped for tiny layouts where the whole working set is a few KB
     R = min(16, max(2, math.ceil(args.rotate_bytes * 2**30 / set_bytes)))
     sets = []
-    for r in range(R):
-        g = [to_dev(a, t.grad_dtype) for a, t in zip(grads_h, w.tensors)]
-        outs = [torch.empty(W * b.S, dtype=fp.TORCH_DTYPE[b.dtype], device=dev) for b in plan.buckets]
+    for gset in B.grad_sets(w, plan, grads_h, R):
+        g_prep, outs, g = gset
         shard_len = [fp.valid_in_chunk(plan, i, 0) if args.flat else plan.P[i] for i in range(len(w.tensors))]
         shards = [torch.randn(P, device=dev).to(fp.TORCH_DTYPE[t.storage_dtype]) for P, t in zip(shard_len, w.tensors)]
         ag = torch.randint(0, 255, (W * plan.B,), dtype=torch.uint8, device=dev)
         params = [torch.empty(t.numel, dtype=fp.TORCH_DTYPE[t.param_dtype], device=dev) for t in w.tensors]
         # pointer arrays validated once, reused every step (as a training loop
         # reuses its buffers)
-        sets.append((fp.prepare_grads(plan, g), outs, fp.prepare_shards(plan, shards, 0), ag,
-                     fp.prepare_params(plan, params), g))
+        sets.append((g_prep, outs, fp.prepare_shards(plan, shards, 0), ag, fp.prepare_params(plan, params), g))
     torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream()
+    stream = B.stream
     nb = len(plan.buckets)
+    new_event = B.new_event
 
     def timed(pair):
         # the library stamps these events at the kernel's own start and end
@@ -188,11 +354,6 @@ def main():
         fp.all_gather_copy_in(plan, 0, shards, ag, stream)
         timed(None if ev is None else ev[nb + 1])
         fp.all_gather_copy_out(plan, ag, params, stream)
-
-    def new_event():
-        e = torch.cuda.Event(enable_timing=True)
-        e.record(stream)          # creates the underlying HIP event
-        return e
 
     # prime: one pass over every buffer set (each set's first call uploads its
     # pointer tables), then the W warm-up steps
@@ -230,19 +391,8 @@ def main():
     # spread of the per-step pack time (all buckets), and the same packs with
     # their data warm: one buffer set repeated, so much of it stays in the
     # 256 MB Infinity Cache between steps
-    per_step = sorted(sum(e[bi][0].elapsed_time(e[bi][1]) for bi in range(nb)) for e in evs)
-
-    def pct(v, q):
-        return v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
-
-    e_warm = [[(new_event(), new_event()) for _ in range(nb)] for _ in range(K)]
-    for i in range(args.warmup + K):
-        g, outs = sets[0][0], sets[0][1]
-        for bi in range(nb):
-            timed(e_warm[i - args.warmup][bi] if i >= args.warmup else None)
-            fp.pack_reduce_scatter_input(plan, bi, g, outs[bi], stream)
-    torch.cuda.synchronize()
-    warm = sorted(sum(a.elapsed_time(b) for a, b in e) for e in e_warm)
+    per_step = [sum(e[bi][0].elapsed_time(e[bi][1]) for bi in range(nb)) for e in evs]
+    warm = [sum(x) for x in B.time_packs(plan, [sets[0][:2] + (None,)], K, args.warmup)]
     copy_in_ms = None if args.pack_only else mean_ms(nb)
     copy_out_ms = None if args.pack_only else mean_ms(nb + 1)
     pack_total_ms = sum(pack_ms)
@@ -251,7 +401,8 @@ def main():
 
     extra = {}
     if not args.pack_only:
-        # ---- pre-cast then homogeneous pack (the pages' comparator), our kernels, 2 launches
+        # ---- pre-cast then homogeneous pack (the pages' comparator), our kernels, 2 launches;
+        # its output must equal the fused pack's, byte for byte
         bf_idx = [i for i, t in enumerate(w.tensors) if t.grad_dtype == fp.BF16]
         if bf_idx and nb == 1 and plan.buckets[0].dtype == fp.FP32 and not args.flat:
             cast_plan = fp.plan_buckets([(w.tensors[i].numel, 1, fp.BF16, fp.FP32, fp.FP32, fp.FP32)
@@ -265,7 +416,8 @@ def main():
                 views = list(sets[r][5])
                 for k, i in enumerate(bf_idx):
                     views[i] = tmp[cast_offsets[k]: cast_offsets[k] + w.tensors[i].numel]
-                csets.append((tmp, fp.prepare_grads(homo, views), sets[r][1][0],
+                cmp_out = torch.empty_like(sets[r][1][0])
+                csets.append((tmp, fp.prepare_grads(homo, views), cmp_out,
                               fp.prepare_grads(cast_plan, [sets[r][5][j] for j in bf_idx])))
             e_c = [(new_event(), new_event(), new_event(), new_event()) for _ in range(K)]
             for i in range(args.warmup + K):
@@ -275,12 +427,21 @@ def main():
                 fp.pack_reduce_scatter_input(cast_plan, 0, bf, tmp, stream)
                 timed(None if e is None else e[2:4])
                 fp.pack_reduce_scatter_input(homo, 0, views, out, stream)
+            # the comparator computes the same result: check it on every set
+            for r in range(R):
+                fp.pack_reduce_scatter_input(plan, 0, sets[r][0], sets[r][1][0], stream)
             torch.cuda.synchronize()
+            for r in range(R):
+                if not torch.equal(csets[r][2].view(torch.int32), sets[r][1][0].view(torch.int32)):
+                    raise SystemExit("bench.py: the pre-cast-then-pack comparator's output differs from the "
+                                     f"fused pack's (set {r})")
             precast_ms = sum(a.elapsed_time(b) + c.elapsed_time(d) for a, b, c, d in e_c) / K
             extra.update(precast_then_pack_ms=round(precast_ms, 5), precast_vs_fused=round(precast_ms / pack_total_ms, 3),
-                         precast_temporaries_MiB=round(temp_elems * 4 / 2**20, 2))
+                         precast_temporaries_MiB=round(temp_elems * 4 / 2**20, 2),
+                         precast_output_equals_fused=True)
             cast_plan.destroy()
             homo.destroy()
+            del csets
 
         # ---- plain-copy ceiling: device-to-device copy moving the pack's byte count
         nbytes = sum(pack_bytes) // 2
@@ -322,12 +483,105 @@ def main():
                 timed(e_w[i - args.warmup][bi] if i >= args.warmup else None)
                 fp.reduce_scatter_copy_out(plan, bi, 0, row, dsts, float(W), stream)
         torch.cuda.synchronize()
-        wb_ms = sum(a.elapsed_time(b) for e in e_w for a, b in e) / K
+        wb_ms_b = [sum(e[bi][0].elapsed_time(e[bi][1]) for e in e_w) / K for bi in range(nb)]
+        wb_ms = sum(wb_ms_b)
         extra["rs_copy_out"] = {"ms": round(wb_ms, 5), "bytes": wb_bytes,
                                 "GBps": round(wb_bytes / (wb_ms * 1e-3) / 1e9, 1),
                                 "frac_of_peak": round(wb_bytes / (wb_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                                 "rank": 0, "divide_factor": W, "buckets": nb}
         del wsets
+
+        # ---- launch floor: each launch of the step against an empty kernel
+        # of the same number of 64-thread workgroups (the dispatch of its
+        # workgroups and the launch's fixed cost)
+        def ceil_div(a, b):
+            return -(-a // b)
+        shift = sets[0][3].data_ptr() % 128
+        wg = {}
+        for bi, b in enumerate(plan.buckets):
+            rows = 1 if args.flat else W
+            row_bytes = (W * b.S if args.flat else b.S) * esz(b.dtype)
+            wg[f"pack[{bi}]"] = (ceil_div(row_bytes, WINDOW_BYTES) + 1) * rows
+        wg["copy_in"] = ceil_div(shift + plan.B, WINDOW_BYTES)
+        wg["copy_out"] = sum(ceil_div(t.numel * esz(t.param_dtype), WINDOW_BYTES) for t in w.tensors if t.numel)
+        for bi, b in enumerate(plan.buckets):
+            if args.flat:
+                wg[f"write_back[{bi}]"] = ceil_div(plan.c * esz(b.dtype), WINDOW_BYTES)
+            else:
+                wg[f"write_back[{bi}]"] = sum(ceil_div(P * esz(w.tensors[i].storage_dtype), WINDOW_BYTES)
+                                              for i, P in zip(b.members, b.P) if P)
+        kernel_ms = {f"pack[{bi}]": pack_ms[bi] for bi in range(nb)}
+        kernel_ms.update(copy_in=copy_in_ms, copy_out=copy_out_ms)
+        kernel_ms.update({f"write_back[{bi}]": wb_ms_b[bi] for bi in range(nb)})
+        floors = {}
+        for name, n in wg.items():
+            f_ms = B.time_empty(n, K)
+            floors[name] = {"workgroups": n, "kernel_us": round(kernel_ms[name] * 1e3, 2),
+                            "floor_us": round(f_ms * 1e3, 2),
+                            "above_floor_us": round((kernel_ms[name] - f_ms) * 1e3, 2)}
+        extra["launch_floor"] = floors
+
+        # ---- pointer churn: every call brings a new set of gradient pointers
+        # (as when gradients are allocated afresh each backward), cycling
+        # through more sets than the library's 16-entry table cache (which
+        # only units of more than 960 parameters use: smaller pointer sets
+        # travel in the launch arguments)
+        n_churn = 20
+        churn = [fp.prepare_grads(plan, [B.to_dev(a, t.grad_dtype) for a, t in zip(grads_h, w.tensors)])
+                 for _ in range(n_churn)]
+        outs0 = sets[0][1]
+        for i in range(2 * n_churn):                # warm: every slot holds one of these sets
+            for bi in range(nb):
+                fp.pack_reduce_scatter_input(plan, bi, churn[i % n_churn], outs0[bi], stream)
+        torch.cuda.synchronize()
+        cnt0 = fp.counters()
+        e_ch = [[(new_event(), new_event()) for _ in range(nb)] for _ in range(K)]
+        host = []
+        torch.cuda.synchronize()
+        t_ch = time.perf_counter()
+        for i in range(K):
+            for bi in range(nb):
+                fp.time_next_launch(*e_ch[i][bi])
+                h0 = time.perf_counter()
+                fp.pack_reduce_scatter_input(plan, bi, churn[(i + 2 * n_churn) % n_churn], outs0[bi], stream)
+                host.append(time.perf_counter() - h0)
+        torch.cuda.synchronize()
+        churn_wall = (time.perf_counter() - t_ch) * 1e3 / K
+        cnt1 = fp.counters()
+        churn_pack = sum(a.elapsed_time(b) for e in e_ch for a, b in e) / K
+        # the same calls queued behind ~2 ms of GPU work: a replacement never
+        # waits for the device, so 16 calls return long before that work ends
+        a_mm = torch.randn(4096, 4096, device=dev, dtype=torch.bfloat16)
+        b_mm = torch.randn(4096, 4096, device=dev, dtype=torch.bfloat16)
+        torch.mm(a_mm, b_mm)                        # (loads the GEMM's code before the timed part)
+        for i in range(n_churn):                    # slots refilled before the busy work
+            for bi in range(nb):
+                fp.pack_reduce_scatter_input(plan, bi, churn[i], outs0[bi], stream)
+        torch.cuda.synchronize()
+        busy0, busy1 = new_event(), new_event()
+        busy0.record(stream)
+        for _ in range(16):
+            torch.mm(a_mm, b_mm)
+        busy1.record(stream)
+        h0 = time.perf_counter()
+        for i in range(16):
+            for bi in range(nb):
+                fp.pack_reduce_scatter_input(plan, bi, churn[i], outs0[bi], stream)
+        host_behind_busy = (time.perf_counter() - h0) * 1e3
+        torch.cuda.synchronize()
+        extra["pointer_churn"] = {
+            "sets": n_churn, "table_slots": 16,
+            "pack_kernel_ms": round(churn_pack, 5),
+            "ms_per_pack_with_upload": round(churn_wall, 5),
+            "host_us_per_call_p50": round(median(host) * 1e6, 1),
+            "inline_pointer_launches": cnt1[6] - cnt0[6],
+            "table_uploads": cnt1[1] - cnt0[1], "table_replacements": cnt1[4] - cnt0[4],
+            "cross_stream_waits": cnt1[5] - cnt0[5],
+            "host_ms_for_16_calls_behind_busy_gpu": round(host_behind_busy, 3),
+            "busy_gpu_ms": round(busy0.elapsed_time(busy1), 3),
+            "device_synchronizations": 0,
+        }
+        del churn, a_mm, b_mm
 
         # ---- pack under concurrent load: packs on a side stream (default
         # priority) while a stream of bf16 GEMMs keeps the GPU busy, as FSDP
@@ -405,7 +659,7 @@ def main():
     traffic = None
     try:
         with open(TRAFFIC_SUMMARY) as f:
-            summ = json.load(f).get(args.workload)
+            summ = json.load(f).get(args.workload + ("_flat" if args.flat else ""))
         # counter figures only stand while the kernel they were taken on does;
         # a layout with several buckets has them per bucket
         if summ and summ.get("kernel_source_sha256_16") == kernel_source_hash():
@@ -416,44 +670,59 @@ def main():
         pass
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": "window_kernel<pack>", "bytes_per_launch": pack_bytes[dom]}
+                "kernel": "pack_kernel", "bytes_per_launch": pack_bytes[dom]}
 
-    # ---- CPU baseline: the oracle, as it stands, on a bounded sample of the same pack
+    # ---- the pack of both target layouts, measured in this run
+    targets = None
+    if not args.flat and not args.pack_only and not args.no_targets:
+        targets = {}
+        for name in TARGET_WORKLOADS:
+            if name == args.workload:
+                targets[name] = {"ms_per_pack": round(pack_total_ms, 5), "pack_bytes": sum(pack_bytes),
+                                 "GBps": round(pack_gbps, 1), "frac_of_peak": roofline["frac"],
+                                 "ms_p10_p50_p90": [round(pct(per_step, q), 5) for q in (0.1, 0.5, 0.9)],
+                                 "buckets": nb, "rotated_sets": R}
+            else:
+                targets[name] = pack_target(B, name, K, args.warmup, args.rotate_bytes)
+            targets[name]["meets_80pct"] = targets[name]["frac_of_peak"] >= 0.80
+
+    # ---- CPU baseline: the oracle, as it stands, on the same pack
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        ref = oracle.plan(w.descs(), W)
-        reps, t_cpu = 0, 0.0
-        t_start = time.perf_counter()
-        packed_h = [None] * nb
-        while reps == 0 or (time.perf_counter() - t_start) < args.cpu_seconds:
-            ta = time.perf_counter()
-            for bi in range(nb):
-                packed_h[bi] = oracle.pack(ref, bi, grads_h)
-            t_cpu += time.perf_counter() - ta
-            reps += 1
-        cpu_gbps = reps * sum(pack_bytes) / t_cpu / 1e9
-        cpu_model = None
-        try:
-            with open("/proc/cpuinfo") as f:
-                cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
-        except OSError:
-            pass
-        cpu = {"value": round(cpu_gbps, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "host_cores_available": len(os.sched_getaffinity(0)), "cpu_model": cpu_model,
-               "sample": f"oracle pack of every bucket of {args.workload}, full size, repeated {reps}x "
-                         f"({t_cpu:.1f} s, single thread); GB/s under the same byte model",
-               "ms_per_pack": round(t_cpu / reps * 1e3, 2)}
-        if "rs_copy_out" in extra:
-            # the oracle's write-back of rank 0 beside the kernel's, same byte model
-            reps_w, t_w = 0, 0.0
-            while reps_w == 0 or t_w < min(args.cpu_seconds, 3.0):
-                ta = time.perf_counter()
-                for bi in range(nb):
-                    oracle.rs_copy_out(ref, bi, 0, packed_h[bi][0], float(W))
-                t_w += time.perf_counter() - ta
-                reps_w += 1
-            extra["rs_copy_out"]["cpu_oracle_GBps"] = round(reps_w * extra["rs_copy_out"]["bytes"] / t_w / 1e9, 3)
+        ref = oracle.plan(w.descs(), W) if not args.flat else None
+        if ref is not None:
+            cores = len(os.sched_getaffinity(0))
+            single, packed_h = cpu_oracle_pack(ref, grads_h, 1, args.cpu_seconds)
+            multi, packed_m = cpu_oracle_pack(ref, grads_h, cores, args.cpu_seconds)
+            # the parallel run computes the same bytes as the single-thread run
+            for a_, b_ in zip(packed_h, packed_m):
+                if a_.tobytes() != b_.tobytes():
+                    raise SystemExit("bench.py: the oracle's pack on several threads differs from one thread")
+            cpu_model = None
+            try:
+                with open("/proc/cpuinfo") as f:
+                    cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+            except OSError:
+                pass
+            ms_1, ms_n = median(single) * 1e3, median(multi) * 1e3
+            cpu = {"value": round(sum(pack_bytes) / (ms_n * 1e-3) / 1e9, 3), "unit": "GB/s", "cores": cores,
+                   "kind": "oracle", "cpu_model": cpu_model, "ms_per_pack": round(ms_n, 3),
+                   "single_thread": {"value": round(sum(pack_bytes) / (ms_1 * 1e-3) / 1e9, 3), "unit": "GB/s",
+                                     "ms_per_pack": round(ms_1, 3), "samples": len(single)},
+                   "sample": f"the oracle's pack of every bucket of {args.workload}, full size; median of "
+                             f"{len(multi)} packs on {cores} threads (one task per member and block of ranks) and of "
+                             f"{len(single)} on one thread, each after one warm-up; GB/s under the same byte model"}
+            if "rs_copy_out" in extra:
+                # the oracle's write-back of rank 0 beside the kernel's, same byte model (one thread)
+                reps_w, t_w = 0, 0.0
+                while reps_w == 0 or t_w < 1.0:
+                    ta = time.perf_counter()
+                    for bi in range(nb):
+                        oracle.rs_copy_out(ref, bi, 0, packed_h[bi][0], float(W))
+                    t_w += time.perf_counter() - ta
+                    reps_w += 1
+                extra["rs_copy_out"]["cpu_oracle_GBps"] = round(reps_w * extra["rs_copy_out"]["bytes"] / t_w / 1e9, 3)
 
     out = {
         "metric": METRIC,
@@ -463,6 +732,7 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "ms_per_pack": round(pack_total_ms, 5),
         "ms_per_step_with_kernel_events": round(ms_per_step_instrumented, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -476,6 +746,7 @@ def main():
                    "rotated_sets": R},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "targets": targets,
         "pack_ms": round(pack_total_ms, 5),
         "pack_GBps": round(pack_gbps, 1),
         "pack_frac_of_peak": round(pack_gbps / HBM_PEAK_GBPS, 4),

@@ -79,10 +79,12 @@ def lib():
         L.fsdppack_last_error.restype = ctypes.c_char_p
         L.fsdppack_counters.argtypes = [P_i64, i32]
         L.fsdppack_time_next_launch.argtypes = [vp, vp]
+        L.fsdppack_empty_launch.argtypes = [i32, i32, vp]
         for f in (L.fsdppack_plan_buckets, L.fsdppack_plan_buckets_flat, L.fsdppack_plan_info, L.fsdppack_plan_bucket,
                   L.fsdppack_plan_all_gather_layout, L.fsdppack_pack_reduce_scatter_input,
                   L.fsdppack_all_gather_copy_in, L.fsdppack_all_gather_copy_out,
-                  L.fsdppack_reduce_scatter_copy_out, L.fsdppack_counters, L.fsdppack_time_next_launch):
+                  L.fsdppack_reduce_scatter_copy_out, L.fsdppack_counters, L.fsdppack_time_next_launch,
+                  L.fsdppack_empty_launch):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -372,7 +374,15 @@ def time_next_launch(start, stop):
 
 
 def counters():
-    """(kernel launches, pointer-table uploads, pointer-table reuses, plan uploads)."""
-    c = (ctypes.c_int64 * 4)()
-    _check(lib().fsdppack_counters(c, 4))
+    """(kernel launches, pointer-table uploads, pointer-table reuses, plan
+    uploads, pointer tables replaced by a new set, cross-stream waits at such a
+    replacement, launches whose pointers travelled in the launch arguments)."""
+    c = (ctypes.c_int64 * 7)()
+    _check(lib().fsdppack_counters(c, 7))
     return tuple(c)
+
+
+def empty_launch(workgroups: int, threads: int = 64, stream=None):
+    """Launch a kernel that does nothing with the given grid (the floor of a
+    launch of that many workgroups; a measurement aid)."""
+    _check(lib().fsdppack_empty_launch(int(workgroups), int(threads), _stream(stream)))

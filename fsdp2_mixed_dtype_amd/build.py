@@ -27,6 +27,10 @@ def command(out: str = LIB) -> list:
             "-Wall", "-Wextra", "-Wno-unused-parameter",
             # no packed-fp32 instructions in device code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # the pack kernel's six leading scalar arguments (its direct test's
+            # inputs) are placed in scalar registers before each wave starts
+            # (with a fallback that loads them on firmware without preloading)
+            "-mllvm", "-amdgpu-kernarg-preload-count=6",
             "-I", os.path.join(HERE, "..", "include"),
             *[os.path.join(CSRC, s) for s in SOURCES], "-o", out]
 

@@ -25,8 +25,8 @@ thread_local std::string g_error;
 thread_local void *g_next_start = nullptr;   // events for the next launch on this thread
 thread_local void *g_next_stop = nullptr;
 // launches, table uploads, table reuses, plan uploads, table evictions,
-// cross-stream waits at an eviction
-constexpr int kCounters = 6;
+// cross-stream waits at an eviction, launches with their pointers inline
+constexpr int kCounters = 7;
 std::atomic<int64_t> g_counters[kCounters];
 
 int fail(int code, const std::string &msg)
@@ -68,6 +68,12 @@ int upload_table(OpTable &op)
         if ((e = hipMemcpy(op.d_columns, op.columns.data(), cbytes, hipMemcpyHostToDevice)) != hipSuccess)
             return hip_fail(e, "hipMemcpy(column map)");
     }
+    const size_t sbytes = op.stretches.size() * sizeof(PackStretch);
+    if (sbytes) {
+        if ((e = hipMalloc(&op.d_stretches, sbytes)) != hipSuccess) return hip_fail(e, "hipMalloc(stretch records)");
+        if ((e = hipMemcpy(op.d_stretches, op.stretches.data(), sbytes, hipMemcpyHostToDevice)) != hipSuccess)
+            return hip_fail(e, "hipMemcpy(stretch records)");
+    }
     return FSDPPACK_OK;
 }
 
@@ -97,10 +103,9 @@ int ensure_device(fsdppack_plan *p)
     return FSDPPACK_OK;
 }
 
-// Find or stage the device table for pointer set `key` in cache `c` (for a
-// narrow pack, the stretch records built from the pointers, then the
-// pointers), ordered before work enqueued next on `stream`.  Caller holds
-// plan->mu.
+// Find or stage the device table for pointer set `key` (more than
+// kInlineLarge pointers) in cache `c`, ordered before work enqueued next on
+// `stream`.  Caller holds plan->mu.
 //
 // Replacing a cached table needs no device-wide synchronisation:
 //  * the slot's previous upload read its pinned staging buffer, so that one
@@ -110,8 +115,7 @@ int ensure_device(fsdppack_plan *p)
 //    upload in stream order, and those on any other stream that used the slot
 //    are waited for on the device (an event recorded on that stream now,
 //    waited on by `stream`).
-int acquire_table(const OpTable &op, PtrCache &c, const std::vector<uint64_t> &key, hipStream_t stream,
-                  PtrSlot **out)
+int acquire_table(PtrCache &c, const std::vector<uint64_t> &key, hipStream_t stream, PtrSlot **out)
 {
     hipError_t e;
     for (PtrSlot &s : c.slots) {
@@ -157,7 +161,7 @@ int acquire_table(const OpTable &op, PtrCache &c, const std::vector<uint64_t> &k
         victim->live = false;
         g_counters[4]++;
     }
-    const size_t bytes = static_cast<size_t>(op.table_bytes(key.size()));
+    const size_t bytes = key.size() * sizeof(uint64_t);
     if (victim->d_table == nullptr) {
         if ((e = hipMalloc(reinterpret_cast<void **>(&victim->d_table), bytes)) != hipSuccess) return hip_fail(e, "hipMalloc(pointer table)");
         if ((e = hipHostMalloc(reinterpret_cast<void **>(&victim->h_stage), bytes, hipHostMallocDefault)) != hipSuccess) return hip_fail(e, "hipHostMalloc(pointer table)");
@@ -165,9 +169,7 @@ int acquire_table(const OpTable &op, PtrCache &c, const std::vector<uint64_t> &k
         if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) return hip_fail(e, "hipEventCreate");
         victim->ready = ev;
     }
-    const int64_t ns = op.stretch_count();
-    if (ns > 0) build_pack_stretches(op, key.data(), reinterpret_cast<PackStretch *>(victim->h_stage));
-    std::memcpy(victim->h_stage + ns * static_cast<int64_t>(sizeof(PackStretch) / 8), key.data(), key.size() * 8);
+    std::memcpy(victim->h_stage, key.data(), bytes);
     if ((e = hipMemcpyAsync(victim->d_table, victim->h_stage, bytes, hipMemcpyHostToDevice, stream)) != hipSuccess)
         return hip_fail(e, "hipMemcpyAsync(pointer table)");
     if ((e = hipEventRecord(static_cast<hipEvent_t>(victim->ready), stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -180,7 +182,8 @@ int acquire_table(const OpTable &op, PtrCache &c, const std::vector<uint64_t> &k
     return FSDPPACK_OK;
 }
 
-// Run one operation: pointer-table lookup, then one kernel launch.
+// Run one operation: one kernel launch, its pointer table in the launch's
+// arguments (up to kInlineLarge entries) or in a cached device table.
 int run_op(fsdppack_plan *p, const OpTable &op, size_t cache_index, const std::vector<uint64_t> &key, char *base,
            void *stream, const char *what, int32_t rank = 0, float divisor = 1.0f)
 {
@@ -194,17 +197,20 @@ int run_op(fsdppack_plan *p, const OpTable &op, size_t cache_index, const std::v
     std::lock_guard<std::mutex> lock(p->mu);
     if (int rc = ensure_device(p)) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    PtrSlot *slot = nullptr;
-    if (int rc = acquire_table(op, p->caches[cache_index], key, s, &slot)) return rc;
     WindowArgs args = op.args(true, shift);
-
-    const int64_t ns = op.stretch_count();
-    args.stretches = ns > 0 ? reinterpret_cast<const PackStretch *>(slot->d_table) : nullptr;
-    args.table = slot->d_table + ns * static_cast<int64_t>(sizeof(PackStretch) / 8);
+    const uint64_t *inline_ptrs = nullptr;
+    if (key.size() <= static_cast<size_t>(kInlineLarge)) {
+        inline_ptrs = key.data();                    // the kernel reads them from its arguments
+        g_counters[6]++;
+    } else {
+        PtrSlot *slot = nullptr;
+        if (int rc = acquire_table(p->caches[cache_index], key, s, &slot)) return rc;
+        args.table = slot->d_table;
+    }
     args.base = base;
     args.rank = rank;
     args.divisor = divisor;
-    const int le = launch_windows(args, stream, ev0, ev1);
+    const int le = launch_windows(args, inline_ptrs, static_cast<int32_t>(key.size()), stream, ev0, ev1);
     if (le != 0) return hip_fail(static_cast<hipError_t>(le), what);
     g_counters[0]++;
     if (trace_on())
@@ -444,8 +450,10 @@ void fsdppack_plan_destroy(fsdppack_plan *plan)
         auto free_table = [](OpTable &op) {
             if (op.d_members) (void)hipFree(op.d_members);
             if (op.d_columns) (void)hipFree(op.d_columns);
+            if (op.d_stretches) (void)hipFree(op.d_stretches);
             op.d_members = nullptr;
             op.d_columns = nullptr;
+            op.d_stretches = nullptr;
         };
         for (BucketPlan &b : plan->buckets) {
             free_table(b.pack);
@@ -464,6 +472,19 @@ int fsdppack_time_next_launch(void *start_event, void *stop_event)
 {
     g_next_start = start_event;
     g_next_stop = stop_event;
+    return FSDPPACK_OK;
+}
+
+int fsdppack_empty_launch(int32_t workgroups, int32_t threads, void *stream)
+{
+    void *ev0 = g_next_start, *ev1 = g_next_stop;
+    g_next_start = g_next_stop = nullptr;
+    if (workgroups < 1 || threads < 64 || threads > 1024 || threads % 64 != 0 ||
+        static_cast<int64_t>(workgroups) * threads >= (int64_t{1} << 32))
+        return fail(FSDPPACK_EINVAL, "empty_launch: workgroups must be >= 1 and threads a multiple of 64 in [64, 1024], "
+                                     "fewer than 2^32 work-items in all");
+    const int le = launch_empty(workgroups, threads, stream, ev0, ev1);
+    if (le != 0) return hip_fail(static_cast<hipError_t>(le), "empty_launch");
     return FSDPPACK_OK;
 }
 

@@ -138,21 +138,21 @@ struct FlatMember {
 };
 static_assert(sizeof(FlatMember) == 32, "shared with the device");
 
-// One candidate member of a pack stretch, with the member's gradient pointer
-// folded in (these records are rebuilt for every pointer set).  Column
-// offsets and counts are 32-bit: stretch records are only built for buckets
-// whose rows hold fewer than 2^31 bytes and whose members' rank chunks
-// hold fewer than 2^32 source bytes (pack_narrow).
-//   source of row r, column c (O <= c < OP):  base + r*Pss + c*size(dt)
+// One candidate member of a pack stretch.  Column offsets and counts are
+// 32-bit: stretch records are only built for buckets whose rows hold fewer
+// than 2^31 bytes and whose members' rank chunks hold fewer than 2^32 source
+// bytes (pack_narrow).
+//   source of row r, column c (O <= c < OP):  table[m] + r*Pss + (c - O)*size(dt)
 //   row r's real columns: [O, OP) for r < full, [O, OT) for r == full, none after
 struct PackCand {
-    uint64_t base;           // gradient address - O*size(dt), modulo 2^64
+    uint32_t m;              // the member (its entry of the pointer table)
     uint32_t Pss;            // P*size(dt): source bytes between consecutive rank chunks
     uint32_t O;              // first column
     uint32_t OP;             // O + P
     uint32_t full;           // ranks whose chunk is all real: numel / P
     uint32_t OT;             // O + numel - full*P
     uint32_t dt;             // source dtype; 0 = no candidate
+    uint32_t reserved;
 };
 static_assert(sizeof(PackCand) == 32, "shared with the device");
 
@@ -189,6 +189,13 @@ struct WindowArgs {
     char *base;              // the call's packed buffer or row (destination or source)
     const PackStretch *stretches;   // pack: one record per map stretch (null: no direct windows)
 };
+
+// Pointer tables of up to this many entries travel in the launch's own
+// arguments (the kernel argument segment: no upload, no device memory, nothing
+// cached), in two sizes so that small units copy few argument bytes; larger
+// tables go through a device table.
+constexpr int kInlineSmall = 64;
+constexpr int kInlineLarge = 960;
 
 // One contiguous range for the copy primitive: elements [lo, hi) of a chunk
 // whose element 0 sits at byte src_off of its source and dst_off of its
@@ -388,20 +395,20 @@ FSDPPACK_HD inline bool pack_direct(const WindowArgs &a, int32_t w, DirectWindow
 }
 
 // Whether window k of row r is a direct window according to the stretch
-// records (a.stretches, built for the call's pointer set by
-// build_pack_stretches): one whole window inside one member's rank chunk,
-// every element real.  One scalar load of 64 bytes (the stretch record of
-// the window's last byte) stands between the launch arguments and the data;
-// the index arithmetic is 32-bit (rows of fewer than 2^31 bytes).  Fills `d`
+// records (a.stretches, built with the plan by build_pack_stretches): one
+// whole window inside one member's rank chunk, every element real.  One
+// scalar load of 64 bytes (the stretch record of the window's last byte),
+// then the member's pointer, stand between the launch arguments and the
+// data; the index arithmetic is 32-bit (rows of fewer than 2^31 bytes).  Fills `d`
 // as pack_direct does; the window then equals the single range
 // pack_window_rk produces for it.
 // (The launch's fields the test reads are passed one by one: the kernel takes
 // them as leading scalar arguments, which the hardware can place in scalar
-// registers before the wave starts.)  rb: row bytes; lg: log2 of the
-// reduction dtype's size.
-FSDPPACK_HD inline bool pack_direct_stretch_s(const PackStretch *stretches, uint32_t rb, uint32_t shift,
-                                              uint32_t map_lg, uint32_t lg, int32_t reduce_dt, int32_t r, int32_t k,
-                                              DirectWindow &d)
+// registers before the wave starts.)  table: the pointer table; rb: row
+// bytes; lg: log2 of the reduction dtype's size.
+FSDPPACK_HD inline bool pack_direct_stretch_s(const PackStretch *stretches, const uint64_t *table, uint32_t rb,
+                                              uint32_t shift, uint32_t map_lg, uint32_t lg, int32_t reduce_dt,
+                                              int32_t r, int32_t k, DirectWindow &d)
 {
     const uint32_t s_r = (shift + static_cast<uint32_t>(r) * rb) & (kLineBytes - 1);
     const uint32_t kb = static_cast<uint32_t>(k) << kWindowLog2;
@@ -422,7 +429,12 @@ FSDPPACK_HD inline bool pack_direct_stretch_s(const PackStretch *stretches, uint
     const uint32_t ur = static_cast<uint32_t>(r);
     if (ur > c.full || (ur == c.full && c1 > c.OT)) return false;       // padding in the window
     const uint32_t ssz = c.dt == kBF16 ? 2u : 4u;
-    d.src = c.base + static_cast<uint64_t>(ur) * c.Pss + static_cast<uint64_t>(c0) * ssz;
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint64_t ptr = ((const FSDPPACK_TABLE uint64_t *)table)[c.m];
+#else
+    const uint64_t ptr = table ? table[c.m] : 0;
+#endif
+    d.src = ptr + static_cast<uint64_t>(ur) * c.Pss + static_cast<uint64_t>((c0 - c.O) * ssz);
     d.dst_off = static_cast<int64_t>(static_cast<uint64_t>(ur) * rb + y0);
     d.src_dt = static_cast<int32_t>(c.dt);
     d.dst_dt = reduce_dt;
@@ -433,7 +445,7 @@ FSDPPACK_HD inline bool pack_direct_stretch_s(const PackStretch *stretches, uint
 FSDPPACK_HD inline bool pack_direct_stretch(const WindowArgs &a, int32_t r, int32_t k, DirectWindow &d)
 {
     const uint32_t lg = a.reduce_dt == kBF16 ? 1u : 2u;
-    return pack_direct_stretch_s(a.stretches, static_cast<uint32_t>(a.S) << lg, static_cast<uint32_t>(a.shift),
+    return pack_direct_stretch_s(a.stretches, a.table, static_cast<uint32_t>(a.S) << lg, static_cast<uint32_t>(a.shift),
                                  static_cast<uint32_t>(a.map_lg), lg, a.reduce_dt, r, k, d);
 }
 
@@ -733,9 +745,16 @@ FSDPPACK_HD inline void for_each_range(const WindowArgs &a, int32_t w, F &&f)
     else flat_window<true>(a, w, f);
 }
 
-// Launch the window kernel on `stream`: one workgroup per window.
+// Launch the window kernel on `stream`: one workgroup per window.  With
+// `inline_ptrs` (n <= kInlineLarge entries) the pointer table travels in the
+// launch's arguments; otherwise args.table is a device table.
 // start_event / stop_event (hipEvent_t, may be NULL) are stamped at the
 // kernel's start and end.  Returns the hipError_t of the launch as an int.
-int launch_windows(const WindowArgs &args, void *stream, void *start_event, void *stop_event);
+int launch_windows(const WindowArgs &args, const uint64_t *inline_ptrs, int32_t n, void *stream, void *start_event,
+                   void *stop_event);
+
+// Launch a kernel that does nothing: `workgroups` workgroups of `threads`
+// threads (checked by the caller).
+int launch_empty(int32_t workgroups, int32_t threads, void *stream, void *start_event, void *stop_event);
 
 }  // namespace fsdppack

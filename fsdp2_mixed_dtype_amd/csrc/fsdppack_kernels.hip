@@ -559,18 +559,33 @@ __device__ __forceinline__ void copy_out_gather(const WindowArgs &a, const CopyO
 // the stretch records (or, in a bucket without them, the column map) show to
 // lie inside one member's rank chunk is copied directly; any other window
 // walks its ranges.
+// A launch's pointer table of up to N entries, passed by value: it lives in
+// the kernel argument segment, and the waves read its entries with scalar
+// loads straight from there.  N = 1: the table is a device table (a.table).
+template <int N> struct PtrTab {
+    uint64_t p[N];
+};
+
+template <int N>
+__device__ __forceinline__ void use_inline_table(WindowArgs &a, const PtrTab<N> &t)
+{
+    if constexpr (N > 1) a.table = (const uint64_t *)&t.p[0];
+}
+
 // The direct test's inputs come first, as scalar arguments (st: the stretch
 // records; rb: row bytes; meta: reduction dtype | log2 of its size << 8 |
 // group_lg << 16), so that they can be preloaded into scalar registers.
+template <int N>
 __global__ void __launch_bounds__(kPackBlock) pack_kernel(const PackStretch *st, uint32_t rb, uint32_t shift,
-                                                          uint32_t map_lg, uint32_t meta, WindowArgs a)
+                                                          uint32_t map_lg, uint32_t meta, WindowArgs a, PtrTab<N> t)
 {
+    use_inline_table(a, t);
     const uint32_t glg = meta >> 16, lg = (meta >> 8) & 0xFFu;
     const int32_t k = static_cast<int32_t>(blockIdx.x >> glg);
     const int32_t r = static_cast<int32_t>((blockIdx.y << glg) + (blockIdx.x & ((1u << glg) - 1)));
     DirectWindow d;
     if (st != nullptr) {
-        if (pack_direct_stretch_s(st, rb, shift, map_lg, lg, static_cast<int32_t>(meta & 0xFFu), r, k, d)) {
+        if (pack_direct_stretch_s(st, a.table, rb, shift, map_lg, lg, static_cast<int32_t>(meta & 0xFFu), r, k, d)) {
             run_direct<false, kPackBlock, kPackUnroll>(d, a.base);
             return;
         }
@@ -584,9 +599,10 @@ __global__ void __launch_bounds__(kPackBlock) pack_kernel(const PackStretch *st,
 
 // One workgroup per window; the window's ranges come from its index and the
 // plan's (cache-resident) record tables.
-template <int OP>
-__global__ void __launch_bounds__(kBlock) window_kernel(WindowArgs a)
+template <int OP, int N>
+__global__ void __launch_bounds__(kBlock) window_kernel(WindowArgs a, PtrTab<N> t)
 {
+    use_inline_table(a, t);
     const int32_t w = static_cast<int32_t>(blockIdx.x);
     auto body = [&](const RangeRef &g) { run_range<true, false>(g, a.base, 1.0f); };
     if constexpr (OP == kOpCopyIn) {
@@ -617,16 +633,29 @@ __global__ void __launch_bounds__(kBlock) window_kernel(WindowArgs a)
         write_back_window(a, w, body);
 }
 
+// A kernel that does nothing (the floor of a launch of its grid).
+__global__ void empty_kernel() {}
+
 }  // namespace
 
-int launch_windows(const WindowArgs &args, void *stream, void *start_event, void *stop_event)
+int launch_empty(int32_t workgroups, int32_t threads, void *stream, void *start_event, void *stop_event)
 {
-    if (args.n_windows <= 0) return static_cast<int>(hipSuccess);
+    hipExtLaunchKernelGGL(empty_kernel, dim3(static_cast<uint32_t>(workgroups)), dim3(static_cast<uint32_t>(threads)), 0,
+                          static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(start_event),
+                          static_cast<hipEvent_t>(stop_event), 0);
+    return static_cast<int>(hipGetLastError());
+}
+
+namespace {
+
+template <int N>
+int launch_sized(const WindowArgs &args, const uint64_t *inline_ptrs, int32_t n, hipStream_t st, hipEvent_t e0,
+                 hipEvent_t e1)
+{
+    PtrTab<N> t{};
+    if (N > 1)
+        for (int32_t i = 0; i < n; ++i) t.p[i] = inline_ptrs[i];
     const dim3 grid(static_cast<uint32_t>(args.n_windows)), block(kBlock);
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    hipEvent_t e0 = static_cast<hipEvent_t>(start_event), e1 = static_cast<hipEvent_t>(stop_event);
-    // hipExtLaunchKernelGGL: when events are given they are stamped by the
-    // dispatch itself, so they bracket exactly this kernel's execution
     if (args.op == kOpPack) {
         // x: the windows of a row group, y: the row groups
         const dim3 grid2(static_cast<uint32_t>((args.gx + 1) << args.group_lg),
@@ -634,15 +663,35 @@ int launch_windows(const WindowArgs &args, void *stream, void *start_event, void
         const uint32_t lg = args.reduce_dt == kBF16 ? 1u : 2u;
         const uint32_t rb = args.stretches ? static_cast<uint32_t>(args.S) << lg : 0u;
         const uint32_t meta = static_cast<uint32_t>(args.reduce_dt) | (lg << 8) | (static_cast<uint32_t>(args.group_lg) << 16);
-        hipExtLaunchKernelGGL(pack_kernel, grid2, dim3(kPackBlock), 0, st, e0, e1, 0, args.stretches, rb,
-                              static_cast<uint32_t>(args.shift), static_cast<uint32_t>(args.map_lg), meta, args);
-    } else if (args.op == kOpCopyIn) hipExtLaunchKernelGGL(window_kernel<kOpCopyIn>, grid, block, 0, st, e0, e1, 0, args);
-    else if (args.op == kOpCopyOut) hipExtLaunchKernelGGL(window_kernel<kOpCopyOut>, grid, block, 0, st, e0, e1, 0, args);
-    else if (args.op == kOpWriteBack) hipExtLaunchKernelGGL(window_kernel<kOpWriteBack>, grid, block, 0, st, e0, e1, 0, args);
-    else if (args.op == kOpWriteBackFlat)
-        hipExtLaunchKernelGGL(window_kernel<kOpWriteBackFlat>, grid, block, 0, st, e0, e1, 0, args);
-    else hipExtLaunchKernelGGL(window_kernel<kOpCopyInFlat>, grid, block, 0, st, e0, e1, 0, args);
+        hipExtLaunchKernelGGL(pack_kernel<N>, grid2, dim3(kPackBlock), 0, st, e0, e1, 0, args.stretches, rb,
+                              static_cast<uint32_t>(args.shift), static_cast<uint32_t>(args.map_lg), meta, args, t);
+    } else if (args.op == kOpCopyIn) {
+        hipExtLaunchKernelGGL(window_kernel<kOpCopyIn, N>, grid, block, 0, st, e0, e1, 0, args, t);
+    } else if (args.op == kOpCopyOut) {
+        hipExtLaunchKernelGGL(window_kernel<kOpCopyOut, N>, grid, block, 0, st, e0, e1, 0, args, t);
+    } else if (args.op == kOpWriteBack) {
+        hipExtLaunchKernelGGL(window_kernel<kOpWriteBack, N>, grid, block, 0, st, e0, e1, 0, args, t);
+    } else if (args.op == kOpWriteBackFlat) {
+        hipExtLaunchKernelGGL(window_kernel<kOpWriteBackFlat, N>, grid, block, 0, st, e0, e1, 0, args, t);
+    } else {
+        hipExtLaunchKernelGGL(window_kernel<kOpCopyInFlat, N>, grid, block, 0, st, e0, e1, 0, args, t);
+    }
     return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace
+
+int launch_windows(const WindowArgs &args, const uint64_t *inline_ptrs, int32_t n, void *stream, void *start_event,
+                   void *stop_event)
+{
+    if (args.n_windows <= 0) return static_cast<int>(hipSuccess);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipEvent_t e0 = static_cast<hipEvent_t>(start_event), e1 = static_cast<hipEvent_t>(stop_event);
+    // hipExtLaunchKernelGGL: when events are given they are stamped by the
+    // dispatch itself, so they bracket exactly this kernel's execution
+    if (inline_ptrs == nullptr) return launch_sized<1>(args, nullptr, 0, st, e0, e1);
+    if (n <= kInlineSmall) return launch_sized<kInlineSmall>(args, inline_ptrs, n, st, e0, e1);
+    return launch_sized<kInlineLarge>(args, inline_ptrs, n, st, e0, e1);
 }
 
 }  // namespace fsdppack

@@ -40,6 +40,14 @@ int64_t round_up16(int64_t x) { return (x + 15) / 16 * 16; }
 // Largest byte count any offset may reach; keeps every derived sum in range.
 constexpr int64_t kMaxBytes = INT64_MAX / 4;
 
+// Largest number of workgroups along one dimension of a launch.  A dispatch
+// counts its grid in work-items in 32 bits, so a dimension of 64-thread
+// workgroups holds fewer than 2^26 of them (each writing a 2 KiB window:
+// about 128 GiB per launch); the pack's rows are its second dimension.
+constexpr int64_t kMaxGridX = (int64_t{1} << 26) - 1;
+// Total workgroups of a launch (the kernels index windows in 32 bits).
+constexpr int64_t kMaxWindows = INT32_MAX;
+
 }  // namespace
 
 // Record map over positions [0, total) for records whose spans [b, e) tile
@@ -195,7 +203,6 @@ int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdp
 
     // ---- operation tables (members with nothing to move are left out, so
     // every lookup lands on a non-empty member)
-    const int64_t kMaxWindows = INT32_MAX;
     for (BucketPlan &b : plan->buckets) {
         // reduce-scatter pack: members in unit order along the columns of
         // every row
@@ -221,7 +228,10 @@ int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdp
             op.src_bytes += plan->numel[t] * dtype_bytes(m.src_dt);
         }
         const int64_t gx = (b.S * dsz + kWindowBytes - 1) / kWindowBytes;
-        if ((gx + 1) * W > kMaxWindows) { err = "plan_buckets: reduce-scatter buffer needs too many workgroups"; return FSDPPACK_EINVAL; }
+        if ((gx + 1) * W > kMaxWindows || (gx + 1) * 2 > kMaxGridX) {
+            err = "plan_buckets: reduce-scatter buffer needs too many workgroups";
+            return FSDPPACK_EINVAL;
+        }
         op.gx = static_cast<int32_t>(gx);
         op.dst_bytes = W * b.S * dsz;
         op.n_windows = static_cast<int32_t>(op.windows(0));
@@ -255,7 +265,7 @@ int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdp
             m.dt = plan->params[t].storage_dtype;
             wb.add(m);
             win += (bytes + kWindowBytes - 1) / kWindowBytes;
-            if (win > kMaxWindows) { err = "plan_buckets: sharded gradients need too many write-back workgroups"; return FSDPPACK_EINVAL; }
+            if (win > kMaxGridX) { err = "plan_buckets: sharded gradients need too many write-back workgroups"; return FSDPPACK_EINVAL; }
             wb.dst_bytes += bytes;
             wb.src_bytes += b.P[k] * dsz;
         }
@@ -267,6 +277,10 @@ int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdp
             return std::make_pair(mem[i].O, mem[i].O + mem[i].P);
         });
         op.narrow = pack_narrow(op, mem);
+        if (op.narrow) {
+            op.stretches.resize(op.columns.size());
+            build_pack_stretches(op, op.stretches.data());
+        }
     }
 
     {   // all-gather copy-in: each parameter owns bytes [A_t, A_{t+1}) of the
@@ -290,7 +304,7 @@ int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdp
             op.src_bytes += plan->P[t] * dtype_bytes(m.src_dt);
         }
         op.dst_bytes = plan->B;
-        if (op.windows(kLineBytes - 1) > kMaxWindows) { err = "plan_buckets: all-gather row needs too many workgroups"; return FSDPPACK_EINVAL; }
+        if (op.windows(kLineBytes - 1) > kMaxGridX) { err = "plan_buckets: all-gather row needs too many workgroups"; return FSDPPACK_EINVAL; }
         op.n_windows = static_cast<int32_t>(op.windows(0));
         // member map: the members each stretch of the row overlaps (the
         // members tile [0, B) in order)
@@ -317,7 +331,7 @@ int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdp
             m.dt = plan->params[t].param_dtype;
             op.add(m);
             win += (bytes + kWindowBytes - 1) / kWindowBytes;
-            if (win > kMaxWindows) { err = "plan_buckets: parameters need too many copy-out workgroups"; return FSDPPACK_EINVAL; }
+            if (win > kMaxGridX) { err = "plan_buckets: parameters need too many copy-out workgroups"; return FSDPPACK_EINVAL; }
             op.src_bytes += bytes;
         }
         op.n_windows = static_cast<int32_t>(win);
@@ -327,12 +341,12 @@ int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdp
     return FSDPPACK_OK;
 }
 
-void build_pack_stretches(const OpTable &op, const uint64_t *ptrs, PackStretch *out)
+void build_pack_stretches(const OpTable &op, PackStretch *out)
 {
     const PackMember *M = reinterpret_cast<const PackMember *>(op.members.data());
     const int lg = op.reduce_dt == kBF16 ? 1 : 2;
     const int64_t rb = op.S << lg, E = int64_t{1} << op.map_lg;
-    const int64_t nx = op.stretch_count();
+    const int64_t nx = static_cast<int64_t>(op.columns.size());
     int32_t first = 0;
     for (int64_t x = 0; x < nx; ++x) {
         // the columns of row bytes [x*E - window, (x+1)*E), clipped to the row:
@@ -348,7 +362,7 @@ void build_pack_stretches(const OpTable &op, const uint64_t *ptrs, PackStretch *
                 const PackMember &m = M[i];
                 const int64_t ssz = dtype_bytes(m.src_dt), full = m.numel / m.P;
                 PackCand &c = s.c[i - first];
-                c.base = ptrs[i] - static_cast<uint64_t>(m.O * ssz);
+                c.m = static_cast<uint32_t>(i);
                 c.Pss = static_cast<uint32_t>(m.P * ssz);
                 c.O = static_cast<uint32_t>(m.O);
                 c.OP = static_cast<uint32_t>(m.O + m.P);
@@ -407,7 +421,6 @@ int build_plan_flat(const fsdppack_param_desc *params, int32_t n, int32_t world,
     }
     fl.c = (fl.N + W - 1) / W;
     const int64_t bsz = dtype_bytes(rdt), psz = dtype_bytes(pdt);
-    const int64_t kMaxWindows = INT32_MAX;
 
     // introspection: one bucket whose members sit at flat offsets
     plan->buckets.emplace_back();
@@ -447,7 +460,7 @@ int build_plan_flat(const fsdppack_param_desc *params, int32_t n, int32_t world,
         if (!mem.empty()) mem.back().P += op.S - fl.N;
         for (const PackMember &m : mem) op.add(m);
         const int64_t gx = (op.S * bsz + kWindowBytes - 1) / kWindowBytes;
-        if (gx + 1 > kMaxWindows) { err = "plan_buckets_flat: reduce-scatter buffer needs too many workgroups"; return FSDPPACK_EINVAL; }
+        if (gx + 1 > kMaxGridX) { err = "plan_buckets_flat: reduce-scatter buffer needs too many workgroups"; return FSDPPACK_EINVAL; }
         op.gx = static_cast<int32_t>(gx);
         op.dst_bytes = op.S * bsz;
         op.n_windows = static_cast<int32_t>(op.windows(0));
@@ -455,6 +468,10 @@ int build_plan_flat(const fsdppack_param_desc *params, int32_t n, int32_t world,
             return std::make_pair(mem[i].O, mem[i].O + mem[i].P);
         });
         op.narrow = pack_narrow(op, mem);
+        if (op.narrow) {
+            op.stretches.resize(op.columns.size());
+            build_pack_stretches(op, op.stretches.data());
+        }
     }
 
     // write-back and copy-in: windows over a rank's row, records by flat offset
@@ -485,7 +502,7 @@ int build_plan_flat(const fsdppack_param_desc *params, int32_t n, int32_t world,
         // the copy-in's windows follow the lines of its destination row; the
         // write-back's row is its source, so its windows start at the row
         op.dst_bytes = copy_in ? row_bytes : 0;
-        if ((row_bytes + kLineBytes - 1 + kWindowBytes - 1) / kWindowBytes > kMaxWindows) {
+        if ((row_bytes + kLineBytes - 1 + kWindowBytes - 1) / kWindowBytes > kMaxGridX) {
             err = "plan_buckets_flat: a rank's row needs too many workgroups";
             return FSDPPACK_EINVAL;
         }
@@ -511,7 +528,7 @@ int build_plan_flat(const fsdppack_param_desc *params, int32_t n, int32_t world,
             m.dt = pdt;
             op.add(m);
             win += (bytes + kWindowBytes - 1) / kWindowBytes;
-            if (win > kMaxWindows) { err = "plan_buckets_flat: parameters need too many copy-out workgroups"; return FSDPPACK_EINVAL; }
+            if (win > kMaxGridX) { err = "plan_buckets_flat: parameters need too many copy-out workgroups"; return FSDPPACK_EINVAL; }
             op.src_bytes += bytes;
         }
         op.n_windows = static_cast<int32_t>(win);

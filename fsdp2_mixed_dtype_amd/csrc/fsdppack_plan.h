@@ -39,10 +39,12 @@ struct OpTable {
     int64_t dst_bytes = 0;                // bytes the operation writes
     int64_t src_bytes = 0;                // bytes it reads
     bool narrow = false;                  // pack: rows of fewer than 2^31 bytes and rank chunks of fewer
-                                          // than 2^32 source bytes, so every pointer set also gets stretch
-                                          // records (one per column-map entry) for the direct windows
+                                          // than 2^32 source bytes, so the plan holds stretch records
+                                          // (one per column-map entry) for the direct windows
+    std::vector<PackStretch> stretches;   // pack: the stretch records (narrow tables only)
     void *d_members = nullptr;            // device copies (owned by the plan)
     void *d_columns = nullptr;
+    void *d_stretches = nullptr;
 
     template <typename T> void add(const T &rec)
     {
@@ -62,14 +64,6 @@ struct OpTable {
         if (op == kOpPack) return (static_cast<int64_t>(gx) + 1) * (dst_bytes / (S * dtype_bytes(reduce_dt)));
         return (shift + dst_bytes + kWindowBytes - 1) >> kWindowLog2;
     }
-    // stretch records in a pointer set's device table (placed before its pointers)
-    int64_t stretch_count() const { return narrow ? static_cast<int64_t>(columns.size()) : 0; }
-    // bytes of a pointer set's device table: the stretch records, then one
-    // pointer per table entry
-    int64_t table_bytes(size_t entries) const
-    {
-        return stretch_count() * static_cast<int64_t>(sizeof(PackStretch)) + static_cast<int64_t>(entries) * 8;
-    }
     // launch arguments against host (`device == false`) or device members
     WindowArgs args(bool device, int32_t shift) const
     {
@@ -88,6 +82,7 @@ struct OpTable {
         a.B = B;
         a.members = device ? d_members : static_cast<const void *>(members.data());
         a.columns = device ? d_columns : static_cast<const void *>(columns.data());
+        a.stretches = narrow ? (device ? static_cast<const PackStretch *>(d_stretches) : stretches.data()) : nullptr;
         return a;
     }
 };
@@ -109,10 +104,11 @@ struct FlatLayout {
     std::vector<int64_t> F;
 };
 
-// Per-call pointer tables, cached on the device by content: the same grads /
-// shards / params pointers (the usual case from step to step) reuse an
-// uploaded table; a new set is staged through pinned host memory and copied
-// on the caller's stream.  A steady-state call records no event; a stream
+// Per-call pointer tables of more than kInlineLarge entries (smaller ones
+// travel in the launch's arguments), cached on the device by content: the
+// same grads / shards / params pointers (the usual case from step to step)
+// reuse an uploaded table; a new set is staged through pinned host memory and
+// copied on the caller's stream.  A steady-state call records no event; a stream
 // that first uses a slot uploaded on another stream waits once for the
 // upload.  Rewriting a slot for a new set waits on the host for the slot's
 // previous upload only, and on the device for the other streams that used it
@@ -173,10 +169,9 @@ int build_plan_flat(const fsdppack_param_desc *params, int32_t n, int32_t world,
 // layout) or the piece inside the rank's flat positions (flat layout).
 int64_t shard_elements(const fsdppack_plan &plan, int32_t t, int32_t r);
 
-// The stretch records of a narrow pack table for one pointer set (`ptrs`: the
-// gradients in member order, the pack's pointer-table order): for each
-// column-map stretch, the members overlapping its bytes extended one window to
-// the left, when there are one or two of them (else none).
-void build_pack_stretches(const OpTable &op, const uint64_t *ptrs, PackStretch *out);
+// The stretch records of a narrow pack table: for each column-map stretch,
+// the members overlapping its bytes extended one window to the left, when
+// there are one or two of them (else none).
+void build_pack_stretches(const OpTable &op, PackStretch *out);
 
 }  // namespace fsdppack

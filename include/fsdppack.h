@@ -54,12 +54,21 @@
  *    streams; its device tables are uploaded on the first compute call that
  *    needs them (a synchronous copy) on the device current at that time, and
  *    the plan may only be used on that device afterwards.
- *  - Per-call pointers reach the kernel through device tables cached by
- *    content, 16 per operation (per bucket for the pack).  A call with a new
- *    set of pointers uploads one asynchronously on `stream`; a 17th distinct
- *    set evicts the least recently used table after a device-wide
- *    synchronisation.  Calls with a known set record no event and upload
- *    nothing.
+ *  - Per-call pointer arrays of up to 960 entries travel to the kernel in its
+ *    own launch arguments: nothing is uploaded or cached, so a call with new
+ *    pointers (gradients allocated afresh every backward) costs the same as
+ *    one with known pointers.  Larger arrays reach the kernel through device
+ *    tables cached by content, 16 per operation (per bucket for the pack): a
+ *    call with a new set uploads one asynchronously on `stream`; a 17th
+ *    distinct set replaces the least recently used table, waiting on the host
+ *    for that table's own earlier upload only and making `stream` wait on the
+ *    device for work other streams had enqueued when they used it (no
+ *    device-wide synchronisation); calls with a known set record no event and
+ *    upload nothing.  A stream passed to a compute call must stay valid until
+ *    the plan is destroyed.
+ *  - A launch's grid is bounded by the hardware's 32-bit work-item counts:
+ *    the planner rejects (EINVAL) a unit whose launches would need more
+ *    workgroups (about 128 GiB written by one launch).
  */
 #ifndef FSDPPACK_H
 #define FSDPPACK_H
@@ -102,7 +111,10 @@ typedef struct fsdppack_param_desc {
 
 typedef struct fsdppack_plan fsdppack_plan;   /* opaque, library-owned */
 
-/* Plan one unit: bucket the n parameters by effective reduction dtype
+/* Plan one unit ("PyTorch adds per-parameter mixed precision to FSDP2",
+ * paragraph 2: one bucket, and one reduce-scatter, per effective reduction
+ * dtype; "The unit you wrapped", padding paragraphs: equal right-padded rank
+ * chunks): bucket the n parameters by effective reduction dtype
  * (reduce_dtype if set, else grad_dtype; buckets in order of first
  * appearance, members in unit order) and compute P, O, S per bucket and the
  * all-gather offsets A and row size B.  Host work only (no HIP call).
@@ -155,7 +167,12 @@ int fsdppack_plan_bucket(const fsdppack_plan *plan, int32_t bucket, int32_t *red
 int fsdppack_plan_all_gather_layout(const fsdppack_plan *plan, int64_t *B, const int64_t **P,
                                     const int64_t **A);
 
-/* Fused reduce-scatter pack of one bucket (the _chunk_cat.out-style op):
+/* Fused reduce-scatter pack of one bucket (the _chunk_cat.out-style op that
+ * "PyTorch adds per-parameter mixed precision to FSDP2" (ainewsletter.today),
+ * paragraphs 2-3, describes: gradients chunked, padded and cast in one pass
+ * into the bucket's reduction dtype, with no pre-cast temporaries; rank
+ * chunks and right-hand padding as in "The unit you wrapped", padding
+ * paragraphs):
  *   out[r*S + O_t + j] = cast(grads[t][r*P_t + j])  if r*P_t + j < numel_t,
  *                      = +0                          otherwise,
  * for every member t, rank r < W and j < P_t, cast = the member's grad dtype
@@ -168,7 +185,10 @@ int fsdppack_plan_all_gather_layout(const fsdppack_plan *plan, int64_t *B, const
 int fsdppack_pack_reduce_scatter_input(const fsdppack_plan *plan, int32_t bucket,
                                        const void *const *grads, void *out, void *stream);
 
-/* All-gather copy-in for rank `rank` (0 <= rank < W): row `rank` of ag_out
+/* All-gather copy-in ("PyTorch adds per-parameter mixed precision to FSDP2",
+ * paragraph 1: the copy-in casts each local shard to its target dtype and
+ * keeps a single all-gather per unit) for rank `rank` (0 <= rank < W): row
+ * `rank` of ag_out
  * (a device [W, B]-byte buffer) receives each parameter's padded local shard
  * cast from its storage dtype to its param dtype at byte A_t; the row's gap
  * bytes are written as zero, the other rows are not touched.  shards: n host
@@ -178,8 +198,10 @@ int fsdppack_pack_reduce_scatter_input(const fsdppack_plan *plan, int32_t bucket
 int fsdppack_all_gather_copy_in(const fsdppack_plan *plan, int32_t rank, const void *const *shards,
                                 void *ag_out, void *stream);
 
-/* All-gather copy-out: rebuild every full parameter from the gathered
- * [W, B]-byte buffer ag, dropping padding:
+/* All-gather copy-out ("The unit you wrapped": the layer's full shape only
+ * returns once the unit is gathered; the right-hand padding exists only for
+ * the even split and is dropped): rebuild every full parameter from the
+ * gathered [W, B]-byte buffer ag, dropping padding:
  *   params[t][r*P_t + j] = element j of parameter t's segment in row r,
  *   for j < min(P_t, numel_t - r*P_t).
  * params: n host entries of device pointers to numel_t elements each
@@ -219,17 +241,30 @@ void fsdppack_plan_destroy(fsdppack_plan *plan);
 /* Message of the last failed call on this thread ("" if none). */
 const char *fsdppack_last_error(void);
 
-/* Kernel timing: the next compute call made on this thread that launches a
- * kernel stamps `start_event` and `stop_event` (hipEvent_t, created by the
- * caller with timing enabled; either may be NULL) at that kernel's start and
- * end, so hipEventElapsedTime gives its exact execution time.  Applies to one
- * launch, then clears.  For benchmarks and profilers. */
+/* Kernel timing: the next compute call made on this thread stamps
+ * `start_event` and `stop_event` (hipEvent_t, created by the caller with
+ * timing enabled; either may be NULL) at its kernel's start and end, so
+ * hipEventElapsedTime gives that kernel's exact execution time.  The next
+ * compute call takes the events whether it launches or not: a call with
+ * nothing to write clears them without stamping them.  For benchmarks and
+ * profilers. */
 int fsdppack_time_next_launch(void *start_event, void *stop_event);
 
 /* Library-wide counters since load (for tests and tracing): counters[0] =
  * kernel launches, [1] = pointer-table uploads, [2] = pointer-table reuses,
- * [3] = plan device-table uploads.  n <= 4 entries are written. */
+ * [3] = plan device-table uploads, [4] = pointer tables replaced by a new set,
+ * [5] = cross-stream waits enqueued at such a replacement, [6] = launches
+ * whose pointers travelled in the launch arguments.  The first min(n, 7)
+ * entries are written. */
 int fsdppack_counters(int64_t *counters, int32_t n);
+
+/* Measurement aid: launch a kernel that does nothing, with `workgroups`
+ * workgroups of `threads` threads (1..1024, a multiple of 64) on `stream`.
+ * Its duration is the floor under which no launch of that grid can go (the
+ * dispatch of its workgroups and the launch's fixed cost), the yardstick for
+ * the small copy-in and write-back launches.  Errors: EINVAL (workgroups < 1,
+ * bad threads, or workgroups * threads >= 2^32), EHIP. */
+int fsdppack_empty_launch(int32_t workgroups, int32_t threads, void *stream);
 
 #ifdef __cplusplus
 }

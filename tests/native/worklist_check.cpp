@@ -126,18 +126,19 @@ static bool check_op(const char *name, const OpTable &op, int32_t W, int32_t shi
     CHECK((op.op != kOpCopyOut && op.op != kOpWriteBack) ||
               op.columns.size() == static_cast<size_t>((op.n_windows + (1 << kGroupLog2) - 1) >> kGroupLog2),
           "%s: group map size", name);
-    // stretch records of a narrow pack for a made-up pointer set: member m's
+    // a made-up pointer set for the pack's stretch-record test: member m's
     // gradient at 2^32 * (m + 1), plus one element for odd m (bf16 sources
     // then start 2 bytes past a dword)
     std::vector<uint64_t> ptrs(static_cast<size_t>(op.n));
-    std::vector<PackStretch> stretches(static_cast<size_t>(op.stretch_count()));
     if (op.op == kOpPack) {
         const PackMember *M = reinterpret_cast<const PackMember *>(op.members.data());
         for (int32_t m = 0; m < op.n; ++m)
             ptrs[m] = (static_cast<uint64_t>(m + 1) << 32) + ((m & 1) ? dtype_bytes(M[m].src_dt) : 0);
-        CHECK(op.narrow == (op.stretch_count() > 0) && (!op.narrow || op.stretch_count() == static_cast<int64_t>(op.columns.size())),
+        CHECK(op.stretches.size() == (op.narrow ? op.columns.size() : 0) && (a.stretches != nullptr) == op.narrow,
               "%s: stretch records", name);
-        if (op.narrow) build_pack_stretches(op, ptrs.data(), stretches.data());
+        for (const PackStretch &e : op.stretches)
+            for (const PackCand &c : e.c)
+                CHECK(c.dt == 0 || (c.m < static_cast<uint32_t>(op.n) && c.O < c.OP), "%s: stretch record", name);
     }
     for (int32_t w = 0; w < a.n_windows; ++w) {
         int ranges = 0;
@@ -179,7 +180,7 @@ static bool check_op(const char *name, const OpTable &op, int32_t W, int32_t shi
             // range of the walk, read from the member's own pointer
             if (op.narrow) {
                 WindowArgs as = a;
-                as.stretches = stretches.data();
+                as.table = ptrs.data();
                 DirectWindow ds{};
                 if (pack_direct_stretch(as, r, k, ds)) {
                     int n_rng = 0;

@@ -151,6 +151,33 @@ def test_planner_errors():
     empty.destroy()
 
 
+def test_planner_rejects_unlaunchable_grids():
+    """A launch counts its grid in 32-bit work-items: a unit whose pack, copy-in,
+    copy-out or write-back would need 2^26 or more 64-thread workgroups in one
+    dimension is rejected when planned, not at launch."""
+    big = 1 << 35                       # fp32 elements: 2^26 windows of 2 KiB for the copy-out
+    for W in (1, 8):
+        for flat in (False, True):
+            fn = fp.plan_buckets_flat if flat else fp.plan_buckets
+            with pytest.raises(fp.FsdpPackError) as e:
+                fn([(big, 1, FP32, 0, FP32, FP32)], W)
+            assert e.value.code == -1 and "too many" in str(e.value)
+    # a pack row of 2^26 windows with every other launch small enough
+    with pytest.raises(fp.FsdpPackError) as e:
+        fp.plan_buckets([(1 << 14, 1 << 21, BF16, FP32, BF16, BF16)], 1)
+    assert e.value.code == -1 and "reduce-scatter buffer" in str(e.value)
+    ok = fp.plan_buckets([(1 << 13, 1 << 20, BF16, 0, BF16, BF16)], 1)      # 2^34 bytes per launch: 2^23 windows
+    ok.destroy()
+
+
+def test_empty_launch_argument_errors():
+    L = fp.lib()
+    for wg, th in ((0, 64), (-1, 64), (1, 0), (1, 63), (1, 2048), (1 << 30, 1024), ((1 << 31) - 1, 64)):
+        assert L.fsdppack_empty_launch(wg, th, None) == -1, (wg, th)
+    assert "empty_launch" in L.fsdppack_last_error().decode()
+    assert fp.counters()[0] == 0
+
+
 def test_compute_call_argument_errors_before_any_gpu_work():
     # all of these are rejected on the host, so they run without a GPU
     import ctypes
