@@ -11,6 +11,7 @@ Functions (same names as the C ABI without the ``fsdppack_`` prefix):
   plan_buckets(params, world)                  -> Plan
   plan_buckets_flat(params, world)             -> Plan   (FSDP1 flat-parameter layout)
   pack_reduce_scatter_input(plan, bucket, grads, out, stream=None)
+  pack_reduce_scatter_input_noalloc(plan, bucket, grads, out, stream=None)   (allocates nothing)
   all_gather_copy_in(plan, rank, shards, ag_out, stream=None)
   all_gather_copy_out(plan, ag, params, stream=None)
   reduce_scatter_copy_out(plan, bucket, rank, rs_out, shard_grads, divide_factor=1.0, stream=None)
@@ -70,6 +71,7 @@ def lib():
         L.fsdppack_plan_bucket.argtypes = [vp, i32, P_i32, P_i64, P_i32, PP_i32, PP_i64, PP_i64]
         L.fsdppack_plan_all_gather_layout.argtypes = [vp, P_i64, PP_i64, PP_i64]
         L.fsdppack_pack_reduce_scatter_input.argtypes = [vp, i32, vp, vp, vp]
+        L.fsdppack_pack_reduce_scatter_input_noalloc.argtypes = [vp, i32, vp, vp, vp]
         L.fsdppack_all_gather_copy_in.argtypes = [vp, i32, vp, vp, vp]
         L.fsdppack_all_gather_copy_out.argtypes = [vp, vp, vp, vp]
         L.fsdppack_reduce_scatter_copy_out.argtypes = [vp, i32, i32, vp, ctypes.c_float, vp, vp]
@@ -82,6 +84,7 @@ def lib():
         L.fsdppack_empty_launch.argtypes = [i32, i32, vp]
         for f in (L.fsdppack_plan_buckets, L.fsdppack_plan_buckets_flat, L.fsdppack_plan_info, L.fsdppack_plan_bucket,
                   L.fsdppack_plan_all_gather_layout, L.fsdppack_pack_reduce_scatter_input,
+                  L.fsdppack_pack_reduce_scatter_input_noalloc,
                   L.fsdppack_all_gather_copy_in, L.fsdppack_all_gather_copy_out,
                   L.fsdppack_reduce_scatter_copy_out, L.fsdppack_counters, L.fsdppack_time_next_launch,
                   L.fsdppack_empty_launch):
@@ -280,6 +283,24 @@ def pack_reduce_scatter_input(plan: Plan, bucket: int, grads, out, stream=None):
                           for i, g in enumerate(grads)])
     optr = _ptr(out, b.dtype, plan.world * b.S, "out")
     _check(lib().fsdppack_pack_reduce_scatter_input(plan.handle, bucket, arr, optr, _stream(stream)))
+    return out
+
+
+def pack_reduce_scatter_input_noalloc(plan: Plan, bucket: int, grads, out, stream=None):
+    """pack_reduce_scatter_input for callers that cannot allocate device
+    memory: the bucket's tables go through the library's fixed device scratch
+    (shared by every such call on the GPU: overlapping calls race)."""
+    b = plan.buckets[bucket]
+    if isinstance(grads, PointerArray):
+        arr = _prepared(plan, grads, "grads", prepare_grads)
+    else:
+        members = set(b.members)
+        if len(grads) != plan.n:
+            raise ValueError(f"grads: expected {plan.n} entries, got {len(grads)}")
+        arr = _ptr_array([_ptr(g, plan.descs[i].grad_dtype, plan.numel[i], f"grads[{i}]") if i in members else 0
+                          for i, g in enumerate(grads)])
+    optr = _ptr(out, b.dtype, plan.world * b.S, "out")
+    _check(lib().fsdppack_pack_reduce_scatter_input_noalloc(plan.handle, bucket, arr, optr, _stream(stream)))
     return out
 
 

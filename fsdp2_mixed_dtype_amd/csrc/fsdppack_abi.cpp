@@ -323,6 +323,71 @@ int fsdppack_pack_reduce_scatter_input(const fsdppack_plan *cplan, int32_t bucke
     }
 }
 
+int fsdppack_pack_reduce_scatter_input_noalloc(const fsdppack_plan *cplan, int32_t bucket, const void *const *grads,
+                                               void *out, void *stream)
+{
+    void *ev0 = g_next_start, *ev1 = g_next_stop;
+    g_next_start = g_next_stop = nullptr;
+    const fsdppack_plan *plan = cplan;
+    if (!plan_ok(plan)) return fail(FSDPPACK_ESTATE, "pack_reduce_scatter_input_noalloc: invalid plan handle");
+    if (bucket < 0 || bucket >= static_cast<int32_t>(plan->buckets.size()))
+        return fail(FSDPPACK_EINVAL, "pack_reduce_scatter_input_noalloc: bucket index out of range");
+    if (grads == nullptr) return fail(FSDPPACK_EINVAL, "pack_reduce_scatter_input_noalloc: grads is NULL");
+    const BucketPlan &b = plan->buckets[bucket];
+    const OpTable &op = b.pack;
+    const int64_t dsz = dtype_bytes(b.dtype);
+    if (b.S > 0 && (out == nullptr || !aligned(out, dsz)))
+        return fail(FSDPPACK_EINVAL, "pack_reduce_scatter_input_noalloc: out is NULL or not aligned to its element size");
+    for (int32_t t : b.members) {
+        if (plan->numel[t] == 0) continue;
+        const void *g = grads[t];
+        if (g == nullptr || !aligned(g, dtype_bytes(plan->params[t].grad_dtype)))
+            return fail(FSDPPACK_EINVAL, "pack_reduce_scatter_input_noalloc: grads[" + std::to_string(t) +
+                                             "] is NULL or not aligned to its element size");
+    }
+    if (op.table_params.size() > static_cast<size_t>(kInlineLarge))
+        return fail(FSDPPACK_EINVAL, "pack_reduce_scatter_input_noalloc: the bucket has more than " +
+                                         std::to_string(kInlineLarge) + " members");
+    // the bucket's tables, each at a 256-byte boundary of the scratch
+    auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+    const int64_t mb = static_cast<int64_t>(op.members.size());
+    const int64_t cb = static_cast<int64_t>(op.columns.size() * sizeof(ColumnWindow));
+    const int64_t sb = static_cast<int64_t>(op.stretches.size() * sizeof(PackStretch));
+    const int64_t c_off = up(mb), s_off = c_off + up(cb);
+    if (s_off + sb > kScratchBytes)
+        return fail(FSDPPACK_EINVAL, "pack_reduce_scatter_input_noalloc: the bucket's tables need " +
+                                         std::to_string(s_off + sb) + " bytes, more than the " +
+                                         std::to_string(kScratchBytes) + "-byte scratch");
+    const int32_t shift = static_cast<int32_t>(reinterpret_cast<uintptr_t>(out) & (kLineBytes - 1));
+    if (op.windows(shift) <= 0) return FSDPPACK_OK;
+    void *sp = nullptr;
+    hipError_t e = static_cast<hipError_t>(scratch_address(&sp));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    char *base = static_cast<char *>(sp);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // the plan's host tables live as long as the plan, so the copies may
+    // complete after this call returns
+    if (mb && (e = hipMemcpyAsync(base, op.members.data(), mb, hipMemcpyHostToDevice, st)) != hipSuccess)
+        return hip_fail(e, "hipMemcpyAsync(member table to scratch)");
+    if (cb && (e = hipMemcpyAsync(base + c_off, op.columns.data(), cb, hipMemcpyHostToDevice, st)) != hipSuccess)
+        return hip_fail(e, "hipMemcpyAsync(column map to scratch)");
+    if (sb && (e = hipMemcpyAsync(base + s_off, op.stretches.data(), sb, hipMemcpyHostToDevice, st)) != hipSuccess)
+        return hip_fail(e, "hipMemcpyAsync(stretch records to scratch)");
+    WindowArgs args = op.args(false, shift);
+    args.members = base;
+    args.columns = base + c_off;
+    args.stretches = sb ? reinterpret_cast<const PackStretch *>(base + s_off) : nullptr;
+    args.table = nullptr;
+    args.base = static_cast<char *>(out);
+    std::vector<uint64_t> key(op.table_params.size());
+    for (size_t m = 0; m < key.size(); ++m) key[m] = reinterpret_cast<uint64_t>(grads[op.table_params[m]]);
+    const int le = launch_windows(args, key.data(), static_cast<int32_t>(key.size()), stream, ev0, ev1);
+    if (le != 0) return hip_fail(static_cast<hipError_t>(le), "pack_reduce_scatter_input_noalloc");
+    g_counters[0]++;
+    g_counters[6]++;
+    return FSDPPACK_OK;
+}
+
 int fsdppack_all_gather_copy_in(const fsdppack_plan *cplan, int32_t rank, const void *const *shards, void *ag_out,
                                 void *stream)
 {

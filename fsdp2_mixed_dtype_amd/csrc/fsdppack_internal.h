@@ -753,6 +753,15 @@ FSDPPACK_HD inline void for_each_range(const WindowArgs &a, int32_t w, F &&f)
 int launch_windows(const WindowArgs &args, const uint64_t *inline_ptrs, int32_t n, void *stream, void *start_event,
                    void *stop_event);
 
+// Bytes of the device scratch the allocation-free pack copies a bucket's
+// pack tables into, and the devices it serves.
+constexpr int64_t kScratchBytes = int64_t{1} << 20;
+constexpr int kMaxDevices = 64;
+
+// The address of the scratch on the current device (looked up once per
+// device).  Returns the hipError_t as an int.
+int scratch_address(void **out);
+
 // Launch a kernel that does nothing: `workgroups` workgroups of `threads`
 // threads (checked by the caller).
 int launch_empty(int32_t workgroups, int32_t threads, void *stream, void *start_event, void *stop_event);

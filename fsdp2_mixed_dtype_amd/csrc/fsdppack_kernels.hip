@@ -35,7 +35,16 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "fsdppack_internal.h"
+
+// Device scratch of the allocation-free pack (fsdppack_pack_reduce_scatter_
+// input_noalloc): the bucket's pack tables are copied here on every call
+// instead of living in memory the library allocates.  Each GPU holds its own
+// copy until the process ends; host code reaches it only through the address
+// scratch_address() looks up per device, never through this name.
+static __device__ __align__(256) unsigned char scratch[fsdppack::kScratchBytes];
 
 namespace fsdppack {
 namespace {
@@ -637,6 +646,25 @@ __global__ void __launch_bounds__(kBlock) window_kernel(WindowArgs a, PtrTab<N> 
 __global__ void empty_kernel() {}
 
 }  // namespace
+
+int scratch_address(void **out)
+{
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return static_cast<int>(e);
+    if (dev < 0 || dev >= kMaxDevices) return static_cast<int>(hipErrorInvalidDevice);
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return static_cast<int>(e);
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return static_cast<int>(hipSuccess);
+}
 
 int launch_empty(int32_t workgroups, int32_t threads, void *stream, void *start_event, void *stop_event)
 {

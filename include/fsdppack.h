@@ -185,6 +185,21 @@ int fsdppack_plan_all_gather_layout(const fsdppack_plan *plan, int64_t *B, const
 int fsdppack_pack_reduce_scatter_input(const fsdppack_plan *plan, int32_t bucket,
                                        const void *const *grads, void *out, void *stream);
 
+/* The same fused reduce-scatter pack, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): it allocates nothing.  The bucket's pack tables are
+ * copied (hipMemcpyAsync from the plan's host memory, on `stream`) into a
+ * library-owned device scratch of 1 MiB per GPU, held until the process
+ * ends, and the pointers travel in the launch arguments; the plan's own
+ * device tables are neither used nor created.  Same arguments, result and
+ * errors as fsdppack_pack_reduce_scatter_input, and also EINVAL when the
+ * bucket has more than 960 members or its tables exceed the scratch (about
+ * 13 000 column-map stretches).  Every call on a GPU shares that GPU's
+ * scratch: calls that overlap on one GPU (on different streams, or from
+ * different threads without ordering) race, so a caller orders them. */
+int fsdppack_pack_reduce_scatter_input_noalloc(const fsdppack_plan *plan, int32_t bucket,
+                                               const void *const *grads, void *out, void *stream);
+
 /* All-gather copy-in ("PyTorch adds per-parameter mixed precision to FSDP2",
  * paragraph 1: the copy-in casts each local shard to its target dtype and
  * keeps a single all-gather per unit) for rank `rank` (0 <= rank < W): row

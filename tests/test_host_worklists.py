@@ -170,6 +170,29 @@ def test_planner_rejects_unlaunchable_grids():
     ok.destroy()
 
 
+def test_no_alloc_pack_argument_errors_before_any_gpu_work():
+    import ctypes
+    L = fp.lib()
+    p = fp.plan_buckets([(4, 4, FP32, 0, FP32, BF16), (3, 1, BF16, 0, FP32, BF16)], 2)
+    ptrs = (ctypes.c_void_p * 2)(0x1000, 0x2002)
+    na = L.fsdppack_pack_reduce_scatter_input_noalloc
+    assert na(p.handle, 5, ptrs, 0x4000, None) == -1                     # bucket out of range
+    assert na(p.handle, 0, None, 0x4000, None) == -1                     # NULL array
+    assert na(p.handle, 0, ptrs, 0x4002, None) == -1                     # misaligned out
+    bad = (ctypes.c_void_p * 2)(0x1001, 0x2002)
+    assert na(p.handle, 0, bad, 0x4000, None) == -1                      # misaligned gradient
+    assert "grads[0]" in L.fsdppack_last_error().decode()
+    assert na(None, 0, ptrs, 0x4000, None) == -5
+    p.destroy()
+    k = 961                                                               # one more than the arguments carry
+    big = fp.plan_buckets([(2, 1, FP32, 0, FP32, FP32)] * k, 2)
+    many = (ctypes.c_void_p * k)(*([0x1000] * k))
+    assert na(big.handle, 0, many, 0x4000, None) == -1
+    assert "members" in L.fsdppack_last_error().decode()
+    big.destroy()
+    assert fp.counters()[0] == 0
+
+
 def test_empty_launch_argument_errors():
     L = fp.lib()
     for wg, th in ((0, 64), (-1, 64), (1, 0), (1, 63), (1, 2048), (1 << 30, 1024), ((1 << 31) - 1, 64)):

@@ -1,0 +1,82 @@
+"""The allocation-free pack (fsdppack_pack_reduce_scatter_input_noalloc) against
+the ordinary pack, byte for byte, through the C ABI: two calls in a row on
+the library's shared device scratch, the second with a smaller layout (so
+any table left from the first call must not leak into it), plus a bucket of
+fp32 gradients into bf16 and a plan that is never used by an allocating call
+(its device tables are never created)."""
+import numpy as np
+import pytest
+
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+import fsdp2_mixed_dtype_amd as fp  # noqa: E402
+
+DEV = torch.device("cuda:0")
+BF16, FP32 = 1, 2
+
+
+def _dev(a, dt, elem_offset=0):
+    a = np.ascontiguousarray(a).reshape(-1)
+    base = torch.empty(a.size + elem_offset, dtype=fp.TORCH_DTYPE[dt], device=DEV)
+    t = base[elem_offset:]
+    host = torch.from_numpy(a.copy())
+    t.copy_(host.view(torch.bfloat16) if dt == BF16 else host)
+    return t
+
+
+def _both(w, out_offset=0):
+    """Every bucket of layout w packed by the ordinary entry point (on one
+    plan) and by the allocation-free one (on a second plan of the same
+    layout); returns the byte arrays and the second plan's counter deltas."""
+    grads = wl.make_grads(w)
+    g_dev = [_dev(g, t.grad_dtype, i % 2) for i, (g, t) in enumerate(zip(grads, w.tensors))]
+    ref_plan = fp.plan_buckets(w.descs(), w.world)
+    na_plan = fp.plan_buckets(w.descs(), w.world)
+    pairs = []
+    for bi, b in enumerate(ref_plan.buckets):
+        n = w.world * b.S
+        a = torch.full((n + out_offset,), 7, dtype=fp.TORCH_DTYPE[b.dtype], device=DEV)[out_offset:]
+        fp.pack_reduce_scatter_input(ref_plan, bi, g_dev, a)
+        torch.cuda.synchronize()
+        c0 = fp.counters()
+        z = torch.full((n + out_offset,), 9, dtype=fp.TORCH_DTYPE[b.dtype], device=DEV)[out_offset:]
+        fp.pack_reduce_scatter_input_noalloc(na_plan, bi, g_dev, z)
+        torch.cuda.synchronize()
+        c1 = fp.counters()
+        pairs.append((a.view(torch.uint8).cpu().numpy(), z.view(torch.uint8).cpu().numpy(),
+                      [y - x for x, y in zip(c0, c1)]))
+    ref_plan.destroy()
+    na_plan.destroy()
+    return pairs
+
+
+def test_no_alloc_pack_matches_the_pack_twice_then_smaller():
+    layouts = [
+        ("mixed50m", wl.mixed50m(), 0),
+        # smaller: two buckets (bf16 and fp32 reduction), gradients of both dtypes, an odd output offset
+        ("small two-bucket", wl.custom([(4 * 1025, 3), (5,), (64, 2), (4 * 700, 8), (33, 7)],
+                                       [BF16, FP32, BF16, FP32, BF16], [FP32, BF16, FP32, BF16, 0], 4, seed=11), 1),
+        ("tiny", wl.tiny(), 0),
+    ]
+    for name, w, off in layouts:
+        print(f"[no-alloc] {name}", flush=True)
+        for bi, (a, z, dc) in enumerate(_both(w, off)):
+            assert np.array_equal(a, z), f"{name}: bucket {bi} differs from the ordinary pack"
+            assert dc[0] == 1                     # one launch ...
+            assert dc[1] == 0 and dc[3] == 0      # ... no pointer table and no plan table created
+
+
+def test_no_alloc_pack_rejects_what_it_cannot_hold():
+    k = 1000                                    # more members than the launch arguments carry
+    w = wl.custom([(3, 1)] * k, [FP32] * k, [FP32] * k, 2)
+    plan = fp.plan_buckets(w.descs(), w.world)
+    g = torch.zeros(3, device=DEV)
+    with pytest.raises(fp.FsdpPackError) as e:
+        fp.pack_reduce_scatter_input_noalloc(plan, 0, [g] * k, torch.empty(2 * plan.buckets[0].S, device=DEV))
+    assert e.value.code == -1 and "members" in str(e.value)
+    plan.destroy()
