@@ -489,6 +489,27 @@ def main():
                                 "GBps": round(wb_bytes / (wb_ms * 1e-3) / 1e9, 1),
                                 "frac_of_peak": round(wb_bytes / (wb_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                                 "rank": 0, "divide_factor": W, "buckets": nb}
+        if nb > 1:
+            # the same write-back, every bucket in one launch
+            asets = []
+            for r in range(R):
+                dsts = [None] * len(w.tensors)
+                for per in wsets[r]:
+                    for i, t in enumerate(per[1].tensors):
+                        if t is not None:
+                            dsts[i] = t
+                asets.append(([per[0] for per in wsets[r]], fp.prepare_shard_grads(plan, None, 0, dsts)))
+            e_a = [(new_event(), new_event()) for _ in range(K)]
+            for i in range(args.warmup + K):
+                rows_i, dsts = asets[i % R]
+                timed(e_a[i - args.warmup] if i >= args.warmup else None)
+                fp.reduce_scatter_copy_out_all(plan, 0, rows_i, dsts, float(W), stream)
+            torch.cuda.synchronize()
+            wb_all_ms = sum(a.elapsed_time(b) for a, b in e_a) / K
+            extra["rs_copy_out"]["all_buckets_one_launch"] = {
+                "ms": round(wb_all_ms, 5), "GBps": round(wb_bytes / (wb_all_ms * 1e-3) / 1e9, 1),
+                "frac_of_peak": round(wb_bytes / (wb_all_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+            del asets
         del wsets
 
         # ---- launch floor: each launch of the step against an empty kernel
@@ -513,6 +534,9 @@ def main():
         kernel_ms = {f"pack[{bi}]": pack_ms[bi] for bi in range(nb)}
         kernel_ms.update(copy_in=copy_in_ms, copy_out=copy_out_ms)
         kernel_ms.update({f"write_back[{bi}]": wb_ms_b[bi] for bi in range(nb)})
+        if nb > 1:
+            wg["write_back_all"] = sum(wg[f"write_back[{bi}]"] for bi in range(nb))
+            kernel_ms["write_back_all"] = wb_all_ms
         floors = {}
         for name, n in wg.items():
             f_ms = B.time_empty(n, K)
@@ -579,7 +603,7 @@ def main():
             "cross_stream_waits": cnt1[5] - cnt0[5],
             "host_ms_for_16_calls_behind_busy_gpu": round(host_behind_busy, 3),
             "busy_gpu_ms": round(busy0.elapsed_time(busy1), 3),
-            "device_synchronizations": 0,
+            "host_waits": cnt1[7] - cnt0[7],
         }
         del churn, a_mm, b_mm
 

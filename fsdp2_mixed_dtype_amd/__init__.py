@@ -75,6 +75,7 @@ def lib():
         L.fsdppack_all_gather_copy_in.argtypes = [vp, i32, vp, vp, vp]
         L.fsdppack_all_gather_copy_out.argtypes = [vp, vp, vp, vp]
         L.fsdppack_reduce_scatter_copy_out.argtypes = [vp, i32, i32, vp, ctypes.c_float, vp, vp]
+        L.fsdppack_reduce_scatter_copy_out_all.argtypes = [vp, i32, vp, ctypes.c_float, vp, vp]
         L.fsdppack_plan_destroy.argtypes = [vp]
         L.fsdppack_plan_destroy.restype = None
         L.fsdppack_last_error.argtypes = []
@@ -346,14 +347,18 @@ def valid_in_chunk(plan: Plan, index: int, rank: int) -> int:
     return max(0, min(P, plan.numel[index] - rank * P))
 
 
-def prepare_shard_grads(plan: Plan, bucket: int, rank: int, grads) -> PointerArray:
-    """Sharded gradients by parameter index for the write-back of `bucket` on
-    `rank`: each member's entry holds the rank chunk's real elements (storage
-    dtype); entries of non-members and of members with nothing on this rank
-    may be None."""
+def prepare_shard_grads(plan: Plan, bucket: int | None, rank: int, grads) -> PointerArray:
+    """Sharded gradients by parameter index for the write-back of `bucket`
+    (None: of every bucket, for reduce_scatter_copy_out_all) on `rank`: each
+    member's entry holds the rank chunk's real elements (storage dtype);
+    entries of non-members and of members with nothing on this rank may be
+    None."""
     if len(grads) != plan.n:
         raise ValueError(f"shard_grads: expected {plan.n} entries, got {len(grads)}")
-    members = set(plan.buckets[bucket].members)
+    if bucket is None:
+        members = {i for b in plan.buckets for i in b.members}
+    else:
+        members = set(plan.buckets[bucket].members)
     ptrs = []
     for i, g in enumerate(grads):
         v = valid_in_chunk(plan, i, rank)
@@ -387,6 +392,28 @@ def reduce_scatter_copy_out(plan: Plan, bucket: int, rank: int, rs_out, shard_gr
     return shard_grads
 
 
+def reduce_scatter_copy_out_all(plan: Plan, rank: int, rs_outs, shard_grads, divide_factor: float = 1.0,
+                                stream=None):
+    """The write-back of every bucket in one launch: for each bucket b, what
+    reduce_scatter_copy_out(plan, b, rank, rs_outs[b], ...) writes.  `rs_outs`
+    holds one reduced row per bucket (S_b elements of its reduction dtype);
+    `shard_grads` is indexed by parameter (prepare_shard_grads(plan, None,
+    rank, grads))."""
+    if len(rs_outs) != len(plan.buckets):
+        raise ValueError(f"rs_outs: expected {len(plan.buckets)} rows, got {len(rs_outs)}")
+    if isinstance(shard_grads, PointerArray):
+        if (shard_grads.kind != "shard_grads" or shard_grads.plan_handle != plan.handle.value
+                or shard_grads.bucket is not None or shard_grads.rank != rank):
+            raise ValueError("pointer array was prepared for another plan, bucket or rank")
+        arr = shard_grads.array
+    else:
+        arr = prepare_shard_grads(plan, None, rank, shard_grads).array
+    rows = _ptr_array([_ptr(r, b.dtype, b.S, f"rs_outs[{i}]") for i, (r, b) in enumerate(zip(rs_outs, plan.buckets))])
+    _check(lib().fsdppack_reduce_scatter_copy_out_all(plan.handle, int(rank), rows, float(divide_factor), arr,
+                                                      _stream(stream)))
+    return shard_grads
+
+
 def time_next_launch(start, stop):
     """Have the next compute call on this thread stamp two timing events
     (torch.cuda.Event(enable_timing=True), already recorded once so that they
@@ -397,9 +424,10 @@ def time_next_launch(start, stop):
 def counters():
     """(kernel launches, pointer-table uploads, pointer-table reuses, plan
     uploads, pointer tables replaced by a new set, cross-stream waits at such a
-    replacement, launches whose pointers travelled in the launch arguments)."""
-    c = (ctypes.c_int64 * 7)()
-    _check(lib().fsdppack_counters(c, 7))
+    replacement, launches whose pointers travelled in the launch arguments,
+    host waits for a replaced table's previous upload)."""
+    c = (ctypes.c_int64 * 8)()
+    _check(lib().fsdppack_counters(c, 8))
     return tuple(c)
 
 

@@ -26,7 +26,7 @@ thread_local void *g_next_start = nullptr;   // events for the next launch on th
 thread_local void *g_next_stop = nullptr;
 // launches, table uploads, table reuses, plan uploads, table evictions,
 // cross-stream waits at an eviction, launches with their pointers inline
-constexpr int kCounters = 7;
+constexpr int kCounters = 8;
 std::atomic<int64_t> g_counters[kCounters];
 
 int fail(int code, const std::string &msg)
@@ -96,7 +96,8 @@ int ensure_device(fsdppack_plan *p)
     }
     if (int rc = upload_table(p->copy_in)) return rc;
     if (int rc = upload_table(p->copy_out)) return rc;
-    p->caches.resize(2 * p->buckets.size() + 2);
+    if (int rc = upload_table(p->write_back_all)) return rc;
+    p->caches.resize(2 * p->buckets.size() + 3);
     p->device = dev;
     p->uploaded = true;
     g_counters[3]++;
@@ -143,6 +144,7 @@ int acquire_table(PtrCache &c, const std::vector<uint64_t> &key, hipStream_t str
             if (s.last_use < victim->last_use) victim = &s;
         if ((e = hipEventSynchronize(static_cast<hipEvent_t>(victim->ready))) != hipSuccess)
             return hip_fail(e, "hipEventSynchronize(previous upload)");
+        g_counters[7]++;
         size_t used = 0;
         for (void *st : victim->streams) {
             if (st == stream) continue;
@@ -498,6 +500,53 @@ int fsdppack_reduce_scatter_copy_out(const fsdppack_plan *cplan, int32_t bucket,
     }
 }
 
+int fsdppack_reduce_scatter_copy_out_all(const fsdppack_plan *cplan, int32_t rank, const void *const *rs_outs,
+                                         float divide_factor, void *const *shard_grads, void *stream)
+{
+    fsdppack_plan *plan = const_cast<fsdppack_plan *>(cplan);
+    if (!plan_ok(plan)) return fail(FSDPPACK_ESTATE, "reduce_scatter_copy_out_all: invalid plan handle");
+    if (rs_outs == nullptr) return fail(FSDPPACK_EINVAL, "reduce_scatter_copy_out_all: rs_outs is NULL");
+    const int32_t nb = static_cast<int32_t>(plan->buckets.size());
+    if (nb <= 1) {
+        // one bucket: the same launch as the per-bucket call
+        if (nb == 0) {
+            if (rank < 0 || rank >= plan->W) return fail(FSDPPACK_EINVAL, "reduce_scatter_copy_out_all: rank out of range");
+            if (!(divide_factor > 0.0f) || divide_factor > 3.4028235e38f)
+                return fail(FSDPPACK_EINVAL, "reduce_scatter_copy_out_all: divide_factor must be finite and positive");
+            g_next_start = g_next_stop = nullptr;     // armed timing events are taken: nothing to launch
+            return FSDPPACK_OK;
+        }
+        return fsdppack_reduce_scatter_copy_out(cplan, 0, rank, rs_outs[0], divide_factor, shard_grads, stream);
+    }
+    if (rank < 0 || rank >= plan->W) return fail(FSDPPACK_EINVAL, "reduce_scatter_copy_out_all: rank out of range");
+    if (!(divide_factor > 0.0f) || divide_factor > 3.4028235e38f)
+        return fail(FSDPPACK_EINVAL, "reduce_scatter_copy_out_all: divide_factor must be finite and positive");
+    if (shard_grads == nullptr) return fail(FSDPPACK_EINVAL, "reduce_scatter_copy_out_all: shard_grads is NULL");
+    // the parameters' entries, then one per bucket: its reduced row
+    std::vector<uint64_t> key(static_cast<size_t>(plan->n) + nb, 0);
+    for (int32_t bi = 0; bi < nb; ++bi) {
+        const BucketPlan &b = plan->buckets[bi];
+        if (b.S > 0 && (rs_outs[bi] == nullptr || !aligned(rs_outs[bi], dtype_bytes(b.dtype))))
+            return fail(FSDPPACK_EINVAL, "reduce_scatter_copy_out_all: rs_outs[" + std::to_string(bi) +
+                                             "] is NULL or not aligned to its element size");
+        key[static_cast<size_t>(plan->n) + bi] = reinterpret_cast<uint64_t>(rs_outs[bi]);
+        for (int32_t t : b.members) {
+            if (shard_elements(*plan, t, rank) == 0) continue;
+            void *g = shard_grads[t];
+            if (g == nullptr || !aligned(g, dtype_bytes(plan->params[t].storage_dtype)))
+                return fail(FSDPPACK_EINVAL, "reduce_scatter_copy_out_all: shard_grads[" + std::to_string(t) +
+                                                 "] is NULL or not aligned to its element size");
+            key[t] = reinterpret_cast<uint64_t>(g);
+        }
+    }
+    try {
+        return run_op(plan, plan->write_back_all, 2 * plan->buckets.size() + 2, key, nullptr, stream,
+                      "reduce_scatter_copy_out_all", rank, divide_factor);
+    } catch (const std::bad_alloc &) {
+        return fail(FSDPPACK_ENOMEM, "reduce_scatter_copy_out_all: out of host memory");
+    }
+}
+
 void fsdppack_plan_destroy(fsdppack_plan *plan)
 {
     if (!plan_ok(plan)) return;
@@ -526,6 +575,7 @@ void fsdppack_plan_destroy(fsdppack_plan *plan)
         }
         free_table(plan->copy_in);
         free_table(plan->copy_out);
+        free_table(plan->write_back_all);
         plan->magic = 0;
     }
     delete plan;

@@ -113,8 +113,10 @@ static_assert(sizeof(CopyInMember) == 32, "shared with the device");
 // index win0; numel elements of dtype dt, rank chunks of P elements found
 // at byte A of each all-gather row.  The reduce-scatter write-back uses the
 // same record for a bucket member: its windows cover the P-element rank
-// chunk in the storage dtype dt, read from byte A = O * size(reduce dtype)
-// of the rank's reduced row.
+// chunk in the storage dtype dt, read from byte A = O * size(src_dt) of the
+// rank's reduced row, whose elements have the bucket's reduction dtype src_dt.
+// That row is the call's buffer (src_slot -1) or, in the write-back of all
+// buckets in one launch, pointer-table entry src_slot.
 struct CopyOutTensor {
     int64_t win0;
     int64_t numel;
@@ -122,8 +124,10 @@ struct CopyOutTensor {
     int64_t A;
     int32_t slot;
     int32_t dt;
+    int32_t src_dt;          // write-back: the reduced row's dtype (copy-out: dt)
+    int32_t src_slot;        // write-back: pointer-table entry of the reduced row, -1: the call's buffer
 };
-static_assert(sizeof(CopyOutTensor) == 40, "shared with the device");
+static_assert(sizeof(CopyOutTensor) == 48, "shared with the device");
 
 // One parameter of an FSDP1 flat layout, for the flat write-back and copy-in:
 // flat positions [F, F + numel); its pieces (the part inside a rank's
@@ -202,6 +206,8 @@ constexpr int kInlineLarge = 960;
 // destination; elements >= valid are +0.
 struct RangeRef {
     uint64_t ptr;            // the caller tensor's address (pointer-table entry `slot`)
+    uint64_t src_ptr = 0;    // a source other than the call's buffer (pointer-table entry src_slot),
+    int32_t src_slot = -1;   // for a range whose table side is its destination; 0 / -1: none
     int64_t src_off;
     int64_t dst_off;
     int64_t lo;
@@ -659,6 +665,8 @@ FSDPPACK_HD inline void write_back_window(const WindowArgs &a, int32_t w, F &&f)
     if (e1 <= e0) return;
     RangeRef g;
     g.ptr = table_entry(a, t.slot);
+    g.src_slot = t.src_slot;
+    if (t.src_slot >= 0) g.src_ptr = table_entry(a, t.src_slot);
     g.src_off = t.A;
     g.dst_off = 0;
     g.lo = e0;
@@ -666,7 +674,7 @@ FSDPPACK_HD inline void write_back_window(const WindowArgs &a, int32_t w, F &&f)
     g.valid = e1;
     g.slot = t.slot;
     g.param = t.slot;
-    g.src_dt = a.reduce_dt;
+    g.src_dt = t.src_dt;
     g.dst_dt = t.dt;
     g.table_side = kTableIsDest;
     f(g);

@@ -392,7 +392,7 @@ __device__ __forceinline__ void run_range(const RangeRef &g, char *base, float d
     const char *src;
     char *dst;
     if (g.table_side == kTableIsSource) { src = tp + g.src_off; dst = base + g.dst_off; }
-    else { src = base + g.src_off; dst = tp + g.dst_off; }
+    else { src = (g.src_ptr ? reinterpret_cast<const char *>(g.src_ptr) : base) + g.src_off; dst = tp + g.dst_off; }
     if constexpr (SAME) {
         if (g.dst_dt == kBF16) copy_range<kBF16, kBF16, NT, DIV, BLK, UNR>(src, dst, g.lo, g.hi, g.valid, d);
         else copy_range<kFP32, kFP32, NT, DIV, BLK, UNR>(src, dst, g.lo, g.hi, g.valid, d);

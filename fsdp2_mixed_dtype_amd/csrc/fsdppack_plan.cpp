@@ -263,6 +263,8 @@ int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdp
             m.A = b.O[k] * dsz;
             m.slot = t;
             m.dt = plan->params[t].storage_dtype;
+            m.src_dt = b.dtype;
+            m.src_slot = -1;
             wb.add(m);
             win += (bytes + kWindowBytes - 1) / kWindowBytes;
             if (win > kMaxGridX) { err = "plan_buckets: sharded gradients need too many write-back workgroups"; return FSDPPACK_EINVAL; }
@@ -281,6 +283,32 @@ int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdp
             op.stretches.resize(op.columns.size());
             build_pack_stretches(op, op.stretches.data());
         }
+    }
+
+    if (plan->buckets.size() > 1) {
+        // the write-back of every bucket in one launch: the buckets' records
+        // one after another, each reading its bucket's reduced row from
+        // pointer-table entry n + bucket (after the parameters' entries)
+        OpTable &op = plan->write_back_all;
+        op.op = kOpWriteBack;
+        op.reduce_dt = plan->buckets[0].dtype;
+        int64_t win = 0;
+        for (size_t bi = 0; bi < plan->buckets.size(); ++bi) {
+            const OpTable &wb = plan->buckets[bi].write_back;
+            const CopyOutTensor *T = reinterpret_cast<const CopyOutTensor *>(wb.members.data());
+            for (int32_t k = 0; k < wb.n; ++k) {
+                CopyOutTensor m = T[k];
+                m.win0 += win;
+                m.src_slot = n + static_cast<int32_t>(bi);
+                op.add(m);
+            }
+            win += wb.n_windows;
+            op.dst_bytes += wb.dst_bytes;
+            op.src_bytes += wb.src_bytes;
+        }
+        if (win > kMaxGridX) { err = "plan_buckets: sharded gradients need too many write-back workgroups"; return FSDPPACK_EINVAL; }
+        op.n_windows = static_cast<int32_t>(win);
+        build_group_map(op);
     }
 
     {   // all-gather copy-in: each parameter owns bytes [A_t, A_{t+1}) of the
@@ -329,6 +357,8 @@ int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdp
             m.A = plan->A[t];
             m.slot = t;
             m.dt = plan->params[t].param_dtype;
+            m.src_dt = m.dt;
+            m.src_slot = -1;
             op.add(m);
             win += (bytes + kWindowBytes - 1) / kWindowBytes;
             if (win > kMaxGridX) { err = "plan_buckets: parameters need too many copy-out workgroups"; return FSDPPACK_EINVAL; }
@@ -526,6 +556,8 @@ int build_plan_flat(const fsdppack_param_desc *params, int32_t n, int32_t world,
             m.A = fl.F[t] * psz;
             m.slot = t;
             m.dt = pdt;
+            m.src_dt = pdt;
+            m.src_slot = -1;
             op.add(m);
             win += (bytes + kWindowBytes - 1) / kWindowBytes;
             if (win > kMaxGridX) { err = "plan_buckets_flat: parameters need too many copy-out workgroups"; return FSDPPACK_EINVAL; }

@@ -146,12 +146,14 @@ struct fsdppack_plan {
     int64_t B = 0;
     std::vector<fsdppack::BucketPlan> buckets;
     fsdppack::OpTable copy_in, copy_out;
+    fsdppack::OpTable write_back_all;         // every bucket's write-back in one launch (two or more buckets)
 
     // device state (guarded by mu)
     std::mutex mu;
     int device = -1;
     bool uploaded = false;
-    std::vector<fsdppack::PtrCache> caches;   // pack per bucket, copy-in, copy-out, write-back per bucket
+    std::vector<fsdppack::PtrCache> caches;   // pack per bucket, copy-in, copy-out, write-back per bucket,
+                                              // write-back of all buckets
 };
 
 namespace fsdppack {

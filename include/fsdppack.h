@@ -248,6 +248,25 @@ int fsdppack_reduce_scatter_copy_out(const fsdppack_plan *plan, int32_t bucket, 
                                      const void *rs_out, float divide_factor, void *const *shard_grads,
                                      void *stream);
 
+/* The write-back of every bucket of the unit in one launch: for each bucket
+ * b, exactly what fsdppack_reduce_scatter_copy_out(plan, b, rank, rs_outs[b],
+ * divide_factor, shard_grads, stream) writes (same passages: each rank keeps
+ * the gradient slice of the parameters it owns, "The unit you wrapped"; the
+ * gradient follows the resident parameter dtype, "Mixed-Precision
+ * Training").  A unit whose parameters reduce in two dtypes has two buckets,
+ * each with its own reduce-scatter; once both are done, this call writes
+ * every sharded gradient at the cost of one launch instead of one per
+ * bucket.  rs_outs: one host entry per bucket (in bucket order) of a device
+ * pointer to the rank's reduced row of that bucket (S_b elements of its
+ * reduction dtype), read only.  shard_grads: n host entries by parameter
+ * index, as for the per-bucket call (NULL allowed where the rank has no real
+ * element).  With one bucket (and for a flat plan) this is the per-bucket
+ * call on bucket 0.  One kernel launch on `stream` when there is anything to
+ * write.  Errors: EINVAL (rank out of range, bad divide_factor, NULL or
+ * misaligned pointer), ESTATE, EHIP, ENOMEM. */
+int fsdppack_reduce_scatter_copy_out_all(const fsdppack_plan *plan, int32_t rank, const void *const *rs_outs,
+                                         float divide_factor, void *const *shard_grads, void *stream);
+
 /* Free a plan and its device tables.  Synchronises the device first if the
  * plan was ever used there (no kernel may still read its tables).  NULL is a
  * no-op. */
@@ -269,8 +288,10 @@ int fsdppack_time_next_launch(void *start_event, void *stop_event);
  * kernel launches, [1] = pointer-table uploads, [2] = pointer-table reuses,
  * [3] = plan device-table uploads, [4] = pointer tables replaced by a new set,
  * [5] = cross-stream waits enqueued at such a replacement, [6] = launches
- * whose pointers travelled in the launch arguments.  The first min(n, 7)
- * entries are written. */
+ * whose pointers travelled in the launch arguments, [7] = host waits for a
+ * replaced table's previous upload (the only waits a compute call makes; no
+ * compute call synchronises the device).  The first min(n, 8) entries are
+ * written. */
 int fsdppack_counters(int64_t *counters, int32_t n);
 
 /* Measurement aid: launch a kernel that does nothing, with `workgroups`

@@ -402,6 +402,45 @@ int main(int argc, char **argv)
             }
         }
     }
+    if (plan.buckets.size() > 1) {
+        // the write-back of every bucket in one launch: each member written
+        // exactly once from its own bucket's row (pointer-table entry
+        // n + bucket), in that bucket's reduction dtype
+        std::vector<int32_t> bucket_of(n, -1);
+        for (size_t bi = 0; bi < plan.buckets.size(); ++bi)
+            for (int32_t t : plan.buckets[bi].members) bucket_of[t] = static_cast<int32_t>(bi);
+        for (int32_t r : ranks) {
+            std::vector<Intervals> written(n);
+            char name[64];
+            std::snprintf(name, sizeof name, "write-back of all buckets, rank %d", r);
+            std::vector<int64_t> dst_limit(n, 0);
+            for (int32_t t = 0; t < n; ++t) dst_limit[t] = bucket_of[t] >= 0 ? piece_bytes(t, r) : 0;
+            bool sources_ok = true;
+            auto row_bytes = [&](const RangeRef &g) -> int64_t {
+                const int32_t bi = g.src_slot - n;
+                if (g.param < 0 || bi != bucket_of[g.param] || g.src_dt != plan.buckets[bi].dtype) {
+                    sources_ok = false;
+                    return -1;
+                }
+                return plan.buckets[bi].S * dtype_bytes(plan.buckets[bi].dtype);
+            };
+            if (!check_op(name, plan.write_back_all, plan.W, 0, n, [&](const RangeRef &g) { return dst_limit[g.param]; },
+                          row_bytes, written, r))
+                return fail();
+            if (!sources_ok) {
+                std::printf("FAIL %s: a range reads another bucket's row or dtype\n", name);
+                return 1;
+            }
+            for (int32_t t = 0; t < n; ++t) {
+                char tn[96];
+                std::snprintf(tn, sizeof tn, "%s param %d", name, t);
+                if (!tiles(written[t], dst_limit[t], tn)) return fail();
+            }
+        }
+    } else if (plan.write_back_all.n_windows != 0 || plan.write_back_all.n != 0) {
+        std::puts("FAIL a one-bucket plan has an all-bucket write-back table");
+        return 1;
+    }
     std::printf("OK %s%zu buckets, windows:", flat ? "flat, " : "", plan.buckets.size());
     for (const BucketPlan &b : plan.buckets) std::printf(" %d (rows/group %d)", b.pack.n_windows, 1 << b.pack.group_lg);
     std::printf(" copy_in %d copy_out %d; direct pack windows %lld, stretch-direct pack windows %lld, "

@@ -334,6 +334,7 @@ def test_pointer_churn_on_two_streams():
     assert c1[1] - c0[1] == 40                       # every set uploaded once
     assert c1[4] - c0[4] == 40 - 16                  # the rest replaced older tables
     assert c1[5] - c0[5] > 0                         # ... some of them used by the other stream
+    assert c1[7] - c0[7] == c1[4] - c0[4]            # one host wait (for an old upload) per replacement
     plan.destroy()
 
 
@@ -667,6 +668,85 @@ def check_rs_copy_out(w, ref, plan, bucket, rank, row, factor, row_offset=0, dst
             bad = np.flatnonzero(got != want)
             pytest.fail(f"{w.name} bucket {bucket} rank {rank} factor {factor}: param {i}: {bad.size} bytes differ, "
                         f"first at byte {bad[0]}")
+
+
+def check_rs_copy_out_all(w, ref, plan, rank, rows, factor, row_offsets=None, dst_offsets=None, prepared=False):
+    """HIP write-back of every bucket in one launch vs the oracle's write-back
+    of each bucket, byte for byte, into guarded destinations."""
+    rs = [to_dev(row, b.dtype, row_offsets[bi] if row_offsets else 0) for bi, (row, b) in enumerate(zip(rows, ref.buckets))]
+    outs = [None] * len(w.tensors)
+    for b in ref.buckets:
+        for k, i in enumerate(b.members):
+            v = oracle.valid_in_chunk(w.tensors[i].numel, b.P[k], rank)
+            if v:
+                outs[i] = Guarded(v, w.tensors[i].storage_dtype, dst_offsets[i] if dst_offsets else i % 3)
+    dst = [o.t if o is not None else None for o in outs]
+    if prepared:
+        dst = fp.prepare_shard_grads(plan, None, rank, dst)
+    c0 = fp.counters()[0]
+    fp.reduce_scatter_copy_out_all(plan, rank, rs, dst, factor)
+    torch.cuda.synchronize()
+    assert fp.counters()[0] - c0 <= 1, "more than one launch"
+    for bi, b in enumerate(ref.buckets):
+        wants = oracle.rs_copy_out(ref, bi, rank, rows[bi], factor)
+        for k, i in enumerate(b.members):
+            if outs[i] is None:
+                assert wants[k].size == 0
+                continue
+            got, want = outs[i].result(), wants[k].view(np.uint8)
+            if not np.array_equal(got, want):
+                bad = np.flatnonzero(got != want)
+                pytest.fail(f"{w.name} all buckets rank {rank} factor {factor}: bucket {bi} param {i}: "
+                            f"{bad.size} bytes differ, first at byte {bad[0]}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "mixed50m", "hetero500"])
+def test_rs_copy_out_all_buckets_matches_oracle(name):
+    """The write-back of every bucket in one launch (one bucket: the per-bucket call)."""
+    print(f"[write-back all] workload={name}", flush=True)
+    w = wl.get(name)
+    ref = oracle.plan(w.descs(), w.world)
+    plan = fp.plan_buckets(w.descs(), w.world)
+    W = w.world
+    rows = []
+    for bi, b in enumerate(ref.buckets):
+        row = wl.random_array(b.S, b.dtype, seed=31 + bi)
+        wl.inject_specials([row], [b.dtype], seed=7 + bi)
+        rows.append(row)
+    ranks = range(W) if W <= 4 else [0, 1, W // 2, W - 1]
+    for rank in ranks:
+        for factor in (1.0, float(W), 3.0):
+            print(f"[write-back all] {name} buckets={len(rows)} rank={rank} factor={factor}", flush=True)
+            check_rs_copy_out_all(w, ref, plan, rank, rows, factor, prepared=(rank % 2 == 1))
+    plan.destroy()
+
+
+def test_rs_copy_out_all_buckets_random_layouts_misaligned():
+    rng = random.Random(5151)
+    done = 0
+    for case in range(400):
+        w = _random_workload(rng, case)
+        ref = oracle.plan(w.descs(), w.world)
+        if len(ref.buckets) < 2:
+            continue
+        plan = fp.plan_buckets(w.descs(), w.world)
+        rows = []
+        for bi, b in enumerate(ref.buckets):
+            row = wl.random_array(b.S, b.dtype, seed=case * 7 + bi)
+            wl.inject_specials([row], [b.dtype], seed=case + bi)
+            rows.append(row)
+        rank = rng.randrange(w.world)
+        factor = rng.choice([1.0, 2.0, 3.0, 0.5, 6.0, float(np.float32(1e-3)), 1e30])
+        row_offs = [rng.choice([0, 0, 1, 3]) for _ in rows]
+        offs = {i: rng.choice([0, 0, 1, 2, 3, 5, 7]) for i in range(len(w.tensors))}
+        print(f"[write-back all random] case={case} W={w.world} buckets={len(rows)} rank={rank} factor={factor} "
+              f"row_off={row_offs} dst_off={offs}", flush=True)
+        check_rs_copy_out_all(w, ref, plan, rank, rows, factor, row_offs, offs)
+        plan.destroy()
+        done += 1
+        if done == 40:
+            break
+    assert done >= 20
 
 
 @pytest.mark.parametrize("name", ["tiny", "mixed50m", "layout500", "kda_block", "hetero500"])

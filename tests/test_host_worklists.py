@@ -193,6 +193,41 @@ def test_no_alloc_pack_argument_errors_before_any_gpu_work():
     assert fp.counters()[0] == 0
 
 
+def test_write_back_all_argument_errors_before_any_gpu_work():
+    import ctypes
+    L = fp.lib()
+    f = L.fsdppack_reduce_scatter_copy_out_all
+    # two buckets (fp32 and bf16 reduction)
+    p = fp.plan_buckets([(4, 4, FP32, FP32, FP32, BF16), (3, 1, BF16, BF16, FP32, BF16)], 2)
+    assert len(p.buckets) == 2
+    grads = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    rows = (ctypes.c_void_p * 2)(0x4000, 0x5000)
+    assert f(p.handle, 0, None, 1.0, grads, None) == -1                   # NULL rows
+    assert f(p.handle, 2, rows, 1.0, grads, None) == -1                   # rank out of range
+    assert f(p.handle, 0, rows, 0.0, grads, None) == -1                   # bad factor
+    assert f(p.handle, 0, rows, float("inf"), grads, None) == -1
+    assert f(p.handle, 0, rows, 1.0, None, None) == -1                    # NULL shard_grads
+    bad_row = (ctypes.c_void_p * 2)(0x4000, 0x5001)
+    assert f(p.handle, 0, bad_row, 1.0, grads, None) == -1                # misaligned bf16 row
+    assert "rs_outs[1]" in L.fsdppack_last_error().decode()
+    bad_grad = (ctypes.c_void_p * 2)(0x1002, 0x2000)
+    assert f(p.handle, 0, rows, 1.0, bad_grad, None) == -1                # misaligned fp32 shard
+    assert "shard_grads[0]" in L.fsdppack_last_error().decode()
+    assert f(None, 0, rows, 1.0, grads, None) == -5
+    p.destroy()
+    # one bucket: the per-bucket call's checks
+    q = fp.plan_buckets([(4, 4, FP32, 0, FP32, BF16)], 2)
+    assert f(q.handle, 0, (ctypes.c_void_p * 1)(0x4001), 1.0, grads, None) == -1
+    assert "rs_out" in L.fsdppack_last_error().decode()
+    q.destroy()
+    # no parameters: nothing to launch, arguments still checked
+    e = fp.plan_buckets([], 2)
+    assert f(e.handle, 0, rows, 1.0, grads, None) == 0
+    assert f(e.handle, 3, rows, 1.0, grads, None) == -1
+    e.destroy()
+    assert fp.counters()[0] == 0
+
+
 def test_empty_launch_argument_errors():
     L = fp.lib()
     for wg, th in ((0, 64), (-1, 64), (1, 0), (1, 63), (1, 2048), (1 << 30, 1024), ((1 << 31) - 1, 64)):
