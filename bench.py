@@ -523,7 +523,13 @@ def main():
             rows = 1 if args.flat else W
             row_bytes = (W * b.S if args.flat else b.S) * esz(b.dtype)
             wg[f"pack[{bi}]"] = (ceil_div(row_bytes, WINDOW_BYTES) + 1) * rows
-        wg["copy_in"] = ceil_div(shift + plan.B, WINDOW_BYTES)
+        if args.flat:
+            wg["copy_in"] = ceil_div(shift + plan.B, WINDOW_BYTES)
+        else:
+            # each parameter's segment [A_t, A_t+1) of the row gets the windows
+            # its worst line alignment needs (a segment starts <= 124 bytes past a line)
+            ends = list(plan.A[1:]) + [plan.B]
+            wg["copy_in"] = sum(ceil_div(e - a + 124, WINDOW_BYTES) for a, e in zip(plan.A, ends) if e > a)
         wg["copy_out"] = sum(ceil_div(t.numel * esz(t.param_dtype), WINDOW_BYTES) for t in w.tensors if t.numel)
         for bi, b in enumerate(plan.buckets):
             if args.flat:

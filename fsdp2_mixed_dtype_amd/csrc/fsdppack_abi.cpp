@@ -421,18 +421,20 @@ int fsdppack_all_gather_copy_in(const fsdppack_plan *cplan, int32_t rank, const 
     }
     if (plan->B > 0 && (ag_out == nullptr || !aligned(ag_out, 4)))
         return fail(FSDPPACK_EINVAL, "all_gather_copy_in: ag_out is NULL or not 4-byte aligned");
-    std::vector<uint64_t> key(plan->n, 0);
-    for (int32_t t = 0; t < plan->n; ++t) {
-        if (plan->P[t] == 0) continue;
+    // the table is in segment-record order (every parameter with P > 0)
+    const OpTable &op = plan->copy_in;
+    std::vector<uint64_t> key(op.table_params.size(), 0);
+    for (size_t m = 0; m < key.size(); ++m) {
+        const int32_t t = op.table_params[m];
         const void *s = shards[t];
         if (s == nullptr || !aligned(s, dtype_bytes(plan->params[t].storage_dtype)))
             return fail(FSDPPACK_EINVAL, "all_gather_copy_in: shards[" + std::to_string(t) +
                                              "] is NULL or not aligned to its element size");
-        key[t] = reinterpret_cast<uint64_t>(s);
+        key[m] = reinterpret_cast<uint64_t>(s);
     }
     char *row = static_cast<char *>(ag_out) + static_cast<int64_t>(rank) * plan->B;
     try {
-        return run_op(plan, plan->copy_in, plan->buckets.size(), key, row, stream, "all_gather_copy_in");
+        return run_op(plan, op, plan->buckets.size(), key, row, stream, "all_gather_copy_in");
     } catch (const std::bad_alloc &) {
         return fail(FSDPPACK_ENOMEM, "all_gather_copy_in: out of host memory");
     }

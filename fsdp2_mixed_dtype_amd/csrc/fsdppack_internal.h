@@ -97,17 +97,30 @@ struct ColumnWindow {
 };
 static_assert(sizeof(ColumnWindow) == 8, "shared with the device");
 
-// One parameter of the all-gather copy-in: bytes [A, A_next) of the row,
-// the first P elements (param dtype) cast from the shard, the rest zero.
-struct CopyInMember {
+// One parameter's segment of the all-gather copy-in row: bytes [A, A_next)
+// with A_next = A + P*size(dst_dt) rounded up to 16 bytes; its first P
+// elements (param dtype dst_dt) are the shard (storage dtype src_dt) cast,
+// the rest (fewer than 16 bytes) zero.  Its windows are win0, win0 + 1, ...
+// (copy_in_windows of them).  The copy-in's pointer table is in record
+// order: entry m is record m's shard.
+struct CopyInSeg {
     int64_t A;
-    int64_t A_next;
     int64_t P;
-    int32_t slot;
+    int32_t win0;
+    int32_t param;           // parameter index (host-side checks)
     int16_t src_dt;
     int16_t dst_dt;
+    int32_t reserved;
 };
-static_assert(sizeof(CopyInMember) == 32, "shared with the device");
+static_assert(sizeof(CopyInSeg) == 32, "shared with the device");
+
+// Windows of a copy-in segment of `bytes` bytes: its bytes cut at the
+// 2 KiB-spaced line boundaries of memory, counted from the line holding its
+// first byte, for the worst start in a line (the row is 4-byte aligned and
+// segments start on 16-byte boundaries of it, so a segment starts at most
+// 124 bytes past a line); a window past the segment's end for its start is
+// empty.
+FSDPPACK_HD inline int64_t copy_in_windows(int64_t bytes) { return (bytes + 124 + 2047) >> 11; }
 
 // One parameter of the all-gather copy-out: its windows start at window
 // index win0; numel elements of dtype dt, rank chunks of P elements found
@@ -455,133 +468,121 @@ FSDPPACK_HD inline bool pack_direct_stretch(const WindowArgs &a, int32_t r, int3
                                  static_cast<uint32_t>(a.map_lg), lg, a.reduce_dt, r, k, d);
 }
 
-// Copy-in window w: bytes [y0, y1) of the row, which lie in one or two
-// stretches of the member map.  Every member's span is a
-// multiple of 16 bytes.
+// The record of the window-indexed table `T` (records sorted by win0)
+// whose windows contain window w: a binary search among the few records the
+// group map names for w's group (usually one).
+template <typename T>
+FSDPPACK_HD inline int32_t find_record(const void *groups, const void *records, int32_t w)
+{
+    const FSDPPACK_TABLE T *R = (const FSDPPACK_TABLE T *)records;
+    const ColumnWindow grp = ((const FSDPPACK_TABLE ColumnWindow *)groups)[w >> kGroupLog2];
+    int32_t lo = grp.first, hi = grp.first + grp.count - 1;   // last record with win0 <= w
+    while (lo < hi) {
+        const int32_t mid = (lo + hi + 1) >> 1;
+        if (R[mid].win0 <= w) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Group map of the copy-in, per 2^kGroupLog2 windows: the record owning the
+// group's first window and, when one more record starts inside the group,
+// the window where it starts (split; INT32_MAX when the group has one record),
+// so that a window names its record without reading any; a group over three
+// or more records holds -(their number) in split, and its windows search.
+struct WindowGroup {
+    int32_t first;
+    int32_t split;
+};
+static_assert(sizeof(WindowGroup) == 8, "shared with the device");
+
+FSDPPACK_HD inline int32_t find_copy_in_record(const void *groups, const void *segs, int32_t w)
+{
+    const WindowGroup g = ((const FSDPPACK_TABLE WindowGroup *)groups)[w >> kGroupLog2];
+    if (g.split >= 0) return g.first + (w >= g.split ? 1 : 0);
+    const FSDPPACK_TABLE CopyInSeg *R = (const FSDPPACK_TABLE CopyInSeg *)segs;
+    int32_t lo = g.first, hi = g.first - g.split - 1;   // last record with win0 <= w
+    while (lo < hi) {
+        const int32_t mid = (lo + hi + 1) >> 1;
+        if (R[mid].win0 <= w) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Copy-in window w of a row that starts `shift` bytes past a cache line:
+// segment m (from the group map; its record `s` read in one scalar load
+// together with its shard's pointer, table entry m) and its bytes [y0, y1) of the row, which
+// end on line boundaries of memory except at the segment's own ends.  Every
+// window is thus one range of one segment; y1 <= y0 for a spare window.
+struct CopyInWindow {
+    CopyInSeg s;
+    uint64_t ptr;
+    int32_t m;
+    int64_t y0, y1, A_next;
+};
+FSDPPACK_HD inline CopyInWindow copy_in_span(const void *groups, const void *segs, const uint64_t *table,
+                                             int32_t shift, int32_t w)
+{
+    CopyInWindow c;
+    c.m = find_copy_in_record(groups, segs, w);
+    c.s = read_record<CopyInSeg>(segs, c.m);
+    c.ptr = table ? ((const FSDPPACK_TABLE uint64_t *)table)[c.m] : 0;
+    const int lg = c.s.dst_dt == kBF16 ? 1 : 2;
+    c.A_next = c.s.A + ((((c.s.P << lg) + 15) >> 4) << 4);
+    const int64_t line0 = ((shift + c.s.A) & ~static_cast<int64_t>(kLineBytes - 1)) - shift;
+    const int64_t start = line0 + (static_cast<int64_t>(w - c.s.win0) << kWindowLog2);
+    c.y0 = imax(c.s.A, start);
+    c.y1 = imin(c.A_next, start + kWindowBytes);
+    return c;
+}
+
+// The window's one range (elements [lo, hi) of the segment; those past P
+// are the zero gap).
+FSDPPACK_HD inline RangeRef copy_in_range(const CopyInWindow &c)
+{
+    const int lg = c.s.dst_dt == kBF16 ? 1 : 2;
+    RangeRef g;
+    g.ptr = c.ptr;
+    g.src_off = 0;
+    g.dst_off = c.s.A;
+    g.lo = (c.y0 - c.s.A) >> lg;
+    g.hi = (c.y1 - c.s.A) >> lg;
+    g.valid = c.s.P;
+    g.slot = c.m;
+    g.param = c.s.param;
+    g.src_dt = c.s.src_dt;
+    g.dst_dt = c.s.dst_dt;
+    g.table_side = kTableIsSource;
+    return g;
+}
+
+// Whether the window is copied whole by the direct copy: 2 KiB of real
+// elements on 16-byte destination vectors (every window but a segment's
+// first and last, on a row 16-byte aligned in memory); fills `d`.  The copy
+// is then exactly the window's range.
+FSDPPACK_HD inline bool copy_in_direct(const CopyInWindow &c, int32_t shift, DirectWindow &d)
+{
+    const int lg = c.s.dst_dt == kBF16 ? 1 : 2;
+    if (c.y1 - c.y0 != kWindowBytes || ((c.y1 - c.s.A) >> lg) > c.s.P || ((shift + c.y0) & 15) != 0) return false;
+    d.src = c.ptr + static_cast<uint64_t>(((c.y0 - c.s.A) >> lg) * dtype_bytes(c.s.src_dt));
+    d.dst_off = c.y0;
+    d.src_dt = c.s.src_dt;
+    d.dst_dt = c.s.dst_dt;
+    return true;
+}
+
+// Copy-in window w of the launch `a` as a range (none for a spare window).
 template <typename F>
 FSDPPACK_HD inline void copy_in_window(const WindowArgs &a, int32_t w, F &&f)
 {
-    const FSDPPACK_TABLE ColumnWindow *C = (const FSDPPACK_TABLE ColumnWindow *)a.columns;
-    int64_t y0, y1;
-    window_span(w, a.shift, a.B, y0, y1);
-    const int32_t m0 = C[y0 >> a.map_lg].first;
-    const ColumnWindow last = C[(y1 - 1) >> a.map_lg];
-    for (int32_t m = m0; m < last.first + last.count; ++m) {
-        const CopyInMember cm = read_record<CopyInMember>(a.members, m);
-        const int64_t b0 = imax(y0, cm.A), b1 = imin(y1, cm.A_next);
-        if (b1 <= b0) continue;                          // in the map's stretch, not in this window
-        const int64_t esz = dtype_bytes(cm.dst_dt);
-        RangeRef g;
-        g.ptr = table_entry(a, cm.slot);
-        g.src_off = 0;
-        g.dst_off = cm.A;
-        g.lo = (b0 - cm.A) / esz;
-        g.hi = (b1 - cm.A) / esz;
-        g.valid = cm.P;
-        g.slot = cm.slot;
-        g.param = cm.slot;
-        g.src_dt = cm.src_dt;
-        g.dst_dt = cm.dst_dt;
-        g.table_side = kTableIsSource;
-        f(g);
-    }
-}
-
-// The copy-in counterpart of pack_direct: window w is one whole window of a
-// single parameter's segment [A, A_next) that lies inside its shard's P
-// elements (no zero gap), the destination on 16-byte vectors in memory and
-// the source on dwords (or 2 bytes past one for bf16).  With one or two
-// candidate records in its map stretches, both are read in one round trip;
-// the pointer table is indexed by parameter, so the pointer follows.  The
-// window then equals the single range copy_in_window produces for it.
-FSDPPACK_HD inline bool copy_in_direct(const WindowArgs &a, int32_t w, DirectWindow &d)
-{
-    const FSDPPACK_TABLE ColumnWindow *C = (const FSDPPACK_TABLE ColumnWindow *)a.columns;
-    int64_t y0, y1;
-    window_span(w, a.shift, a.B, y0, y1);
-    if (y1 - y0 != kWindowBytes) return false;
-    const ColumnWindow e0 = C[y0 >> a.map_lg], e1 = C[(y1 - 1) >> a.map_lg];
-    const int32_t m0 = e0.first, n = e1.first + e1.count - m0;
-    if (n < 1 || n > 2) return false;
-    const CopyInMember c0 = read_record<CopyInMember>(a.members, m0);
-    const CopyInMember c1 = read_record<CopyInMember>(a.members, m0 + n - 1);
-    const CopyInMember cm = y0 >= c1.A ? c1 : c0;        // members tile the row in order
-    const int64_t esz = dtype_bytes(cm.dst_dt);
-    if (y0 < cm.A || y1 > cm.A_next || (y1 - cm.A) / esz > cm.P) return false;
-    d.src = table_entry(a, cm.slot) + static_cast<uint64_t>((y0 - cm.A) / esz * dtype_bytes(cm.src_dt));
-    d.dst_off = y0;
-    d.src_dt = cm.src_dt;
-    d.dst_dt = cm.dst_dt;
-    return (d.src & (cm.src_dt == kBF16 ? 1u : 3u)) == 0 && ((a.shift + y0) & 15) == 0;
-}
-
-// Segments a copy-in window must overlap to be gathered vector by vector in
-// one pass instead of walked segment by segment (each segment a full round
-// trip of loads and stores).  Segments start on 16-byte
-// boundaries of the row and span whole 16-byte vectors, so when the row
-// itself starts on a 16-byte boundary of memory every destination vector
-// lies in a single segment.
-constexpr int32_t kCopyInGatherRecords = 3;
-
-// Whether copy-in window w is gathered: the row 16-byte aligned in memory
-// and at least kCopyInGatherRecords segments overlapping the window's bytes
-// [y0, y1) (multiples of 16 from the row's start), which are those of
-// records m0 ... m0 + n - 1.
-FSDPPACK_HD inline bool copy_in_gathered(const WindowArgs &a, int32_t w, int64_t &y0, int64_t &y1, int32_t &m0,
-                                         int32_t &n)
-{
-    if ((a.shift & 15) != 0) return false;
-    const FSDPPACK_TABLE ColumnWindow *C = (const FSDPPACK_TABLE ColumnWindow *)a.columns;
-    window_span(w, a.shift, a.B, y0, y1);
-    const int32_t c0 = C[y0 >> a.map_lg].first;
-    const ColumnWindow last = C[(y1 - 1) >> a.map_lg];
-    const int32_t nc = last.first + last.count - c0;
-    if (nc < kCopyInGatherRecords) return false;
-    int32_t k0 = 0, k1 = 0;                  // the records owning bytes y0 and y1 - 1
-    for (int32_t k = 0; k < nc; ++k) {
-        const int64_t A = read_record<CopyInMember>(a.members, c0 + k).A;
-        if (A <= y0) k0 = k;
-        if (A < y1) k1 = k;
-    }
-    m0 = c0 + k0;
-    n = k1 - k0 + 1;
-    return n >= kCopyInGatherRecords;
-}
-
-// The copy-in record owning row byte y among the candidates m0 ... m0+n-1
-// (the last whose segment starts at or before y: members tile the row in
-// order), with its shard's pointer.  Called per lane with a wave-uniform
-// candidate list, so the records are read by scalar loads and each lane
-// keeps its own pick.
-struct CopyInPick {
-    CopyInMember m;
-    uint64_t ptr;
-};
-FSDPPACK_HD inline CopyInPick copy_in_member_at(const WindowArgs &a, int32_t m0, int32_t n, int64_t y)
-{
-    CopyInPick p;
-    p.m = read_record<CopyInMember>(a.members, m0);
-    p.ptr = table_entry(a, p.m.slot);
-    for (int32_t k = 1; k < n; ++k) {
-        const CopyInMember cm = read_record<CopyInMember>(a.members, m0 + k);
-        const uint64_t ptr = table_entry(a, cm.slot);
-        if (y >= cm.A) { p.m = cm; p.ptr = ptr; }
-    }
-    return p;
+    const CopyInWindow c = copy_in_span(a.columns, a.members, a.table, a.shift, w);
+    if (c.y1 > c.y0) f(copy_in_range(c));
 }
 
 // The tensor record whose windows contain window w: a binary search on win0
 // among the few records the group map names for w's group (usually one).
 FSDPPACK_HD inline CopyOutTensor find_tensor(const WindowArgs &a, int32_t w)
 {
-    const FSDPPACK_TABLE CopyOutTensor *T = (const FSDPPACK_TABLE CopyOutTensor *)a.members;
-    const ColumnWindow grp = ((const FSDPPACK_TABLE ColumnWindow *)a.columns)[w >> kGroupLog2];
-    int32_t lo = grp.first, hi = grp.first + grp.count - 1;   // last record with win0 <= w
-    while (lo < hi) {
-        const int32_t mid = (lo + hi + 1) >> 1;
-        if (T[mid].win0 <= w) lo = mid; else hi = mid - 1;
-    }
-    return T[lo];
+    return ((const FSDPPACK_TABLE CopyOutTensor *)a.members)[find_record<CopyOutTensor>(a.columns, a.members, w)];
 }
 
 // Elements [e0, e1) of tensor t that copy-out window w covers: bytes

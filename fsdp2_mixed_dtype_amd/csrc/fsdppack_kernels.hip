@@ -16,11 +16,12 @@
 // design aims at HBM bandwidth, not at the matrix cores:
 //  * each workgroup (one wave64) owns one 2 KiB window, finds the ranges it
 //    overlaps from its index and the plan's small tables, and walks them; a
-//    pack or copy-in window inside a single member's chunk with no padding
-//    (nearly all of them in large layouts) skips the walk and copies
-//    directly, and a copy-in or copy-out window over many small segments or
-//    rank chunks gathers its elements in one pass instead of one round trip
-//    of loads and stores per piece;
+//    pack window inside a single member's chunk with no padding (nearly all
+//    of them in large layouts) skips the walk and copies directly, a copy-in
+//    window is always one range of one parameter's segment (copied directly
+//    when whole), and a copy-out window over many small rank chunks gathers
+//    its elements in one pass instead of one round trip of loads and stores
+//    per chunk;
 //  * every whole 16-byte destination vector is written by one 16-byte vector
 //    store (element stores only at a range's unaligned head and tail),
 //    64-lane wavefronts covering 1 KiB per store instruction;
@@ -484,60 +485,6 @@ __device__ __forceinline__ void run_direct(const DirectWindow &d, char *base)
     }
 }
 
-// A copy-in window over many small segments (copy_in_gathered): each lane
-// takes its destination vectors, finds the segment holding each one among
-// the window's candidate records, and loads that segment's source elements
-// one by one (the dtype pair changes from segment to segment); then it
-// converts and stores the vectors, so the whole window is one round of
-// loads and one of stores.  Elements past a shard's P are the zero gap.
-__device__ __forceinline__ void copy_in_gather(const WindowArgs &a, int64_t y0, int64_t y1, int32_t m0, int32_t n)
-{
-    const VecOut out(a.base + y0, (y1 - y0) >> 4);
-    const int tid = threadIdx.x;
-    uint32_t e[kUnroll][8];
-    int32_t kind[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        const int64_t y = y0 + static_cast<int64_t>(tid + u * kBlock) * 16;
-        kind[u] = -1;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) e[u][k] = 0;
-        if (y < y1) {
-            const CopyInPick p = copy_in_member_at(a, m0, n, y);
-            const int dlg = p.m.dst_dt == kBF16 ? 1 : 2;              // log2 of the destination element size
-            const int64_t first = (y - p.m.A) >> dlg;
-            const char *src = reinterpret_cast<const char *>(p.ptr);
-            kind[u] = p.m.src_dt * 4 + p.m.dst_dt;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                if (k < (16 >> dlg) && first + k < p.m.P) {
-                    if (p.m.src_dt == kBF16) e[u][k] = __builtin_nontemporal_load(gin<uint16_t>(src) + first + k);
-                    else e[u][k] = __builtin_nontemporal_load(gin<uint32_t>(src) + first + k);
-                }
-            }
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        if (kind[u] < 0) continue;
-        const uint32_t *x = e[u];
-        u32x4 r;
-        if (kind[u] == kBF16 * 4 + kBF16) {
-            r.x = x[0] | (x[1] << 16); r.y = x[2] | (x[3] << 16); r.z = x[4] | (x[5] << 16); r.w = x[6] | (x[7] << 16);
-        } else if (kind[u] == kFP32 * 4 + kBF16) {
-            r.x = f32_to_bf16(x[0]) | (f32_to_bf16(x[1]) << 16);
-            r.y = f32_to_bf16(x[2]) | (f32_to_bf16(x[3]) << 16);
-            r.z = f32_to_bf16(x[4]) | (f32_to_bf16(x[5]) << 16);
-            r.w = f32_to_bf16(x[6]) | (f32_to_bf16(x[7]) << 16);
-        } else if (kind[u] == kBF16 * 4 + kFP32) {
-            r.x = x[0] << 16; r.y = x[1] << 16; r.z = x[2] << 16; r.w = x[3] << 16;
-        } else {
-            r.x = x[0]; r.y = x[1]; r.z = x[2]; r.w = x[3];
-        }
-        out.put(tid + u * kBlock, r);
-    }
-}
-
 // A copy-out window over many small rank chunks (copy_out_gathered): each
 // lane fetches its elements one by one from wherever their chunks sit in the
 // gathered buffer, so the whole window is one round of loads and one of
@@ -606,6 +553,25 @@ __global__ void __launch_bounds__(kPackBlock) pack_kernel(const PackStretch *st,
                    [&](const RangeRef &g) { run_range<false, false, false, kPackBlock, kPackUnroll>(g, a.base, 1.0f); });
 }
 
+// The all-gather copy-in: one workgroup per window of a parameter's segment
+// of the row.  The window's group-map entry, then its segment record with
+// the shard's pointer, are the only reads before its data; their table
+// addresses and the row's line offset come first among the arguments, so
+// that they are preloaded into scalar registers.  A whole window of real
+// elements is copied directly, a segment's first and last window as a range.
+template <int N>
+__global__ void __launch_bounds__(kBlock) copy_in_kernel(const ColumnWindow *groups, const CopyInSeg *segs,
+                                                        uint32_t shift, WindowArgs a, PtrTab<N> t)
+{
+    use_inline_table(a, t);
+    const CopyInWindow c = copy_in_span(groups, segs, a.table, static_cast<int32_t>(shift),
+                                        static_cast<int32_t>(blockIdx.x));
+    if (c.y1 <= c.y0) return;                       // the segment's spare window
+    DirectWindow d;
+    if (copy_in_direct(c, static_cast<int32_t>(shift), d)) run_direct<true>(d, a.base);
+    else run_range<true, false>(copy_in_range(c), a.base, 1.0f);
+}
+
 // One workgroup per window; the window's ranges come from its index and the
 // plan's (cache-resident) record tables.
 template <int OP, int N>
@@ -614,14 +580,7 @@ __global__ void __launch_bounds__(kBlock) window_kernel(WindowArgs a, PtrTab<N> 
     use_inline_table(a, t);
     const int32_t w = static_cast<int32_t>(blockIdx.x);
     auto body = [&](const RangeRef &g) { run_range<true, false>(g, a.base, 1.0f); };
-    if constexpr (OP == kOpCopyIn) {
-        DirectWindow d;
-        int64_t y0, y1;
-        int32_t m0, n;
-        if (copy_in_direct(a, w, d)) run_direct<true>(d, a.base);
-        else if (copy_in_gathered(a, w, y0, y1, m0, n)) copy_in_gather(a, y0, y1, m0, n);
-        else copy_in_window(a, w, body);
-    } else if constexpr (OP == kOpCopyOut) {
+    if constexpr (OP == kOpCopyOut) {
         const CopyOutTensor t = find_tensor(a, w);
         int64_t e0, e1;
         copy_out_span(t, w, e0, e1);
@@ -694,7 +653,9 @@ int launch_sized(const WindowArgs &args, const uint64_t *inline_ptrs, int32_t n,
         hipExtLaunchKernelGGL(pack_kernel<N>, grid2, dim3(kPackBlock), 0, st, e0, e1, 0, args.stretches, rb,
                               static_cast<uint32_t>(args.shift), static_cast<uint32_t>(args.map_lg), meta, args, t);
     } else if (args.op == kOpCopyIn) {
-        hipExtLaunchKernelGGL(window_kernel<kOpCopyIn, N>, grid, block, 0, st, e0, e1, 0, args, t);
+        hipExtLaunchKernelGGL(copy_in_kernel<N>, grid, block, 0, st, e0, e1, 0,
+                              static_cast<const ColumnWindow *>(args.columns), static_cast<const CopyInSeg *>(args.members),
+                              static_cast<uint32_t>(args.shift), args, t);
     } else if (args.op == kOpCopyOut) {
         hipExtLaunchKernelGGL(window_kernel<kOpCopyOut, N>, grid, block, 0, st, e0, e1, 0, args, t);
     } else if (args.op == kOpWriteBack) {

@@ -105,21 +105,22 @@ static bool pack_narrow(const OpTable &op, const std::vector<PackMember> &mem)
     return true;
 }
 
-// Group map of a table of CopyOutTensor records whose windows are
-// consecutive (record t owns windows [win0_t, win0_{t+1})): for each group of
-// 2^kGroupLog2 windows, the records owning its first and last windows.
+// Group map of a table of records (CopyOutTensor, CopyInSeg) whose windows
+// are consecutive (record t owns windows [win0_t, win0_{t+1})): for each group
+// of 2^kGroupLog2 windows, the records owning its first and last windows.
+template <typename T = CopyOutTensor>
 static void build_group_map(OpTable &op)
 {
-    const CopyOutTensor *T = reinterpret_cast<const CopyOutTensor *>(op.members.data());
+    const T *R = reinterpret_cast<const T *>(op.members.data());
     const int64_t win = op.n_windows;
     const int64_t ng = (win + (int64_t{1} << kGroupLog2) - 1) >> kGroupLog2;
     op.columns.resize(static_cast<size_t>(ng));
     int32_t t0 = 0;
     for (int64_t j = 0; j < ng; ++j) {
         const int64_t w0 = j << kGroupLog2, w1 = std::min(win, (j + 1) << kGroupLog2) - 1;
-        while (t0 + 1 < op.n && T[t0 + 1].win0 <= w0) ++t0;     // owner of the group's first window
+        while (t0 + 1 < op.n && R[t0 + 1].win0 <= w0) ++t0;     // owner of the group's first window
         int32_t t1 = t0;
-        while (t1 + 1 < op.n && T[t1 + 1].win0 <= w1) ++t1;     // owner of its last window
+        while (t1 + 1 < op.n && R[t1 + 1].win0 <= w1) ++t1;     // owner of its last window
         op.columns[j] = ColumnWindow{t0, t1 - t0 + 1};
     }
 }
@@ -312,33 +313,38 @@ int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdp
     }
 
     {   // all-gather copy-in: each parameter owns bytes [A_t, A_{t+1}) of the
-        // row: its cast shard, then zero gap bytes up to the next slot
+        // row, its cast shard then zero gap bytes up to the next slot, cut
+        // into windows of its own
         OpTable &op = plan->copy_in;
         op.op = kOpCopyIn;
         op.B = plan->B;
-        std::vector<CopyInMember> mem;
+        int64_t win = 0;
         for (int32_t t = 0; t < n; ++t) {
             const int64_t next = (t + 1 < n) ? plan->A[t + 1] : plan->B;
             if (next == plan->A[t]) continue;
-            CopyInMember m{};
+            CopyInSeg m{};
             m.A = plan->A[t];
-            m.A_next = next;
             m.P = plan->P[t];
-            m.slot = t;
+            m.win0 = static_cast<int32_t>(win);
+            m.param = t;
             m.src_dt = static_cast<int16_t>(plan->params[t].storage_dtype);
             m.dst_dt = static_cast<int16_t>(plan->params[t].param_dtype);
             op.add(m);
-            mem.push_back(m);
+            op.table_params.push_back(t);
+            win += copy_in_windows(next - m.A);
+            if (win > kMaxGridX) { err = "plan_buckets: all-gather row needs too many workgroups"; return FSDPPACK_EINVAL; }
             op.src_bytes += plan->P[t] * dtype_bytes(m.src_dt);
         }
         op.dst_bytes = plan->B;
-        if (op.windows(kLineBytes - 1) > kMaxGridX) { err = "plan_buckets: all-gather row needs too many workgroups"; return FSDPPACK_EINVAL; }
-        op.n_windows = static_cast<int32_t>(op.windows(0));
-        // member map: the members each stretch of the row overlaps (the
-        // members tile [0, B) in order)
-        op.map_lg = build_record_map(op.columns, plan->B, 0, mem.size(), [&](size_t i) {
-            return std::make_pair(mem[i].A, mem[i].A_next);
-        });
+        op.n_windows = static_cast<int32_t>(win);
+        // group map with split windows (WindowGroup)
+        build_group_map<CopyInSeg>(op);
+        const CopyInSeg *R = reinterpret_cast<const CopyInSeg *>(op.members.data());
+        for (ColumnWindow &g : op.columns) {
+            const int32_t count = g.count;
+            g.count = count == 1 ? INT32_MAX : count == 2 ? R[g.first + 1].win0 : -count;
+        }
+        static_assert(sizeof(ColumnWindow) == sizeof(WindowGroup), "the same map entries");
     }
 
     {   // all-gather copy-out: each parameter's bytes cut into windows; a

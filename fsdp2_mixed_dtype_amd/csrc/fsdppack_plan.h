@@ -22,14 +22,14 @@ namespace fsdppack {
 // geometry.
 struct OpTable {
     int32_t op = kOpPack;
-    std::vector<unsigned char> members;   // PackMember / CopyInMember / CopyOutTensor records
-    std::vector<ColumnWindow> columns;    // record map (pack, copy-in, flat ops: per 2^map_lg bytes of a row;
-                                          // copy-out, write-back: per window group)
+    std::vector<unsigned char> members;   // PackMember / CopyInSeg / CopyOutTensor / FlatMember records
+    std::vector<ColumnWindow> columns;    // record map (pack, flat ops: per 2^map_lg bytes of a row;
+                                          // copy-in, copy-out, write-back: per window group)
     std::vector<int32_t> table_params;    // pointer-table entry -> parameter index
     int32_t n = 0;                        // records
-    int32_t n_windows = 0;                // workgroups per launch (pack / copy-in: destination window-aligned)
+    int32_t n_windows = 0;                // workgroups per launch (pack, flat copy-in: destination window-aligned)
     int32_t gx = 0;                       // pack: windows per row, less the spare one
-    int32_t map_lg = kWindowLog2;         // pack, copy-in, flat ops: log2 of the bytes per map entry
+    int32_t map_lg = kWindowLog2;         // pack, flat ops: log2 of the bytes per map entry
     int32_t group_lg = 0;                 // pack: log2 of the rows interleaved per row group
     int32_t rows = 1;                     // pack: rows of the launch (W; 1 for a flat layout)
     int64_t flat_n = 0;                   // flat ops: the flat parameter's real length N
@@ -54,12 +54,13 @@ struct OpTable {
     }
     // Workgroups of a launch whose destination starts `shift` bytes past a
     // cache-line boundary: the pack gives every row gx + 1 windows (enough
-    // for any alignment of the row), the copy-in cuts its row at line
-    // boundaries of memory, and the copy-out's and write-back's windows
-    // start at each parameter's first byte.
+    // for any alignment of the row), the flat copy-in cuts its row at line
+    // boundaries of memory, the copy-in gives each parameter's segment the
+    // windows its worst alignment needs, and the copy-out's and write-back's
+    // windows start at each parameter's first byte.
     int64_t windows(int32_t shift) const
     {
-        if (op == kOpCopyOut || op == kOpWriteBack || op == kOpWriteBackFlat) return n_windows;
+        if (op == kOpCopyIn || op == kOpCopyOut || op == kOpWriteBack || op == kOpWriteBackFlat) return n_windows;
         if (dst_bytes == 0) return 0;
         if (op == kOpPack) return (static_cast<int64_t>(gx) + 1) * (dst_bytes / (S * dtype_bytes(reduce_dt)));
         return (shift + dst_bytes + kWindowBytes - 1) >> kWindowLog2;

@@ -55,12 +55,13 @@ def gathered_copy_out_layout():
     ]
 
 
-def gathered_copy_in_layout():
+def small_segment_copy_in_layout():
     """A W=4 layout of 40 small parameters (1-12 rows of 1-9 columns) whose
-    all-gather segments are a few vectors long, so that copy-in windows span
-    many segments (the kernel's vector-by-vector gather); storage -> param
-    dtypes cycle through all four pairs.  Returns (shapes, storage dtypes,
-    param dtypes, W)."""
+    all-gather segments are a few vectors long (most of them shorter than a
+    window, many with a zero gap), so that nearly every copy-in window is a
+    short range at both ends of a segment; storage -> param dtypes cycle
+    through all four pairs.  Returns (shapes, storage dtypes, param dtypes,
+    W)."""
     BF16, FP32 = 1, 2
     pairs = [(BF16, BF16), (FP32, BF16), (BF16, FP32), (FP32, FP32)]
     shapes = [(1 + (i * 7) % 12, 1 + (i * 5) % 9) for i in range(40)]

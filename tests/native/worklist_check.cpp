@@ -47,7 +47,6 @@ static int64_t g_direct = 0;      // pack windows taking the direct copy (column
 static int64_t g_direct_st = 0;   // pack windows taking it through the stretch records
 static int64_t g_direct_in = 0;   // copy-in windows taking it
 static int64_t g_gather = 0;      // copy-out windows gathered element by element
-static int64_t g_gather_in = 0;   // copy-in windows gathered vector by vector
 
 #define CHECK(cond, ...)                                                  \
     do {                                                                  \
@@ -68,7 +67,7 @@ static bool check_range(const char *name, int32_t w, int32_t shift, const RangeR
 {
     CHECK(dtype_ok(g.src_dt) && dtype_ok(g.dst_dt), "%s: window %d bad dtype", name, w);
     CHECK(g.lo >= 0 && g.lo < g.hi, "%s: window %d empty or reversed range", name, w);
-    const bool by_record = op.op == kOpPack || op.op == kOpWriteBackFlat || op.op == kOpCopyInFlat;
+    const bool by_record = op.op == kOpPack || op.op == kOpCopyIn || op.op == kOpWriteBackFlat || op.op == kOpCopyInFlat;
     if (g.param < 0) {
         // a flat copy-in's padding: +0 only, no source and no table entry
         CHECK(op.op == kOpCopyInFlat && g.valid == 0 && g.table_side == kTableIsSource,
@@ -107,7 +106,7 @@ static bool check_op(const char *name, const OpTable &op, int32_t W, int32_t shi
     a.divisor = 1.0f;
     CHECK(a.n_windows == op.windows(shift) && (shift != 0 || a.n_windows == op.n_windows), "%s: window count", name);
     const size_t rec = op.op == kOpPack ? sizeof(PackMember)
-                       : op.op == kOpCopyIn ? sizeof(CopyInMember)
+                       : op.op == kOpCopyIn ? sizeof(CopyInSeg)
                        : (op.op == kOpCopyInFlat || op.op == kOpWriteBackFlat) ? sizeof(FlatMember)
                                                                                   : sizeof(CopyOutTensor);
     CHECK(op.members.size() == static_cast<size_t>(op.n) * rec, "%s: member table size", name);
@@ -118,8 +117,10 @@ static bool check_op(const char *name, const OpTable &op, int32_t W, int32_t shi
     CHECK(op.op != kOpPack ||
               (op.columns.size() == static_cast<size_t>((op.S * dtype_bytes(op.reduce_dt) + stretch - 1) / stretch) &&
                op.table_params.size() == static_cast<size_t>(op.n)), "%s: column map size", name);
-    CHECK(op.op != kOpCopyIn || op.columns.size() == static_cast<size_t>((op.B + stretch - 1) / stretch),
-          "%s: member map size", name);
+    CHECK(op.op != kOpCopyIn ||
+              (op.columns.size() == static_cast<size_t>((op.n_windows + (1 << kGroupLog2) - 1) >> kGroupLog2) &&
+               op.table_params.size() == static_cast<size_t>(op.n)),
+          "%s: copy-in group map size", name);
     CHECK((op.op != kOpCopyInFlat && op.op != kOpWriteBackFlat) ||
               op.columns.size() == static_cast<size_t>((op.flat_n * dtype_bytes(op.reduce_dt) + stretch - 1) / stretch),
           "%s: flat map size", name);
@@ -199,46 +200,32 @@ static bool check_op(const char *name, const OpTable &op, int32_t W, int32_t shi
             }
         }
         if (op.op == kOpCopyIn) {
-            // likewise the copy-in's direct copy of a whole window of one segment
-            DirectWindow d{};
-            if (copy_in_direct(a, w, d)) {
-                int n_rng = 0;
-                bool same = false;
-                for_each_range(a, w, [&](const RangeRef &g) {
-                    ++n_rng;
-                    const int64_t ssz = dtype_bytes(g.src_dt), dsz = dtype_bytes(g.dst_dt);
-                    same = g.hi - g.lo == kWindowBytes / dsz && g.valid >= g.hi && g.src_dt == d.src_dt &&
-                           g.dst_dt == d.dst_dt && static_cast<int64_t>(d.src) == g.src_off + g.lo * ssz &&
-                           d.dst_off == g.dst_off + g.lo * dsz && (a.shift + d.dst_off) % 16 == 0;
-                });
-                CHECK(n_rng == 1 && same, "%s: window %d (shift %d): direct copy-in differs from its range", name, w,
-                      shift);
-                ++g_direct_in;
+            // a copy-in window is one range of one segment (or empty: the
+            // segment's spare window), bounded by line boundaries of memory
+            // or by the segment's own ends; its direct copy, when it takes
+            // one, is exactly that range
+            const CopyInWindow c = copy_in_span(a.columns, a.members, nullptr, a.shift, w);
+            CHECK(ranges <= 1 && (ranges == 1) == (c.y1 > c.y0), "%s: window %d has %d ranges", name, w, ranges);
+            if (ranges == 1) {
+                CHECK((c.y0 == c.s.A || (shift + c.y0) % kLineBytes == 0) &&
+                          (c.y1 == c.A_next || (shift + c.y1) % kLineBytes == 0) && c.y1 - c.y0 <= kWindowBytes,
+                      "%s: window %d (shift %d) writes [%lld,%lld) of a segment [%lld,%lld), off the line boundaries",
+                      name, w, shift, (long long)c.y0, (long long)c.y1, (long long)c.s.A, (long long)c.A_next);
+                CHECK(w == c.s.win0 || c.y0 > c.s.A, "%s: window %d: a segment's later window starts at its first byte",
+                      name, w);
+            } else {
+                CHECK(w > c.s.win0 && c.y0 >= c.A_next, "%s: window %d: an empty window before its segment's end", name,
+                      w);
             }
-            // a gathered copy-in window: every 16-byte vector lies inside the
-            // segment of the record picked for it, which is the record whose
-            // range the walk writes those bytes from, with the same dtypes
-            int64_t y0, y1;
-            int32_t m0, ncand;
-            if (!copy_in_direct(a, w, d) && copy_in_gathered(a, w, y0, y1, m0, ncand)) {
-                std::vector<RangeRef> rs;
-                for_each_range(a, w, [&](const RangeRef &g) { rs.push_back(g); });
-                CHECK(y0 % 16 == 0 && y1 % 16 == 0, "%s: window %d (shift %d): gathered window off 16 bytes", name, w,
-                      shift);
-                for (int64_t y = y0; y < y1; y += 16) {
-                    const CopyInPick p = copy_in_member_at(a, m0, ncand, y);
-                    bool found = false;
-                    for (const RangeRef &g : rs) {
-                        const int64_t esz = dtype_bytes(g.dst_dt);
-                        if (g.dst_off + g.lo * esz <= y && y + 16 <= g.dst_off + g.hi * esz)
-                            found = g.slot == p.m.slot && g.src_dt == p.m.src_dt && g.dst_dt == p.m.dst_dt &&
-                                    g.valid == p.m.P && g.dst_off == p.m.A;
-                    }
-                    CHECK(found && p.m.A <= y && y + 16 <= p.m.A_next,
-                          "%s: window %d (shift %d): gathered vector at byte %lld differs from the walk", name, w, shift,
-                          (long long)y);
-                }
-                ++g_gather_in;
+            DirectWindow d{};
+            if (ranges == 1 && copy_in_direct(c, shift, d)) {
+                const RangeRef g = copy_in_range(c);
+                const int64_t ssz = dtype_bytes(g.src_dt), dsz = dtype_bytes(g.dst_dt);
+                CHECK(g.hi - g.lo == kWindowBytes / dsz && g.valid >= g.hi && g.src_dt == d.src_dt && g.dst_dt == d.dst_dt &&
+                          static_cast<int64_t>(d.src) == g.src_off + g.lo * ssz && d.dst_off == g.dst_off + g.lo * dsz &&
+                          (a.shift + d.dst_off) % 16 == 0,
+                      "%s: window %d (shift %d): direct copy-in differs from its range", name, w, shift);
+                ++g_direct_in;
             }
         }
         if (op.op == kOpCopyOut) {
@@ -275,11 +262,12 @@ static bool check_op(const char *name, const OpTable &op, int32_t W, int32_t shi
             CHECK((ranges == 0) == spare, "%s: window %d (row %d, shift %d) has %d ranges", name, w, r, shift, ranges);
             row0 = shift + r * rb;
             row1 = row0 + rb;
-        } else if (op.op != kOpWriteBack && op.op != kOpWriteBackFlat) {
-            // (write-back windows past a rank's real elements are empty)
+        } else if (op.op != kOpWriteBack && op.op != kOpWriteBackFlat && op.op != kOpCopyIn) {
+            // (write-back windows past a rank's real elements, and a copy-in
+            // segment's spare window, are empty)
             CHECK(ranges > 0, "%s: window %d has no range", name, w);
         }
-        if ((op.op == kOpPack || op.op == kOpCopyIn || op.op == kOpCopyInFlat) && ranges > 0)
+        if ((op.op == kOpPack || op.op == kOpCopyInFlat) && ranges > 0)
             CHECK((lo == row0 || lo % kLineBytes == 0) && (hi == row1 || hi % kLineBytes == 0) &&
                       hi - lo <= kWindowBytes,
                   "%s: window %d (shift %d) writes [%lld,%lld) from the aligned origin, off the line boundaries",
@@ -444,9 +432,9 @@ int main(int argc, char **argv)
     std::printf("OK %s%zu buckets, windows:", flat ? "flat, " : "", plan.buckets.size());
     for (const BucketPlan &b : plan.buckets) std::printf(" %d (rows/group %d)", b.pack.n_windows, 1 << b.pack.group_lg);
     std::printf(" copy_in %d copy_out %d; direct pack windows %lld, stretch-direct pack windows %lld, "
-                "direct copy-in windows %lld, gathered copy-in windows %lld, gathered copy-out windows %lld\n",
+                "direct copy-in windows %lld, gathered copy-out windows %lld\n",
                 plan.copy_in.n_windows, plan.copy_out.n_windows, static_cast<long long>(g_direct),
                 static_cast<long long>(g_direct_st),
-                static_cast<long long>(g_direct_in), static_cast<long long>(g_gather_in), static_cast<long long>(g_gather));
+                static_cast<long long>(g_direct_in), static_cast<long long>(g_gather));
     return 0;
 }

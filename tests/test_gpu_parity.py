@@ -536,19 +536,19 @@ def test_copy_out_gathered_windows():
         plan.destroy()
 
 
-def test_copy_in_gathered_segments_every_dtype_pair():
-    """Copy-in windows over many small segments in all four storage -> param
-    dtype pairs: gathered vector by vector when the all-gather buffer is
-    16-byte aligned, walked segment by segment when it starts 4, 8 or 12 bytes
-    past a 16-byte boundary; shards at element offsets 0-2."""
-    from conftest import gathered_copy_in_layout
-    shapes, sdt, pdt, W = gathered_copy_in_layout()
+def test_copy_in_small_segments_every_dtype_pair():
+    """Copy-in windows of many small segments in all four storage -> param
+    dtype pairs, with the all-gather buffer 0, 4, 8 or 12 bytes past a
+    16-byte boundary (segment ends off the line and vector boundaries of
+    memory); shards at element offsets 0-2."""
+    from conftest import small_segment_copy_in_layout
+    shapes, sdt, pdt, W = small_segment_copy_in_layout()
     n = len(shapes)
     w = wl.custom(shapes, [FP32] * n, [0] * n, W, storage_dtypes=sdt, param_dtypes=pdt)
     ref = oracle.plan(w.descs(), W)
     plan = fp.plan_buckets(w.descs(), W)
     for row_off in (0, 4, 8, 12):
-        print(f"[copy-in gathered] all-gather buffer at +{row_off} bytes", flush=True)
+        print(f"[copy-in small segments] all-gather buffer at +{row_off} bytes", flush=True)
         ag = Guarded(W * plan.B, None, row_off)
         ag_ref = np.full((W, ref.B), POISON, np.uint8)
         for r in range(W):
@@ -566,8 +566,8 @@ def test_copy_in_gathered_segments_every_dtype_pair():
 
 def _edge_layouts():
     """The pack's edge layouts plus a crowded one: tiny parameters with
-    zero-size ones between them, so that gathered copy-in and copy-out
-    windows meet empty segments and empty rank chunks."""
+    zero-size ones between them, so that copy-in windows meet empty
+    segments and gathered copy-out windows empty rank chunks."""
     return [
         wl.custom([(0, 4), (0, 1)], [FP32, BF16], [FP32, FP32], 4),
         wl.custom([(1,)], [BF16], [FP32], 8, param_dtypes=[FP32]),

@@ -87,18 +87,19 @@ def test_gathered_copy_out_windows_are_exercised(checker):
         assert gathered >= 2, res.stdout
 
 
-def test_gathered_copy_in_windows_are_exercised(checker):
-    """The small-segment layout of the GPU tests produces copy-in windows
-    that the kernel gathers vector by vector (checked against the walk)."""
-    from conftest import gathered_copy_in_layout
-    shapes, sdt, pdt, W = gathered_copy_in_layout()
+def test_small_segment_copy_in_windows(checker):
+    """The small-segment layout of the GPU tests: every segment gets windows
+    of its own (at least one each), each one range, which the checker walks
+    at every row offset."""
+    from conftest import small_segment_copy_in_layout
+    shapes, sdt, pdt, W = small_segment_copy_in_layout()
     n = len(shapes)
     w = wl.custom(shapes, [FP32] * n, [0] * n, W, storage_dtypes=sdt, param_dtypes=pdt)
     text = f"{W} {n}\n" + "".join(" ".join(str(int(x)) for x in d) + "\n" for d in w.descs())
     res = subprocess.run([checker], input=text, capture_output=True, text=True, timeout=600)
     assert res.returncode == 0 and res.stdout.startswith("OK"), res.stdout + res.stderr[-3000:]
-    gathered = int(res.stdout.rsplit("gathered copy-in windows", 1)[1].split()[0].rstrip(","))
-    assert gathered >= 2, res.stdout
+    windows = int(res.stdout.split(" copy_in ", 1)[1].split()[0])
+    assert windows >= n, res.stdout
 
 
 def test_worklists_in_bounds_random(checker):
