@@ -199,7 +199,7 @@ struct WindowArgs {
     int64_t flat_n;          // flat layout: the flat parameter's real length N (its rows hold S = c each)
     int64_t S;               // pack: row length in elements; flat ops: c, a rank's row length
     int64_t B;               // copy-in row bytes / copy-out row stride
-    const void *members;     // PackMember / CopyInMember / CopyOutTensor / FlatMember records
+    const void *members;     // PackMember / CopyInSeg / CopyOutTensor / FlatMember records
     const void *columns;     // ColumnWindow map: per 2^map_lg bytes of a row (pack, copy-in) or of
                              // flat positions (flat ops), or per group of windows (copy-out, write-back)
     const uint64_t *table;   // device pointer table (by record for the pack and flat ops, else by parameter)
