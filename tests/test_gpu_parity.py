@@ -915,18 +915,28 @@ def _pattern_bits(idx):
     return ((h >> 16) & 0x3FFF) | ((h >> 1) & 0x8000)
 
 
+def _oracle_sampled_pack(bits: np.ndarray) -> np.ndarray:
+    """The oracle's fp32 pack of bf16 gradient elements given by their bits,
+    element by element: a one-row layout of just these elements."""
+    m = int(bits.size)
+    ref = oracle.plan([(m, 1, BF16, FP32, FP32, BF16)], 1)
+    return oracle.pack(ref, 0, [bits.astype(np.uint16).view(np.uint16)])[0].view(np.uint32)
+
+
 def test_pack_and_write_back_beyond_2_31_elements():
     """One bf16 gradient of 2^31 + 2^20 + 3 elements (4.3 GB) and a small fp32
-    one, W=2: the [2, S] fp32 pack (8.6 GB) and rank 1's write-back divided by 2
-    checked on sampled positions against the definition (element offsets past
-    2^31 exercise every 64-bit index path)."""
+    one, W=2: the [2, S] fp32 pack (8.6 GB) and rank 1's write-back divided by 2,
+    checked on sampled positions against the oracle, which computes each
+    sampled output from the same seeded input (element offsets past 2^31
+    exercise every 64-bit index path)."""
     numel = (1 << 31) + (1 << 20) + 3
     print(f"[beyond 2^31] numel={numel}", flush=True)
     descs = [(numel, 1, BF16, FP32, FP32, BF16), (5, 3, FP32, FP32, FP32, BF16)]
     plan = fp.plan_buckets(descs, 2)
     b = plan.buckets[0]
     P0, P1, S = b.P[0], b.P[1], b.S
-    assert (b.O[0], b.O[1]) == (0, P0) and P0 == (numel + 1) // 2
+    ref = oracle.plan(descs, 2)
+    assert (b.O[0], b.O[1]) == (ref.buckets[0].O[0], ref.buckets[0].O[1]) == (0, P0) and P0 == ref.P[0]
     g0 = torch.empty(numel, dtype=torch.bfloat16, device=DEV)
     bits0 = g0.view(torch.int16)
     chunk = 1 << 28
@@ -945,15 +955,25 @@ def test_pack_and_write_back_beyond_2_31_elements():
         rng.integers(0, P0, 20000),
         np.arange(max(0, (1 << 31) - P0 - 4), min(P0, (1 << 31) - P0 + 4)),   # flat source index 2^31 on rank 1
         np.arange(0, 4), np.arange(P0 - 4, P0)]))
+    # the small tensor's part of the rows, from the oracle's pack of the whole
+    # layout with the large tensor replaced by a 2-element stand-in (its own
+    # columns are not compared here)
+    small_ref = oracle.plan([(2, 1, BF16, FP32, FP32, BF16), descs[1]], 2)
+    small_rows = oracle.pack(small_ref, 0, [np.zeros(2, np.uint16), g1_h])
+    pad_ref = oracle.plan([(1, 1, BF16, FP32, FP32, BF16)], 2)      # rank 1's chunk is all padding
+    pad_bits = oracle.pack(pad_ref, 0, [np.zeros(1, np.uint16)])[1].view(np.uint32)[0]
+    rows_want = {}
     for r in (0, 1):
         src = r * P0 + j
-        want = np.where(src < numel, (_pattern_bits(src).astype(np.int64) & 0xFFFF) << 16, 0).astype(np.uint32)
+        real = src < numel
+        want = np.zeros(j.size, np.uint32)
+        want[real] = _oracle_sampled_pack((_pattern_bits(src[real]).astype(np.int64) & 0xFFFF).astype(np.uint16))
+        want[~real] = pad_bits                 # past the tensor's end: the oracle's padding
+        rows_want[r] = want
         got = out.view(torch.int32)[torch.from_numpy(r * S + j).to(DEV)].cpu().numpy().view(np.uint32)
         assert np.array_equal(got, want), f"rank {r}: pack of the large tensor differs"
         small = out[r * S + P0: r * S + P0 + P1].cpu().numpy()
-        v = max(0, min(P1, 15 - r * P1))
-        assert np.array_equal(small[:v].view(np.uint32), g1_h[r * P1: r * P1 + v].view(np.uint32))
-        assert not np.any(small[v:].view(np.uint32))
+        assert np.array_equal(small.view(np.uint32), small_rows[r, small_ref.buckets[0].O[1]:].view(np.uint32))
 
     # write-back of rank 1 (its row of the pack standing in for the reduced row), divided by 2
     v0 = numel - P0
@@ -961,9 +981,11 @@ def test_pack_and_write_back_beyond_2_31_elements():
     dst1 = torch.empty(max(0, min(P1, 15 - P1)), dtype=torch.float32, device=DEV)
     fp.reduce_scatter_copy_out(plan, 0, 1, out[S:2 * S], [dst0, dst1], 2.0)
     torch.cuda.synchronize()
-    jj = j[j < v0]
-    row1 = (_pattern_bits(P0 + jj).astype(np.int64) & 0xFFFF) << 16
-    want = (row1.astype(np.uint32).view(np.float32) / np.float32(2.0)).view(np.uint32)   # exact: a power of two
+    keep = j < v0
+    jj = j[keep]
+    # the oracle's write-back of the sampled elements of the oracle's row 1
+    wb_ref = oracle.plan([(int(jj.size), 1, FP32, FP32, FP32, BF16)], 1)
+    want = oracle.rs_copy_out(wb_ref, 0, 0, rows_want[1][keep].view(np.float32), 2.0)[0].view(np.uint32)
     got = dst0.view(torch.int32)[torch.from_numpy(jj).to(DEV)].cpu().numpy().view(np.uint32)
     assert np.array_equal(got, want), "write-back of the large tensor differs"
     del g0, out, dst0
