@@ -104,9 +104,34 @@ int ensure_device(fsdppack_plan *p)
     return FSDPPACK_OK;
 }
 
-// Find or stage the device table for pointer set `key` (more than
-// kInlineLarge pointers) in cache `c`, ordered before work enqueued next on
-// `stream`.  Caller holds plan->mu.
+// The cached device table holding pointer set `key`, if any (*out = NULL
+// when there is none), ordered before work enqueued next on `stream`.
+// Caller holds plan->mu.
+int find_table(PtrCache &c, const std::vector<uint64_t> &key, hipStream_t stream, PtrSlot **out)
+{
+    *out = nullptr;
+    for (PtrSlot &s : c.slots) {
+        if (s.live && s.key == key) {
+            bool ordered = false;
+            for (void *st : s.streams) ordered |= (st == stream);
+            if (!ordered) {
+                // first use on this stream: wait once for the upload
+                hipError_t e;
+                if ((e = hipStreamWaitEvent(stream, static_cast<hipEvent_t>(s.ready), 0)) != hipSuccess)
+                    return hip_fail(e, "hipStreamWaitEvent");
+                s.streams.push_back(stream);
+            }
+            s.last_use = ++c.clock;
+            g_counters[2]++;
+            *out = &s;
+            return FSDPPACK_OK;
+        }
+    }
+    return FSDPPACK_OK;
+}
+
+// Find or stage the device table for pointer set `key` in cache `c`, ordered
+// before work enqueued next on `stream`.  Caller holds plan->mu.
 //
 // Replacing a cached table needs no device-wide synchronisation:
 //  * the slot's previous upload read its pinned staging buffer, so that one
@@ -119,22 +144,8 @@ int ensure_device(fsdppack_plan *p)
 int acquire_table(PtrCache &c, const std::vector<uint64_t> &key, hipStream_t stream, PtrSlot **out)
 {
     hipError_t e;
-    for (PtrSlot &s : c.slots) {
-        if (s.live && s.key == key) {
-            bool ordered = false;
-            for (void *st : s.streams) ordered |= (st == stream);
-            if (!ordered) {
-                // first use on this stream: wait once for the upload
-                if ((e = hipStreamWaitEvent(stream, static_cast<hipEvent_t>(s.ready), 0)) != hipSuccess)
-                    return hip_fail(e, "hipStreamWaitEvent");
-                s.streams.push_back(stream);
-            }
-            s.last_use = ++c.clock;
-            g_counters[2]++;
-            *out = &s;
-            return FSDPPACK_OK;
-        }
-    }
+    if (int rc = find_table(c, key, stream, out)) return rc;
+    if (*out != nullptr) return FSDPPACK_OK;
     PtrSlot *victim = nullptr;
     for (PtrSlot &s : c.slots)
         if (!s.live) { victim = &s; break; }
@@ -200,21 +211,39 @@ int run_op(fsdppack_plan *p, const OpTable &op, size_t cache_index, const std::v
     if (int rc = ensure_device(p)) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     WindowArgs args = op.args(true, shift);
+    // Up to kInlineSmall pointers travel in the launch's arguments.  A larger
+    // set uses its cached device table when there is one (on MI355X a
+    // 960-entry argument table made a launch about 0.5 us longer than a device
+    // table), else its pointers travel in the arguments (up to kInlineLarge)
+    // and the set is uploaded behind this launch, for the next call that
+    // passes it; beyond kInlineLarge the device table is staged first.
     const uint64_t *inline_ptrs = nullptr;
-    if (key.size() <= static_cast<size_t>(kInlineLarge)) {
-        inline_ptrs = key.data();                    // the kernel reads them from its arguments
-        g_counters[6]++;
+    bool upload_after = false;
+    if (key.size() <= static_cast<size_t>(kInlineSmall)) {
+        inline_ptrs = key.data();
     } else {
         PtrSlot *slot = nullptr;
-        if (int rc = acquire_table(p->caches[cache_index], key, s, &slot)) return rc;
-        args.table = slot->d_table;
+        if (int rc = find_table(p->caches[cache_index], key, s, &slot)) return rc;
+        if (slot == nullptr && key.size() <= static_cast<size_t>(kInlineLarge)) {
+            inline_ptrs = key.data();
+            upload_after = true;
+        } else {
+            if (slot == nullptr)
+                if (int rc = acquire_table(p->caches[cache_index], key, s, &slot)) return rc;
+            args.table = slot->d_table;
+        }
     }
+    if (inline_ptrs != nullptr) g_counters[6]++;
     args.base = base;
     args.rank = rank;
     args.divisor = divisor;
     const int le = launch_windows(args, inline_ptrs, static_cast<int32_t>(key.size()), stream, ev0, ev1);
     if (le != 0) return hip_fail(static_cast<hipError_t>(le), what);
     g_counters[0]++;
+    if (upload_after) {
+        PtrSlot *slot = nullptr;
+        if (int rc = acquire_table(p->caches[cache_index], key, s, &slot)) return rc;
+    }
     if (trace_on())
         std::fprintf(stderr, "fsdppack: %s: %d workgroups, %lld bytes read, %lld bytes written\n", what,
                      args.n_windows, static_cast<long long>(op.src_bytes), static_cast<long long>(op.dst_bytes));

@@ -54,18 +54,21 @@
  *    streams; its device tables are uploaded on the first compute call that
  *    needs them (a synchronous copy) on the device current at that time, and
  *    the plan may only be used on that device afterwards.
- *  - Per-call pointer arrays of up to 960 entries travel to the kernel in its
- *    own launch arguments: nothing is uploaded or cached, so a call with new
- *    pointers (gradients allocated afresh every backward) costs the same as
- *    one with known pointers.  Larger arrays reach the kernel through device
- *    tables cached by content, 16 per operation (per bucket for the pack): a
- *    call with a new set uploads one asynchronously on `stream`; a 17th
- *    distinct set replaces the least recently used table, waiting on the host
- *    for that table's own earlier upload only and making `stream` wait on the
- *    device for work other streams had enqueued when they used it (no
- *    device-wide synchronisation); calls with a known set record no event and
- *    upload nothing.  A stream passed to a compute call must stay valid until
- *    the plan is destroyed.
+ *  - Per-call pointer arrays reach the kernel in one of two ways.  Up to 64
+ *    entries travel in the launch's own arguments: nothing is uploaded or
+ *    cached, so a call with new pointers (gradients allocated afresh every
+ *    backward) costs the same as one with known pointers.  Larger arrays use
+ *    device tables cached by content, 16 per operation (per bucket for the
+ *    pack): a call whose set is cached uses its table; a call with a new set
+ *    of up to 960 entries passes it in the launch arguments and then uploads
+ *    it asynchronously on `stream`, behind its launch, for the next call
+ *    with that set (a larger new set is uploaded before the launch).  A 17th
+ *    distinct set replaces the least recently used table, waiting on the
+ *    host for that table's own earlier upload only and making `stream` wait
+ *    on the device for work other streams had enqueued when they used it (no
+ *    device-wide synchronisation); calls with a cached set record no event
+ *    and upload nothing.  A stream passed to a compute call must stay valid
+ *    until the plan is destroyed.
  *  - A launch's grid is bounded by the hardware's 32-bit work-item counts:
  *    the planner rejects (EINVAL) a unit whose launches would need more
  *    workgroups (about 128 GiB written by one launch).

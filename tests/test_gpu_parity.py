@@ -259,6 +259,59 @@ def test_new_pointers_every_call_inline():
     plan.destroy()
 
 
+def test_mid_size_pointer_sets_inline_then_cached():
+    """A bucket of 200 members (more than the small argument table holds): a
+    pointer set seen for the first time travels in the launch arguments and
+    is uploaded behind the launch; the same set next time uses its cached
+    device table (also from another stream, which waits for the upload);
+    every result is exact."""
+    w = _many_params(200, W=4, seed=3)
+    ref = oracle.plan(w.descs(), w.world)
+    plan = fp.plan_buckets(w.descs(), w.world)
+    assert any(len(b.members) > 64 for b in plan.buckets)
+    side = torch.cuda.Stream(device=DEV)
+    sets = []
+    for k in range(2):
+        grads = wl.make_grads(w, seed=700 + k)
+        sets.append((grads, [to_dev(g, t.grad_dtype, k % 3) for g, t in zip(grads, w.tensors)]))
+    big = [bi for bi, b in enumerate(plan.buckets) if len(b.members) > 64]
+
+    def pack(k, stream=None):
+        grads, g_dev = sets[k]
+        outs = []
+        for bi in big:
+            b = plan.buckets[bi]
+            out = torch.empty(w.world * b.S, dtype=fp.TORCH_DTYPE[b.dtype], device=DEV)
+            if stream is None:
+                fp.pack_reduce_scatter_input(plan, bi, g_dev, out)
+            else:
+                with torch.cuda.stream(stream):
+                    fp.pack_reduce_scatter_input(plan, bi, g_dev, out)
+            outs.append((bi, out))
+        return grads, outs
+
+    def check(grads, outs, stream=None):
+        (stream or torch.cuda.current_stream()).synchronize()
+        for bi, out in outs:
+            assert np.array_equal(host_bytes(out), oracle.pack(ref, bi, grads).view(np.uint8).reshape(-1))
+
+    nb = len(big)
+    c0 = fp.counters()
+    check(*pack(0))                                       # new set: inline, then uploaded
+    c1 = fp.counters()
+    assert c1[6] - c0[6] == nb and c1[1] - c0[1] == nb and c1[2] - c0[2] == 0
+    check(*pack(0))                                       # same set: its cached table
+    c2 = fp.counters()
+    assert c2[6] - c1[6] == 0 and c2[1] - c1[1] == 0 and c2[2] - c1[2] == nb
+    check(*pack(1))                                       # another new set
+    c3 = fp.counters()
+    assert c3[6] - c2[6] == nb and c3[1] - c2[1] == nb
+    check(*pack(1, side), side)                           # the cached table from another stream
+    c4 = fp.counters()
+    assert c4[6] - c3[6] == 0 and c4[2] - c3[2] == nb
+    plan.destroy()
+
+
 def _many_params(k=1000, W=4, seed=0):
     """A unit of more parameters than a launch's arguments carry (the pointer
     table goes through the device-table cache)."""

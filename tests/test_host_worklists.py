@@ -83,7 +83,7 @@ def test_gathered_copy_out_windows_are_exercised(checker):
         text = f"{W} {len(w.descs())}\n" + "".join(" ".join(str(int(x)) for x in d) + "\n" for d in w.descs())
         res = subprocess.run([checker], input=text, capture_output=True, text=True, timeout=600)
         assert res.returncode == 0 and res.stdout.startswith("OK"), res.stdout + res.stderr[-3000:]
-        gathered = int(res.stdout.rsplit("gathered copy-out windows", 1)[1].split()[0])
+        gathered = int(res.stdout.rsplit("gathered copy-out windows", 1)[1].split()[0].rstrip(","))
         assert gathered >= 2, res.stdout
 
 
