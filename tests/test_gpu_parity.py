@@ -312,6 +312,49 @@ def test_mid_size_pointer_sets_inline_then_cached():
     plan.destroy()
 
 
+def test_mid_size_pointer_churn_on_two_streams():
+    """20 pointer sets of a 200-member bucket, more than the 16 cached tables,
+    passed twice in turn on two streams: every call either finds its set
+    cached or passes it in the launch arguments (uploading it behind the
+    launch, evicting an older table that a kernel on the other stream may
+    have read); every result is exact."""
+    w = _many_params(200, W=4, seed=5)
+    ref = oracle.plan(w.descs(), w.world)
+    plan = fp.plan_buckets(w.descs(), w.world)
+    side = torch.cuda.Stream(device=DEV)
+    main = torch.cuda.current_stream()
+    n_sets = 20
+    sets = []
+    for k in range(n_sets):
+        grads = wl.make_grads(w, seed=900 + k)
+        sets.append((grads, [to_dev(g, t.grad_dtype, k % 3) for g, t in zip(grads, w.tensors)]))
+    b = plan.buckets[0]
+    c0 = fp.counters()
+    results = []
+    for rnd in range(2):
+        for k in range(n_sets):
+            stream = side if (k // 3 + rnd) % 2 else main
+            grads, g_dev = sets[k]
+            out = torch.empty(w.world * b.S, dtype=fp.TORCH_DTYPE[b.dtype], device=DEV)
+            stream.wait_stream(main)
+            with torch.cuda.stream(stream):
+                fp.pack_reduce_scatter_input(plan, 0, g_dev, out)
+            out.record_stream(stream)
+            results.append((k, out))
+        k = n_sets - 1                                    # the last set again: now cached
+        out = torch.empty(w.world * b.S, dtype=fp.TORCH_DTYPE[b.dtype], device=DEV)
+        fp.pack_reduce_scatter_input(plan, 0, sets[k][1], out)
+        results.append((k, out))
+    torch.cuda.synchronize()
+    c1 = fp.counters()
+    for k, out in results:
+        assert np.array_equal(host_bytes(out), oracle.pack(ref, 0, sets[k][0]).view(np.uint8).reshape(-1)), k
+    assert c1[0] - c0[0] == len(results)
+    assert c1[2] - c0[2] >= 2                             # the repeated sets found their tables
+    assert c1[4] - c0[4] > 0 and c1[5] - c0[5] > 0        # tables replaced, some used by the other stream
+    plan.destroy()
+
+
 def _many_params(k=1000, W=4, seed=0):
     """A unit of more parameters than a launch's arguments carry (the pointer
     table goes through the device-table cache)."""
