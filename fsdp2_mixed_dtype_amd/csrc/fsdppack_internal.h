@@ -743,6 +743,39 @@ FSDPPACK_HD inline void flat_window(const WindowArgs &a, int32_t w, F &&f)
     }
 }
 
+// Whether FSDP1 flat copy-in window w is one whole window inside a single
+// parameter's piece of the rank's row, with every element real and its
+// destination on 16-byte vectors; fills `d` (source: the piece's pointer
+// plus the window's offset in it; destination: the window's row offset).
+// With one or two records in the window's map stretches, both records and
+// pointers (table in record order) are read in one round trip.  The window
+// then equals the single range flat_window<true> produces for it.
+FSDPPACK_HD inline bool flat_copy_in_direct(const WindowArgs &a, int32_t w, DirectWindow &d)
+{
+    const FSDPPACK_TABLE ColumnWindow *C = (const FSDPPACK_TABLE ColumnWindow *)a.columns;
+    const int lg = a.reduce_dt == kBF16 ? 1 : 2;          // log2 of the row's element size
+    int64_t y0, y1;
+    window_span(w, a.shift, a.S << lg, y0, y1);
+    if (y1 - y0 != kWindowBytes || ((a.shift + y0) & 15) != 0) return false;
+    const int64_t base = static_cast<int64_t>(a.rank) * a.S;   // flat position of row element 0
+    const int64_t f0 = base + (y0 >> lg), f1 = base + (y1 >> lg);
+    if (f1 > a.flat_n) return false;                      // padding in the window
+    const ColumnWindow e0 = C[f0 >> (a.map_lg - lg)], e1 = C[(f1 - 1) >> (a.map_lg - lg)];
+    const int32_t m0 = e0.first, n = e1.first + e1.count - m0;
+    if (n < 1 || n > 2) return false;
+    const FlatMember r0 = read_record<FlatMember>(a.members, m0);
+    const FlatMember r1 = read_record<FlatMember>(a.members, m0 + n - 1);
+    const uint64_t p0 = table_entry(a, m0), p1 = table_entry(a, m0 + n - 1);
+    const bool second = f0 >= r1.F;                       // records tile the flat positions in order
+    const FlatMember &fm = second ? r1 : r0;
+    if (f0 < fm.F || f1 > fm.F + fm.numel) return false;
+    d.src = (second ? p1 : p0) + static_cast<uint64_t>((f0 - imax(fm.F, base)) * dtype_bytes(fm.dt));
+    d.dst_off = y0;
+    d.src_dt = fm.dt;
+    d.dst_dt = a.reduce_dt;
+    return true;
+}
+
 template <typename F>
 FSDPPACK_HD inline void for_each_range(const WindowArgs &a, int32_t w, F &&f)
 {

@@ -589,7 +589,9 @@ __global__ void __launch_bounds__(kBlock) window_kernel(WindowArgs a, PtrTab<N> 
         else if (t.dt == kBF16) copy_out_gather<uint16_t>(a, t, e0, e1);
         else copy_out_gather<uint32_t>(a, t, e0, e1);
     } else if constexpr (OP == kOpCopyInFlat) {
-        flat_window<true>(a, w, body);
+        DirectWindow d;
+        if (flat_copy_in_direct(a, w, d)) run_direct<true>(d, a.base);
+        else flat_window<true>(a, w, body);
     } else if constexpr (OP == kOpWriteBackFlat) {
         if (a.divisor != 1.0f)     // uniform across the launch
             flat_window<false>(a, w, [&](const RangeRef &g) { run_range<true, true>(g, a.base, a.divisor); });

@@ -45,6 +45,7 @@ using namespace fsdppack;
 static std::string g_fail;
 static int64_t g_direct = 0;      // pack windows taking the direct copy (column map)
 static int64_t g_direct_st = 0;   // pack windows taking it through the stretch records
+static int64_t g_direct_flat = 0;   // flat copy-in windows taking the direct copy
 static int64_t g_direct_in = 0;   // copy-in windows taking it
 static int64_t g_gather = 0;      // copy-out windows gathered element by element
 
@@ -131,6 +132,11 @@ static bool check_op(const char *name, const OpTable &op, int32_t W, int32_t shi
     // gradient at 2^32 * (m + 1), plus one element for odd m (bf16 sources
     // then start 2 bytes past a dword)
     std::vector<uint64_t> ptrs(static_cast<size_t>(op.n));
+    if (op.op == kOpCopyInFlat) {
+        const FlatMember *M = reinterpret_cast<const FlatMember *>(op.members.data());
+        for (int32_t m = 0; m < op.n; ++m)
+            ptrs[m] = (static_cast<uint64_t>(m + 1) << 32) + ((m & 1) ? dtype_bytes(M[m].dt) : 0);
+    }
     if (op.op == kOpPack) {
         const PackMember *M = reinterpret_cast<const PackMember *>(op.members.data());
         for (int32_t m = 0; m < op.n; ++m)
@@ -226,6 +232,28 @@ static bool check_op(const char *name, const OpTable &op, int32_t W, int32_t shi
                           (a.shift + d.dst_off) % 16 == 0,
                       "%s: window %d (shift %d): direct copy-in differs from its range", name, w, shift);
                 ++g_direct_in;
+            }
+        }
+        if (op.op == kOpCopyInFlat) {
+            // the flat copy-in's direct copy of a whole window of one piece
+            // is exactly the one range the walk gives for it
+            DirectWindow d{};
+            WindowArgs at = a;
+            at.table = ptrs.data();
+            if (flat_copy_in_direct(at, w, d)) {
+                int n_rng = 0;
+                bool same = false;
+                for_each_range(a, w, [&](const RangeRef &g) {
+                    ++n_rng;
+                    const int64_t ssz = dtype_bytes(g.src_dt), dsz = dtype_bytes(g.dst_dt);
+                    same = g.hi - g.lo == kWindowBytes / dsz && g.valid >= g.hi && g.src_dt == d.src_dt &&
+                           g.dst_dt == d.dst_dt && g.table_side == kTableIsSource &&
+                           d.src == ptrs[g.slot] + static_cast<uint64_t>(g.src_off + g.lo * ssz) &&
+                           d.dst_off == g.dst_off + g.lo * dsz && (a.shift + d.dst_off) % 16 == 0;
+                });
+                CHECK(n_rng == 1 && same, "%s: window %d (shift %d): direct flat copy-in differs from its range", name,
+                      w, shift);
+                ++g_direct_flat;
             }
         }
         if (op.op == kOpCopyOut) {
@@ -432,9 +460,9 @@ int main(int argc, char **argv)
     std::printf("OK %s%zu buckets, windows:", flat ? "flat, " : "", plan.buckets.size());
     for (const BucketPlan &b : plan.buckets) std::printf(" %d (rows/group %d)", b.pack.n_windows, 1 << b.pack.group_lg);
     std::printf(" copy_in %d copy_out %d; direct pack windows %lld, stretch-direct pack windows %lld, "
-                "direct copy-in windows %lld, gathered copy-out windows %lld\n",
+                "direct copy-in windows %lld, gathered copy-out windows %lld, direct flat copy-in windows %lld\n",
                 plan.copy_in.n_windows, plan.copy_out.n_windows, static_cast<long long>(g_direct),
                 static_cast<long long>(g_direct_st),
-                static_cast<long long>(g_direct_in), static_cast<long long>(g_gather));
+                static_cast<long long>(g_direct_in), static_cast<long long>(g_gather), static_cast<long long>(g_direct_flat));
     return 0;
 }
