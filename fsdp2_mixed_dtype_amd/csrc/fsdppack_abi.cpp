@@ -141,7 +141,11 @@ int find_table(PtrCache &c, const std::vector<uint64_t> &key, hipStream_t stream
 //    upload in stream order, and those on any other stream that used the slot
 //    are waited for on the device (an event recorded on that stream now,
 //    waited on by `stream`).
-int acquire_table(PtrCache &c, const std::vector<uint64_t> &key, hipStream_t stream, PtrSlot **out)
+// With may_wait false the table is only staged if that takes no host wait:
+// when the slot to replace still has its previous upload in flight, *out is
+// NULL and nothing is enqueued.
+int acquire_table(PtrCache &c, const std::vector<uint64_t> &key, hipStream_t stream, PtrSlot **out,
+                  bool may_wait = true)
 {
     hipError_t e;
     if (int rc = find_table(c, key, stream, out)) return rc;
@@ -153,9 +157,15 @@ int acquire_table(PtrCache &c, const std::vector<uint64_t> &key, hipStream_t str
         victim = &c.slots[0];
         for (PtrSlot &s : c.slots)
             if (s.last_use < victim->last_use) victim = &s;
-        if ((e = hipEventSynchronize(static_cast<hipEvent_t>(victim->ready))) != hipSuccess)
-            return hip_fail(e, "hipEventSynchronize(previous upload)");
-        g_counters[7]++;
+        if (!may_wait) {
+            e = hipEventQuery(static_cast<hipEvent_t>(victim->ready));
+            if (e == hipErrorNotReady) return FSDPPACK_OK;      // skip: its staging is still being read
+            if (e != hipSuccess) return hip_fail(e, "hipEventQuery(previous upload)");
+        } else {
+            if ((e = hipEventSynchronize(static_cast<hipEvent_t>(victim->ready))) != hipSuccess)
+                return hip_fail(e, "hipEventSynchronize(previous upload)");
+            g_counters[7]++;
+        }
         size_t used = 0;
         for (void *st : victim->streams) {
             if (st == stream) continue;
@@ -216,7 +226,8 @@ int run_op(fsdppack_plan *p, const OpTable &op, size_t cache_index, const std::v
     // 960-entry argument table made a launch about 0.5 us longer than a device
     // table), else its pointers travel in the arguments (up to kInlineLarge)
     // and the set is uploaded behind this launch, for the next call that
-    // passes it; beyond kInlineLarge the device table is staged first.
+    // passes it, when that needs no host wait; beyond kInlineLarge the device
+    // table is staged first.
     const uint64_t *inline_ptrs = nullptr;
     bool upload_after = false;
     if (key.size() <= static_cast<size_t>(kInlineSmall)) {
@@ -241,8 +252,10 @@ int run_op(fsdppack_plan *p, const OpTable &op, size_t cache_index, const std::v
     if (le != 0) return hip_fail(static_cast<hipError_t>(le), what);
     g_counters[0]++;
     if (upload_after) {
+        // cache the set for the next call that passes it, unless that would
+        // make the host wait (the table to replace is still being uploaded)
         PtrSlot *slot = nullptr;
-        if (int rc = acquire_table(p->caches[cache_index], key, s, &slot)) return rc;
+        if (int rc = acquire_table(p->caches[cache_index], key, s, &slot, false)) return rc;
     }
     if (trace_on())
         std::fprintf(stderr, "fsdppack: %s: %d workgroups, %lld bytes read, %lld bytes written\n", what,

@@ -62,10 +62,12 @@
  *    pack): a call whose set is cached uses its table; a call with a new set
  *    of up to 960 entries passes it in the launch arguments and then uploads
  *    it asynchronously on `stream`, behind its launch, for the next call
- *    with that set (a larger new set is uploaded before the launch).  A 17th
- *    distinct set replaces the least recently used table, waiting on the
- *    host for that table's own earlier upload only and making `stream` wait
- *    on the device for work other streams had enqueued when they used it (no
+ *    with that set, unless the table it would replace is still being
+ *    uploaded (then the set is not cached: the call never waits).  A larger
+ *    new set is uploaded before its launch; when it replaces the least
+ *    recently used table the call waits on the host for that table's own
+ *    earlier upload only.  A replacement makes `stream` wait on the device
+ *    for work other streams had enqueued when they used the table (no
  *    device-wide synchronisation); calls with a cached set record no event
  *    and upload nothing.  A stream passed to a compute call must stay valid
  *    until the plan is destroyed.

@@ -316,8 +316,8 @@ def test_mid_size_pointer_churn_on_two_streams():
     """20 pointer sets of a 200-member bucket, more than the 16 cached tables,
     passed twice in turn on two streams: every call either finds its set
     cached or passes it in the launch arguments (uploading it behind the
-    launch, evicting an older table that a kernel on the other stream may
-    have read); every result is exact."""
+    launch when that needs no host wait, possibly replacing an older table
+    that a kernel on the other stream read); every result is exact."""
     w = _many_params(200, W=4, seed=5)
     ref = oracle.plan(w.descs(), w.world)
     plan = fp.plan_buckets(w.descs(), w.world)
@@ -350,8 +350,8 @@ def test_mid_size_pointer_churn_on_two_streams():
     for k, out in results:
         assert np.array_equal(host_bytes(out), oracle.pack(ref, 0, sets[k][0]).view(np.uint8).reshape(-1)), k
     assert c1[0] - c0[0] == len(results)
-    assert c1[2] - c0[2] >= 2                             # the repeated sets found their tables
-    assert c1[4] - c0[4] > 0 and c1[5] - c0[5] > 0        # tables replaced, some used by the other stream
+    assert c1[1] - c0[1] >= 16                            # the first sets filled the free tables
+    assert c1[7] - c0[7] == 0                             # an upload behind a launch never waits on the host
     plan.destroy()
 
 
