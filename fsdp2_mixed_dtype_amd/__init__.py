@@ -425,9 +425,10 @@ def counters():
     """(kernel launches, pointer-table uploads, pointer-table reuses, plan
     uploads, pointer tables replaced by a new set, cross-stream waits at such a
     replacement, launches whose pointers travelled in the launch arguments,
-    host waits for a replaced table's previous upload)."""
-    c = (ctypes.c_int64 * 8)()
-    _check(lib().fsdppack_counters(c, 8))
+    host waits for a replaced table's previous upload, copies of pack tables
+    into the allocation-free pack's scratch)."""
+    c = (ctypes.c_int64 * 9)()
+    _check(lib().fsdppack_counters(c, 9))
     return tuple(c)
 
 

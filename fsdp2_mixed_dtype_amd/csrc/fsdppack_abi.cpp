@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -25,9 +26,24 @@ thread_local std::string g_error;
 thread_local void *g_next_start = nullptr;   // events for the next launch on this thread
 thread_local void *g_next_stop = nullptr;
 // launches, table uploads, table reuses, plan uploads, table evictions,
-// cross-stream waits at an eviction, launches with their pointers inline
-constexpr int kCounters = 8;
+// cross-stream waits at an eviction, launches with their pointers inline,
+// host waits for a replaced table's upload, allocation-free table copies
+constexpr int kCounters = 9;
 std::atomic<int64_t> g_counters[kCounters];
+std::atomic<uint64_t> g_plan_serial{0};
+
+// What each device's scratch holds: the image the last allocation-free pack
+// on that device copied there (plan serial, and region: -1 for the plan-wide
+// image, else the bucket) and an event recorded after the copy, on the
+// copying stream.  A call whose image is the one held, with that copy
+// complete, copies nothing.
+struct ScratchHolds {
+    uint64_t serial = 0;
+    int32_t region = 0;
+    hipEvent_t copied = nullptr;
+};
+std::mutex g_scratch_mu;
+ScratchHolds g_scratch_holds[kMaxDevices];
 
 int fail(int code, const std::string &msg)
 {
@@ -286,6 +302,7 @@ int make_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdpp
         delete p;
         return fail(rc, err);
     }
+    p->serial = ++g_plan_serial;
     *out_plan = p;
     return FSDPPACK_OK;
 }
@@ -392,40 +409,67 @@ int fsdppack_pack_reduce_scatter_input_noalloc(const fsdppack_plan *cplan, int32
     if (op.table_params.size() > static_cast<size_t>(kInlineLarge))
         return fail(FSDPPACK_EINVAL, "pack_reduce_scatter_input_noalloc: the bucket has more than " +
                                          std::to_string(kInlineLarge) + " members");
-    // the bucket's tables, each at a 256-byte boundary of the scratch
-    auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
-    const int64_t mb = static_cast<int64_t>(op.members.size());
-    const int64_t cb = static_cast<int64_t>(op.columns.size() * sizeof(ColumnWindow));
-    const int64_t sb = static_cast<int64_t>(op.stretches.size() * sizeof(PackStretch));
-    const int64_t c_off = up(mb), s_off = c_off + up(cb);
-    if (s_off + sb > kScratchBytes)
+    // the bucket's tables: in the plan-wide image, else in its own
+    const bool whole = !plan->scratch_image.empty() && plan->scratch_at[bucket] >= 0;
+    if (!whole && op.scratch_image.empty() && op.scratch_need > 0)
         return fail(FSDPPACK_EINVAL, "pack_reduce_scatter_input_noalloc: the bucket's tables need " +
-                                         std::to_string(s_off + sb) + " bytes, more than the " +
+                                         std::to_string(op.scratch_need) + " bytes, more than the " +
                                          std::to_string(kScratchBytes) + "-byte scratch");
     const int32_t shift = static_cast<int32_t>(reinterpret_cast<uintptr_t>(out) & (kLineBytes - 1));
     if (op.windows(shift) <= 0) return FSDPPACK_OK;
     void *sp = nullptr;
     hipError_t e = static_cast<hipError_t>(scratch_address(&sp));
     if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
-    char *base = static_cast<char *>(sp);
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    // the plan's host tables live as long as the plan, so the copies may
-    // complete after this call returns
-    if (mb && (e = hipMemcpyAsync(base, op.members.data(), mb, hipMemcpyHostToDevice, st)) != hipSuccess)
-        return hip_fail(e, "hipMemcpyAsync(member table to scratch)");
-    if (cb && (e = hipMemcpyAsync(base + c_off, op.columns.data(), cb, hipMemcpyHostToDevice, st)) != hipSuccess)
-        return hip_fail(e, "hipMemcpyAsync(column map to scratch)");
-    if (sb && (e = hipMemcpyAsync(base + s_off, op.stretches.data(), sb, hipMemcpyHostToDevice, st)) != hipSuccess)
-        return hip_fail(e, "hipMemcpyAsync(stretch records to scratch)");
+    int dev = -1;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return hip_fail(e, "hipGetDevice");
+    const unsigned char *img = whole ? plan->scratch_image.data() : op.scratch_image.data();
+    const size_t img_bytes = whole ? plan->scratch_image.size() : op.scratch_image.size();
+    const int32_t region = whole ? -1 : bucket;
+    char *base = static_cast<char *>(sp) + (whole ? plan->scratch_at[bucket] : 0);
+    {
+        // Copy the image unless the scratch holds it; when it does and the
+        // copy that put it there may still be in flight, the launch waits for
+        // that copy on the device (whichever stream made it).  The plan's host
+        // images live as long as the plan, and destroying a plan that copied
+        // waits for the device, so a copy may complete after this call returns.
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        ScratchHolds &h = g_scratch_holds[dev];
+        if (h.copied == nullptr && (e = hipEventCreateWithFlags(&h.copied, hipEventDisableTiming)) != hipSuccess) {
+            h.copied = nullptr;
+            return hip_fail(e, "hipEventCreate(scratch copy)");
+        }
+        if (h.serial == plan->serial && h.region == region) {
+            e = hipEventQuery(h.copied);
+            if (e == hipErrorNotReady) {
+                if ((e = hipStreamWaitEvent(static_cast<hipStream_t>(stream), h.copied, 0)) != hipSuccess)
+                    return hip_fail(e, "hipStreamWaitEvent(scratch copy)");
+            } else if (e != hipSuccess) {
+                return hip_fail(e, "hipEventQuery(scratch copy)");
+            }
+        } else {
+            h.serial = 0;   // unknown until the copy is enqueued
+            plan->staged.store(true);
+            e = hipMemcpyAsync(static_cast<char *>(sp), img, img_bytes, hipMemcpyHostToDevice,
+                               static_cast<hipStream_t>(stream));
+            if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(tables to scratch)");
+            if ((e = hipEventRecord(h.copied, static_cast<hipStream_t>(stream))) != hipSuccess)
+                return hip_fail(e, "hipEventRecord(scratch copy)");
+            h.serial = plan->serial;
+            h.region = region;
+            g_counters[8]++;
+        }
+    }
     WindowArgs args = op.args(false, shift);
     args.members = base;
-    args.columns = base + c_off;
-    args.stretches = sb ? reinterpret_cast<const PackStretch *>(base + s_off) : nullptr;
+    args.columns = base + op.scratch_c_off;
+    args.stretches = op.narrow ? reinterpret_cast<const PackStretch *>(base + op.scratch_s_off) : nullptr;
     args.table = nullptr;
     args.base = static_cast<char *>(out);
-    std::vector<uint64_t> key(op.table_params.size());
-    for (size_t m = 0; m < key.size(); ++m) key[m] = reinterpret_cast<uint64_t>(grads[op.table_params[m]]);
-    const int le = launch_windows(args, key.data(), static_cast<int32_t>(key.size()), stream, ev0, ev1);
+    // the pointer table travels in the launch's arguments
+    uint64_t key[kInlineLarge];
+    const int32_t nk = static_cast<int32_t>(op.table_params.size());
+    for (int32_t m = 0; m < nk; ++m) key[m] = reinterpret_cast<uint64_t>(grads[op.table_params[m]]);
+    const int le = launch_windows(args, key, nk, stream, ev0, ev1);
     if (le != 0) return hip_fail(static_cast<hipError_t>(le), "pack_reduce_scatter_input_noalloc");
     g_counters[0]++;
     g_counters[6]++;
@@ -596,7 +640,9 @@ void fsdppack_plan_destroy(fsdppack_plan *plan)
     if (!plan_ok(plan)) return;
     {
         std::lock_guard<std::mutex> lock(plan->mu);
-        if (plan->uploaded) (void)hipDeviceSynchronize();   // no kernel may still read the tables
+        // no kernel may still read the tables, and no copy into the scratch
+        // still read the plan's host images
+        if (plan->uploaded || plan->staged.load()) (void)hipDeviceSynchronize();
         for (PtrCache &c : plan->caches) {
             for (PtrSlot &s : c.slots) {
                 if (s.ready) (void)hipEventDestroy(static_cast<hipEvent_t>(s.ready));

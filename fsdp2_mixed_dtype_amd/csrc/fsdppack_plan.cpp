@@ -26,6 +26,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <cstring>
 #include <map>
 #include <utility>
 
@@ -374,7 +375,53 @@ int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdp
         op.dst_bytes = op.src_bytes;
         build_group_map(op);
     }
+    build_scratch_images(plan);
     return FSDPPACK_OK;
+}
+
+void build_scratch_images(fsdppack_plan *plan)
+{
+    auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+    const size_t nb = plan->buckets.size();
+    plan->scratch_image.clear();
+    plan->scratch_at.assign(nb, -1);
+    auto eligible = [](const OpTable &op) {
+        return op.scratch_need > 0 && op.table_params.size() <= static_cast<size_t>(kInlineLarge);
+    };
+    auto lay = [](const OpTable &op, unsigned char *img) {
+        if (!op.members.empty()) std::memcpy(img, op.members.data(), op.members.size());
+        if (!op.columns.empty())
+            std::memcpy(img + op.scratch_c_off, op.columns.data(), op.columns.size() * sizeof(ColumnWindow));
+        if (!op.stretches.empty())
+            std::memcpy(img + op.scratch_s_off, op.stretches.data(), op.stretches.size() * sizeof(PackStretch));
+    };
+    int64_t total = 0;
+    for (BucketPlan &b : plan->buckets) {
+        OpTable &op = b.pack;
+        op.scratch_c_off = up(static_cast<int64_t>(op.members.size()));
+        op.scratch_s_off = op.scratch_c_off + up(static_cast<int64_t>(op.columns.size() * sizeof(ColumnWindow)));
+        op.scratch_need = op.scratch_s_off + static_cast<int64_t>(op.stretches.size() * sizeof(PackStretch));
+        op.scratch_image.clear();
+        if (eligible(op)) total += up(op.scratch_need);
+    }
+    if (total > 0 && total <= kScratchBytes) {
+        plan->scratch_image.assign(static_cast<size_t>(total), 0);
+        int64_t at = 0;
+        for (size_t bi = 0; bi < nb; ++bi) {
+            const OpTable &op = plan->buckets[bi].pack;
+            if (!eligible(op)) continue;
+            plan->scratch_at[bi] = at;
+            lay(op, plan->scratch_image.data() + at);
+            at += up(op.scratch_need);
+        }
+        return;
+    }
+    for (BucketPlan &b : plan->buckets) {
+        OpTable &op = b.pack;
+        if (!eligible(op) || op.scratch_need > kScratchBytes) continue;
+        op.scratch_image.assign(static_cast<size_t>(op.scratch_need), 0);
+        lay(op, op.scratch_image.data());
+    }
 }
 
 void build_pack_stretches(const OpTable &op, PackStretch *out)
@@ -573,6 +620,7 @@ int build_plan_flat(const fsdppack_param_desc *params, int32_t n, int32_t world,
         op.dst_bytes = op.src_bytes;
         build_group_map(op);
     }
+    build_scratch_images(plan);
     return FSDPPACK_OK;
 }
 

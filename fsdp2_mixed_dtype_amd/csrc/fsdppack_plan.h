@@ -8,6 +8,7 @@
 // builds the record tables and maps the kernels read (one per operation).
 #pragma once
 
+#include <atomic>
 #include <cstdint>
 #include <mutex>
 #include <string>
@@ -42,6 +43,14 @@ struct OpTable {
                                           // than 2^32 source bytes, so the plan holds stretch records
                                           // (one per column-map entry) for the direct windows
     std::vector<PackStretch> stretches;   // pack: the stretch records (narrow tables only)
+    // pack: where the allocation-free pack finds the member table, column map
+    // and stretch records in the device scratch (byte offsets from the
+    // bucket's place there: members at 0, the others each at a 256-byte
+    // boundary; scratch_need bytes in all), and the bucket's own image of them
+    // when the plan has no plan-wide image (empty when they need more than
+    // kScratchBytes or the pointer table has more than kInlineLarge entries)
+    std::vector<unsigned char> scratch_image;
+    int64_t scratch_c_off = 0, scratch_s_off = 0, scratch_need = 0;
     void *d_members = nullptr;            // device copies (owned by the plan)
     void *d_columns = nullptr;
     void *d_stretches = nullptr;
@@ -148,6 +157,15 @@ struct fsdppack_plan {
     std::vector<fsdppack::BucketPlan> buckets;
     fsdppack::OpTable copy_in, copy_out;
     fsdppack::OpTable write_back_all;         // every bucket's write-back in one launch (two or more buckets)
+    uint64_t serial = 0;                      // unique among the process's plans, never reused
+    // allocation-free pack: every eligible bucket's pack tables one after
+    // another, as they sit in the device scratch (bucket bi at scratch_at[bi];
+    // -1 for a bucket with nothing to pack or more than kInlineLarge
+    // pointers), when they fit it together, so one copy serves every bucket;
+    // empty otherwise
+    std::vector<unsigned char> scratch_image;
+    std::vector<int64_t> scratch_at;
+    mutable std::atomic<bool> staged{false};  // an allocation-free pack has copied from this plan's images
 
     // device state (guarded by mu)
     std::mutex mu;
@@ -171,6 +189,11 @@ int build_plan_flat(const fsdppack_param_desc *params, int32_t n, int32_t world,
 // Real elements of parameter t on rank r: the rank chunk's (per-parameter
 // layout) or the piece inside the rank's flat positions (flat layout).
 int64_t shard_elements(const fsdppack_plan &plan, int32_t t, int32_t r);
+
+// Lay every bucket's pack tables out as the allocation-free pack copies them
+// into the device scratch: one plan-wide image when they fit it together,
+// else one image per bucket that fits alone.
+void build_scratch_images(fsdppack_plan *plan);
 
 // The stretch records of a narrow pack table: for each column-map stretch,
 // the members overlapping its bytes extended one window to the left, when

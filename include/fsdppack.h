@@ -192,11 +192,19 @@ int fsdppack_pack_reduce_scatter_input(const fsdppack_plan *plan, int32_t bucket
 
 /* The same fused reduce-scatter pack, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
- * that forbid hipMalloc): it allocates nothing.  The bucket's pack tables are
- * copied (hipMemcpyAsync from the plan's host memory, on `stream`) into a
- * library-owned device scratch of 1 MiB per GPU, held until the process
- * ends, and the pointers travel in the launch arguments; the plan's own
- * device tables are neither used nor created.  Same arguments, result and
+ * that forbid hipMalloc): it allocates nothing.  The kernel reads the
+ * bucket's pack tables from a library-owned device scratch of 1 MiB per GPU,
+ * held until the process ends, and the pointers travel in the launch
+ * arguments; the plan's own device tables are neither used nor created.
+ * The plan lays its tables out for the scratch when it is built: every
+ * bucket's in one image when they fit together, else one image per bucket.
+ * A call copies its image there (one hipMemcpyAsync from the plan's host
+ * memory, on `stream`) only when the scratch does not already hold it;
+ * when it does but the copy that put it there may still be running, the
+ * call's stream waits for that copy on the device (hipStreamWaitEvent).  At
+ * its first call on a device it looks up the scratch's address and creates
+ * the event that marks those copies.  Destroying a plan that this entry
+ * point copied from synchronises the device.  Same arguments, result and
  * errors as fsdppack_pack_reduce_scatter_input, and also EINVAL when the
  * bucket has more than 960 members or its tables exceed the scratch (about
  * 13 000 column-map stretches).  Every call on a GPU shares that GPU's
@@ -295,7 +303,8 @@ int fsdppack_time_next_launch(void *start_event, void *stop_event);
  * [5] = cross-stream waits enqueued at such a replacement, [6] = launches
  * whose pointers travelled in the launch arguments, [7] = host waits for a
  * replaced table's previous upload (the only waits a compute call makes; no
- * compute call synchronises the device).  The first min(n, 8) entries are
+ * compute call synchronises the device), [8] = copies of pack tables into
+ * the allocation-free pack's scratch.  The first min(n, 9) entries are
  * written. */
 int fsdppack_counters(int64_t *counters, int32_t n);
 

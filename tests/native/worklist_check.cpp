@@ -48,6 +48,7 @@ static int64_t g_direct_st = 0;   // pack windows taking it through the stretch 
 static int64_t g_direct_flat = 0;   // flat copy-in windows taking the direct copy
 static int64_t g_direct_in = 0;   // copy-in windows taking it
 static int64_t g_gather = 0;      // copy-out windows gathered element by element
+static int64_t g_scratch_images = 0;   // buckets whose tables fit the allocation-free pack's scratch
 
 #define CHECK(cond, ...)                                                  \
     do {                                                                  \
@@ -371,6 +372,56 @@ int main(int argc, char **argv)
             }
         }
     }
+    // the allocation-free pack's scratch images: each eligible bucket's three
+    // tables, each at a 256-byte boundary, byte for byte -- all of them in
+    // one plan-wide image, one after another, when they fit it together,
+    // else each bucket that fits alone in its own
+    {
+        int64_t total = 0;
+        auto eligible = [](const OpTable &op) {
+            return op.scratch_need > 0 && op.table_params.size() <= static_cast<size_t>(kInlineLarge);
+        };
+        for (const BucketPlan &b : plan.buckets)
+            if (eligible(b.pack)) total += (b.pack.scratch_need + 255) / 256 * 256;
+        const bool whole = total > 0 && total <= kScratchBytes;
+        if (whole != !plan.scratch_image.empty() || plan.scratch_at.size() != plan.buckets.size()) {
+            g_fail = "plan-wide scratch image present when it should not be, or missing";
+            return fail();
+        }
+        int64_t next = 0;
+        for (size_t bi = 0; bi < plan.buckets.size(); ++bi) {
+            const OpTable &op = plan.buckets[bi].pack;
+            const size_t mb = op.members.size(), cb = op.columns.size() * sizeof(ColumnWindow),
+                         sb = op.stretches.size() * sizeof(PackStretch);
+            bool ok = op.scratch_c_off % 256 == 0 && op.scratch_s_off % 256 == 0 &&
+                      op.scratch_c_off >= static_cast<int64_t>(mb) &&
+                      op.scratch_s_off >= op.scratch_c_off + static_cast<int64_t>(cb) &&
+                      op.scratch_need == op.scratch_s_off + static_cast<int64_t>(sb);
+            const unsigned char *img = nullptr;
+            if (whole) {
+                ok = ok && op.scratch_image.empty() && plan.scratch_at[bi] == (eligible(op) ? next : -1);
+                if (eligible(op)) {
+                    img = plan.scratch_image.data() + next;
+                    next += (op.scratch_need + 255) / 256 * 256;
+                    ok = ok && next <= static_cast<int64_t>(plan.scratch_image.size());
+                }
+            } else {
+                const bool own = eligible(op) && op.scratch_need <= kScratchBytes;
+                ok = ok && plan.scratch_at[bi] == -1 && own == !op.scratch_image.empty() &&
+                     (!own || op.scratch_image.size() == static_cast<size_t>(op.scratch_need));
+                if (own) img = op.scratch_image.data();
+            }
+            if (ok && img)
+                ok = (mb == 0 || std::memcmp(img, op.members.data(), mb) == 0) &&
+                     (cb == 0 || std::memcmp(img + op.scratch_c_off, op.columns.data(), cb) == 0) &&
+                     (sb == 0 || std::memcmp(img + op.scratch_s_off, op.stretches.data(), sb) == 0);
+            if (!ok) {
+                g_fail = "pack[" + std::to_string(bi) + "] scratch image does not hold the pack's tables";
+                return fail();
+            }
+            if (img) ++g_scratch_images;
+        }
+    }
     const int64_t row_esz = flat ? dtype_bytes(plan.copy_in.reduce_dt) : 4;
     for (int32_t r : flat ? ranks : std::vector<int32_t>{0}) {
         for (int32_t u : kShiftUnits) {
@@ -460,9 +511,11 @@ int main(int argc, char **argv)
     std::printf("OK %s%zu buckets, windows:", flat ? "flat, " : "", plan.buckets.size());
     for (const BucketPlan &b : plan.buckets) std::printf(" %d (rows/group %d)", b.pack.n_windows, 1 << b.pack.group_lg);
     std::printf(" copy_in %d copy_out %d; direct pack windows %lld, stretch-direct pack windows %lld, "
-                "direct copy-in windows %lld, gathered copy-out windows %lld, direct flat copy-in windows %lld\n",
+                "direct copy-in windows %lld, gathered copy-out windows %lld, direct flat copy-in windows %lld, "
+                "scratch images %lld\n",
                 plan.copy_in.n_windows, plan.copy_out.n_windows, static_cast<long long>(g_direct),
                 static_cast<long long>(g_direct_st),
-                static_cast<long long>(g_direct_in), static_cast<long long>(g_gather), static_cast<long long>(g_direct_flat));
+                static_cast<long long>(g_direct_in), static_cast<long long>(g_gather), static_cast<long long>(g_direct_flat),
+                static_cast<long long>(g_scratch_images));
     return 0;
 }

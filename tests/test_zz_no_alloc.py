@@ -3,7 +3,8 @@ the ordinary pack, byte for byte, through the C ABI: two calls in a row on
 the library's shared device scratch, the second with a smaller layout (so
 any table left from the first call must not leak into it), plus a bucket of
 fp32 gradients into bf16 and a plan that is never used by an allocating call
-(its device tables are never created)."""
+(its device tables are never created), and the scratch's reuse of the
+tables it already holds."""
 import numpy as np
 import pytest
 
@@ -69,6 +70,76 @@ def test_no_alloc_pack_matches_the_pack_twice_then_smaller():
             assert np.array_equal(a, z), f"{name}: bucket {bi} differs from the ordinary pack"
             assert dc[0] == 1                     # one launch ...
             assert dc[1] == 0 and dc[3] == 0      # ... no pointer table and no plan table created
+
+
+class _Layout:
+    """A layout's gradients on the GPU, the ordinary pack of each bucket, and
+    a second plan for the allocation-free calls."""
+
+    def __init__(self, w):
+        self.w = w
+        self.g = [_dev(g, t.grad_dtype) for g, t in zip(wl.make_grads(w), w.tensors)]
+        ref = fp.plan_buckets(w.descs(), w.world)
+        self.ref = []
+        for bi, b in enumerate(ref.buckets):
+            a = torch.empty(w.world * b.S, dtype=fp.TORCH_DTYPE[b.dtype], device=DEV)
+            fp.pack_reduce_scatter_input(ref, bi, self.g, a)
+            self.ref.append(a)
+        torch.cuda.synchronize()
+        ref.destroy()
+        self.plan = fp.plan_buckets(w.descs(), w.world)
+        self.outs = []
+
+    def call(self, bi):
+        b = self.plan.buckets[bi]
+        z = torch.full((self.w.world * b.S,), 9, dtype=fp.TORCH_DTYPE[b.dtype], device=DEV)
+        c0 = fp.counters()[8]
+        fp.pack_reduce_scatter_input_noalloc(self.plan, bi, self.g, z)
+        self.outs.append((bi, z))
+        return fp.counters()[8] - c0
+
+    def check(self, name):
+        for bi, z in self.outs:
+            assert torch.equal(z.view(torch.uint8), self.ref[bi].view(torch.uint8)), \
+                f"{name}: bucket {bi} differs from the ordinary pack"
+        self.plan.destroy()
+
+
+def test_no_alloc_pack_copies_its_tables_only_when_the_scratch_lacks_them():
+    """The scratch keeps the last image copied into it.  A plan whose buckets
+    fit it together copies once for all of them, and again only after another
+    plan's image has replaced it; a plan whose buckets fit only one at a time
+    copies at every change of bucket.  A call on a second stream, ordered
+    after the first but issued while the copy may still be running, reuses
+    the image (its stream waits for the copy).  Every result equals the
+    ordinary pack's."""
+    a = _Layout(wl.custom([(4 * 1025, 3), (5,), (64, 2), (4 * 700, 8), (33, 7)],
+                          [BF16, FP32, BF16, FP32, BF16], [FP32, BF16, FP32, BF16, 0], 4, seed=12))
+    b = _Layout(wl.tiny())
+    # two buckets of about 620 KB of tables each (one large member and 900
+    # one-element members: a column-map entry per window of the 16 MB rows)
+    big = [(2 * 4 * 1024 * 1024,)] + [(1,)] * 900 + [(2 * 8 * 1024 * 1024,)] + [(1,)] * 900
+    c = _Layout(wl.custom(big, [FP32] * 901 + [BF16] * 901, [FP32] * 901 + [BF16] * 901, 2, seed=13))
+    assert len(a.plan.buckets) == 2 and len(c.plan.buckets) == 2
+    print("[no-alloc] residency: one plan, both buckets", flush=True)
+    assert a.call(0) == 1
+    assert a.call(1) == 0 and a.call(0) == 0
+    s2 = torch.cuda.Stream()
+    s2.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s2):
+        assert a.call(1) == 0
+    torch.cuda.current_stream().wait_stream(s2)
+    torch.cuda.synchronize()
+    assert a.call(0) == 0
+    print("[no-alloc] residency: another plan in between", flush=True)
+    assert b.call(0) == 1 and b.call(0) == 0
+    assert a.call(1) == 1
+    print("[no-alloc] residency: buckets that fit one at a time", flush=True)
+    assert c.call(0) == 1 and c.call(0) == 0
+    assert c.call(1) == 1 and c.call(0) == 1 and c.call(1) == 1
+    torch.cuda.synchronize()
+    for name, lay in (("two-bucket", a), ("tiny", b), ("one bucket at a time", c)):
+        lay.check(name)
 
 
 def test_no_alloc_pack_rejects_what_it_cannot_hold():
