@@ -2,9 +2,12 @@
 //
 // Argument checks are synchronous and on the host; every compute call then
 // enqueues one launch of a window kernel on the caller's stream.
-// Per-call device pointers (grads, shards, params) reach the kernel through a
-// small device table cached by content (see PtrCache in fsdppack_plan.h), so
-// a training loop that passes the same buffers each step pays no upload.
+// Per-call device pointers (grads, shards, params) travel in the launch's
+// arguments when there are at most 64 of them; larger sets reach the kernel
+// through a device table cached by content (see PtrCache in
+// fsdppack_plan.h), so a training loop that passes the same buffers each step
+// pays no upload, and a set of up to 960 that is not cached yet travels in
+// the arguments while its table is uploaded behind the launch.
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>

@@ -41,10 +41,11 @@
 #include "fsdppack_internal.h"
 
 // Device scratch of the allocation-free pack (fsdppack_pack_reduce_scatter_
-// input_noalloc): the bucket's pack tables are copied here on every call
-// instead of living in memory the library allocates.  Each GPU holds its own
-// copy until the process ends; host code reaches it only through the address
-// scratch_address() looks up per device, never through this name.
+// input_noalloc): the plan's pack tables are copied here, when it does not
+// already hold them, instead of living in memory the library allocates.
+// Each GPU holds its own copy until the process ends; host code reaches it
+// only through the address scratch_address() looks up per device, never
+// through this name.
 static __device__ __align__(256) unsigned char scratch[fsdppack::kScratchBytes];
 
 namespace fsdppack {

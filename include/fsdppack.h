@@ -281,8 +281,9 @@ int fsdppack_reduce_scatter_copy_out_all(const fsdppack_plan *plan, int32_t rank
                                          float divide_factor, void *const *shard_grads, void *stream);
 
 /* Free a plan and its device tables.  Synchronises the device first if the
- * plan was ever used there (no kernel may still read its tables).  NULL is a
- * no-op. */
+ * plan was ever used there (no kernel may still read its tables) or the
+ * allocation-free pack copied from it (no copy may still read its host
+ * images).  NULL is a no-op. */
 void fsdppack_plan_destroy(fsdppack_plan *plan);
 
 /* Message of the last failed call on this thread ("" if none). */
