@@ -142,6 +142,36 @@ def test_no_alloc_pack_copies_its_tables_only_when_the_scratch_lacks_them():
         lay.check(name)
 
 
+def test_no_alloc_pack_of_flat_plans_matches_the_pack():
+    """FSDP1 flat plans (one row of W*c elements, +0 past the flat length N)
+    through the allocation-free pack, against the ordinary flat pack: a full
+    size layout of mixed gradient dtypes, and a small one whose output and
+    gradients sit at odd element offsets."""
+    def flat(w):
+        ts = w.tensors
+        return wl.custom([t.shape for t in ts], [t.grad_dtype for t in ts], [FP32] * len(ts), w.world, w.seed,
+                         storage_dtypes=[t.storage_dtype for t in ts], param_dtypes=[BF16] * len(ts))
+
+    cases = [("mixed50m", flat(wl.mixed50m()), 0),
+             ("small", wl.custom([(37, 3), (5,), (64, 2), (700, 8), (33, 7)], [BF16, FP32, BF16, FP32, BF16],
+                                 [FP32] * 5, 4, seed=14, param_dtypes=[BF16] * 5), 1)]
+    for name, w, off in cases:
+        print(f"[no-alloc] flat {name}", flush=True)
+        g = [_dev(x, t.grad_dtype, off * (i % 2)) for i, (x, t) in enumerate(zip(wl.make_grads(w), w.tensors))]
+        ref = fp.plan_buckets_flat(w.descs(), w.world)
+        na = fp.plan_buckets_flat(w.descs(), w.world)
+        assert len(ref.buckets) == 1
+        n = w.world * ref.c
+        a = torch.full((n + off,), 7, dtype=torch.float32, device=DEV)[off:]
+        z = torch.full((n + off,), 9, dtype=torch.float32, device=DEV)[off:]
+        fp.pack_reduce_scatter_input(ref, 0, g, a)
+        fp.pack_reduce_scatter_input_noalloc(na, 0, g, z)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.uint8), z.view(torch.uint8)), f"flat {name} differs from the ordinary pack"
+        ref.destroy()
+        na.destroy()
+
+
 def test_no_alloc_pack_rejects_what_it_cannot_hold():
     k = 1000                                    # more members than the launch arguments carry
     w = wl.custom([(3, 1)] * k, [FP32] * k, [FP32] * k, 2)
