@@ -38,12 +38,15 @@ std::atomic<uint64_t> g_plan_serial{0};
 // What each device's scratch holds: the image the last allocation-free pack
 // on that device copied there (plan serial, and region: -1 for the plan-wide
 // image, else the bucket) and an event recorded after the copy, on the
-// copying stream.  A call whose image is the one held, with that copy
-// complete, copies nothing.
+// copying stream.  A call whose image is the one held copies nothing.  Once
+// a call has been captured into a graph on the device, every replay of that
+// graph rewrites the scratch, so from then on the device's calls always copy
+// (`captured`).
 struct ScratchHolds {
     uint64_t serial = 0;
     int32_t region = 0;
     hipEvent_t copied = nullptr;
+    bool captured = false;
 };
 std::mutex g_scratch_mu;
 ScratchHolds g_scratch_holds[kMaxDevices];
@@ -425,6 +428,9 @@ int fsdppack_pack_reduce_scatter_input_noalloc(const fsdppack_plan *cplan, int32
     if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
     int dev = -1;
     if ((e = hipGetDevice(&dev)) != hipSuccess) return hip_fail(e, "hipGetDevice");
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if ((e = hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cap)) != hipSuccess)
+        return hip_fail(e, "hipStreamIsCapturing");
     const unsigned char *img = whole ? plan->scratch_image.data() : op.scratch_image.data();
     const size_t img_bytes = whole ? plan->scratch_image.size() : op.scratch_image.size();
     const int32_t region = whole ? -1 : bucket;
@@ -435,13 +441,21 @@ int fsdppack_pack_reduce_scatter_input_noalloc(const fsdppack_plan *cplan, int32
         // that copy on the device (whichever stream made it).  The plan's host
         // images live as long as the plan, and destroying a plan that copied
         // waits for the device, so a copy may complete after this call returns.
+        // Under stream capture the copy becomes a node of the graph, ahead of
+        // the kernel, and the scratch's contents are unknown from then on.
         std::lock_guard<std::mutex> lock(g_scratch_mu);
         ScratchHolds &h = g_scratch_holds[dev];
-        if (h.copied == nullptr && (e = hipEventCreateWithFlags(&h.copied, hipEventDisableTiming)) != hipSuccess) {
-            h.copied = nullptr;
-            return hip_fail(e, "hipEventCreate(scratch copy)");
+        if (cap != hipStreamCaptureStatusNone) {
+            h.captured = true;
+            h.serial = 0;
         }
-        if (h.serial == plan->serial && h.region == region) {
+        if (!h.captured && h.copied == nullptr) {
+            if ((e = hipEventCreateWithFlags(&h.copied, hipEventDisableTiming)) != hipSuccess) {
+                h.copied = nullptr;
+                return hip_fail(e, "hipEventCreate(scratch copy)");
+            }
+        }
+        if (!h.captured && h.serial == plan->serial && h.region == region) {
             e = hipEventQuery(h.copied);
             if (e == hipErrorNotReady) {
                 if ((e = hipStreamWaitEvent(static_cast<hipStream_t>(stream), h.copied, 0)) != hipSuccess)
@@ -455,10 +469,12 @@ int fsdppack_pack_reduce_scatter_input_noalloc(const fsdppack_plan *cplan, int32
             e = hipMemcpyAsync(static_cast<char *>(sp), img, img_bytes, hipMemcpyHostToDevice,
                                static_cast<hipStream_t>(stream));
             if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(tables to scratch)");
-            if ((e = hipEventRecord(h.copied, static_cast<hipStream_t>(stream))) != hipSuccess)
-                return hip_fail(e, "hipEventRecord(scratch copy)");
-            h.serial = plan->serial;
-            h.region = region;
+            if (!h.captured) {
+                if ((e = hipEventRecord(h.copied, static_cast<hipStream_t>(stream))) != hipSuccess)
+                    return hip_fail(e, "hipEventRecord(scratch copy)");
+                h.serial = plan->serial;
+                h.region = region;
+            }
             g_counters[8]++;
         }
     }

@@ -203,8 +203,14 @@ int fsdppack_pack_reduce_scatter_input(const fsdppack_plan *plan, int32_t bucket
  * when it does but the copy that put it there may still be running, the
  * call's stream waits for that copy on the device (hipStreamWaitEvent).  At
  * its first call on a device it looks up the scratch's address and creates
- * the event that marks those copies.  Destroying a plan that this entry
- * point copied from synchronises the device.  Same arguments, result and
+ * the event that marks those copies (make that first call outside stream
+ * capture).  Under stream capture the copy is recorded into the graph ahead
+ * of the kernel, so every replay brings its own tables; from then on every
+ * call on that device copies, since a replay may have replaced what the
+ * scratch held.  A graph holding such a call reads the plan's host image at
+ * each replay: it must not be replayed once the plan is destroyed.
+ * Destroying a plan that this entry point copied from synchronises the
+ * device.  Same arguments, result and
  * errors as fsdppack_pack_reduce_scatter_input, and also EINVAL when the
  * bucket has more than 960 members or its tables exceed the scratch (about
  * 13 000 column-map stretches).  Every call on a GPU shares that GPU's

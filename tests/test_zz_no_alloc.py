@@ -3,8 +3,8 @@ the ordinary pack, byte for byte, through the C ABI: two calls in a row on
 the library's shared device scratch, the second with a smaller layout (so
 any table left from the first call must not leak into it), plus a bucket of
 fp32 gradients into bf16 and a plan that is never used by an allocating call
-(its device tables are never created), and the scratch's reuse of the
-tables it already holds."""
+(its device tables are never created), the scratch's reuse of the
+tables it already holds, flat plans, and calls captured into a graph."""
 import numpy as np
 import pytest
 
@@ -181,3 +181,49 @@ def test_no_alloc_pack_rejects_what_it_cannot_hold():
         fp.pack_reduce_scatter_input_noalloc(plan, 0, [g] * k, torch.empty(2 * plan.buckets[0].S, device=DEV))
     assert e.value.code == -1 and "members" in str(e.value)
     plan.destroy()
+
+
+# Last in this file: once a call has been captured on the device, every later
+# allocation-free call there copies its tables (the residency test above
+# expects reuse).
+def test_no_alloc_pack_captured_in_a_graph_and_replayed():
+    """Both buckets of plan X packed by the allocation-free entry point under
+    stream capture (torch.cuda.graph) and replayed three times, with eager
+    calls of another plan A around each replay.  A replay copies X's tables
+    into the scratch ahead of its kernels; the eager call of A after it must
+    copy A's tables again rather than trust that the scratch still holds them
+    (once a graph holds such a copy, every eager call copies).  Every replay
+    and every eager result equals the ordinary pack's."""
+    x = _Layout(wl.custom([(4 * 1025, 3), (5,), (64, 2), (4 * 700, 8), (33, 7)],
+                          [BF16, FP32, BF16, FP32, BF16], [FP32, BF16, FP32, BF16, 0], 4, seed=15))
+    a = _Layout(wl.tiny())
+    nb = len(x.plan.buckets)
+    outs = [torch.full_like(r, 9) for r in x.ref]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                # set-up outside the capture, as torch advises
+        for bi in range(nb):
+            fp.pack_reduce_scatter_input_noalloc(x.plan, bi, x.g, outs[bi])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    print("[no-alloc] capture", flush=True)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for bi in range(nb):
+            fp.pack_reduce_scatter_input_noalloc(x.plan, bi, x.g, outs[bi])
+    torch.cuda.synchronize()
+    for rep in range(3):
+        print(f"[no-alloc] replay {rep}", flush=True)
+        for o in outs:
+            o.fill_(9)
+        assert a.call(0) == 1
+        graph.replay()
+        assert a.call(0) == 1                    # the replay replaced the tables: copied again
+        assert x.call(rep % nb) == 1
+        torch.cuda.synchronize()
+        for bi in range(nb):
+            assert torch.equal(outs[bi].view(torch.uint8), x.ref[bi].view(torch.uint8)), \
+                f"replay {rep}: bucket {bi} differs from the ordinary pack"
+    graph.reset()
+    for name, lay in (("captured plan, eager calls", x), ("tiny", a)):
+        lay.check(name)
