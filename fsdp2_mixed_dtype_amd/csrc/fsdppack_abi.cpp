@@ -75,6 +75,20 @@ bool plan_ok(const fsdppack_plan *p) { return p != nullptr && p->magic == kPlanM
 
 bool aligned(const void *p, int64_t bytes) { return (reinterpret_cast<uintptr_t>(p) % bytes) == 0; }
 
+// Timing events armed for this thread's next launch.  Every compute call
+// takes them when it starts: its launch stamps them, and a call that launches
+// nothing (nothing to write, or rejected) leaves them unstamped.
+struct ArmedEvents {
+    void *start = nullptr, *stop = nullptr;
+};
+
+ArmedEvents take_armed_events()
+{
+    ArmedEvents ev{g_next_start, g_next_stop};
+    g_next_start = g_next_stop = nullptr;
+    return ev;
+}
+
 int upload_table(OpTable &op)
 {
     hipError_t e;
@@ -230,12 +244,8 @@ int acquire_table(PtrCache &c, const std::vector<uint64_t> &key, hipStream_t str
 // Run one operation: one kernel launch, its pointer table in the launch's
 // arguments (up to kInlineLarge entries) or in a cached device table.
 int run_op(fsdppack_plan *p, const OpTable &op, size_t cache_index, const std::vector<uint64_t> &key, char *base,
-           void *stream, const char *what, int32_t rank = 0, float divisor = 1.0f)
+           void *stream, const ArmedEvents &ev, const char *what, int32_t rank = 0, float divisor = 1.0f)
 {
-    // timing events armed for the next launch are taken by this call, also
-    // when it has nothing to launch
-    void *ev0 = g_next_start, *ev1 = g_next_stop;
-    g_next_start = g_next_stop = nullptr;
     // window boundaries follow the cache lines of memory, not the buffer's start
     const int32_t shift = static_cast<int32_t>(reinterpret_cast<uintptr_t>(base) & (kLineBytes - 1));
     if (op.windows(shift) <= 0) return FSDPPACK_OK;
@@ -270,7 +280,7 @@ int run_op(fsdppack_plan *p, const OpTable &op, size_t cache_index, const std::v
     args.base = base;
     args.rank = rank;
     args.divisor = divisor;
-    const int le = launch_windows(args, inline_ptrs, static_cast<int32_t>(key.size()), stream, ev0, ev1);
+    const int le = launch_windows(args, inline_ptrs, static_cast<int32_t>(key.size()), stream, ev.start, ev.stop);
     if (le != 0) return hip_fail(static_cast<hipError_t>(le), what);
     g_counters[0]++;
     if (upload_after) {
@@ -282,6 +292,28 @@ int run_op(fsdppack_plan *p, const OpTable &op, size_t cache_index, const std::v
     if (trace_on())
         std::fprintf(stderr, "fsdppack: %s: %d workgroups, %lld bytes read, %lld bytes written\n", what,
                      args.n_windows, static_cast<long long>(op.src_bytes), static_cast<long long>(op.dst_bytes));
+    return FSDPPACK_OK;
+}
+
+// Argument checks shared by the two pack entry points (`what` names the
+// call).  A message is built only for an argument that is rejected.
+int check_pack_args(const fsdppack_plan *plan, int32_t bucket, const void *const *grads, const void *out,
+                    const char *what)
+{
+    auto bad = [what](int code, const std::string &msg) { return fail(code, std::string(what) + ": " + msg); };
+    if (!plan_ok(plan)) return bad(FSDPPACK_ESTATE, "invalid plan handle");
+    if (bucket < 0 || bucket >= static_cast<int32_t>(plan->buckets.size()))
+        return bad(FSDPPACK_EINVAL, "bucket index out of range");
+    if (grads == nullptr) return bad(FSDPPACK_EINVAL, "grads is NULL");
+    const BucketPlan &b = plan->buckets[bucket];
+    if (b.S > 0 && (out == nullptr || !aligned(out, dtype_bytes(b.dtype))))
+        return bad(FSDPPACK_EINVAL, "out is NULL or not aligned to its element size");
+    for (int32_t t : b.members) {
+        if (plan->numel[t] == 0) continue;
+        const void *g = grads[t];
+        if (g == nullptr || !aligned(g, dtype_bytes(plan->params[t].grad_dtype)))
+            return bad(FSDPPACK_EINVAL, "grads[" + std::to_string(t) + "] is NULL or not aligned to its element size");
+    }
     return FSDPPACK_OK;
 }
 
@@ -363,28 +395,16 @@ int fsdppack_plan_all_gather_layout(const fsdppack_plan *plan, int64_t *B, const
 int fsdppack_pack_reduce_scatter_input(const fsdppack_plan *cplan, int32_t bucket, const void *const *grads,
                                        void *out, void *stream)
 {
+    const ArmedEvents ev = take_armed_events();
+    if (int rc = check_pack_args(cplan, bucket, grads, out, "pack_reduce_scatter_input")) return rc;
     fsdppack_plan *plan = const_cast<fsdppack_plan *>(cplan);
-    if (!plan_ok(plan)) return fail(FSDPPACK_ESTATE, "pack_reduce_scatter_input: invalid plan handle");
-    if (bucket < 0 || bucket >= static_cast<int32_t>(plan->buckets.size()))
-        return fail(FSDPPACK_EINVAL, "pack_reduce_scatter_input: bucket index out of range");
-    if (grads == nullptr) return fail(FSDPPACK_EINVAL, "pack_reduce_scatter_input: grads is NULL");
-    BucketPlan &b = plan->buckets[bucket];
-    const int64_t dsz = dtype_bytes(b.dtype);
-    if (b.S > 0 && (out == nullptr || !aligned(out, dsz)))
-        return fail(FSDPPACK_EINVAL, "pack_reduce_scatter_input: out is NULL or not aligned to its element size");
-    for (int32_t t : b.members) {
-        if (plan->numel[t] == 0) continue;
-        const void *g = grads[t];
-        if (g == nullptr || !aligned(g, dtype_bytes(plan->params[t].grad_dtype)))
-            return fail(FSDPPACK_EINVAL, "pack_reduce_scatter_input: grads[" + std::to_string(t) +
-                                             "] is NULL or not aligned to its element size");
-    }
+    const BucketPlan &b = plan->buckets[bucket];
     // the pack's pointer table is in member order (entry m = member m)
     std::vector<uint64_t> key(b.pack.table_params.size());
     for (size_t m = 0; m < key.size(); ++m) key[m] = reinterpret_cast<uint64_t>(grads[b.pack.table_params[m]]);
     try {
-        return run_op(plan, b.pack, static_cast<size_t>(bucket), key, static_cast<char *>(out), stream,
-                        "pack_reduce_scatter_input");
+        return run_op(plan, b.pack, static_cast<size_t>(bucket), key, static_cast<char *>(out), stream, ev,
+                      "pack_reduce_scatter_input");
     } catch (const std::bad_alloc &) {
         return fail(FSDPPACK_ENOMEM, "pack_reduce_scatter_input: out of host memory");
     }
@@ -393,25 +413,10 @@ int fsdppack_pack_reduce_scatter_input(const fsdppack_plan *cplan, int32_t bucke
 int fsdppack_pack_reduce_scatter_input_noalloc(const fsdppack_plan *cplan, int32_t bucket, const void *const *grads,
                                                void *out, void *stream)
 {
-    void *ev0 = g_next_start, *ev1 = g_next_stop;
-    g_next_start = g_next_stop = nullptr;
+    const ArmedEvents ev = take_armed_events();
+    if (int rc = check_pack_args(cplan, bucket, grads, out, "pack_reduce_scatter_input_noalloc")) return rc;
     const fsdppack_plan *plan = cplan;
-    if (!plan_ok(plan)) return fail(FSDPPACK_ESTATE, "pack_reduce_scatter_input_noalloc: invalid plan handle");
-    if (bucket < 0 || bucket >= static_cast<int32_t>(plan->buckets.size()))
-        return fail(FSDPPACK_EINVAL, "pack_reduce_scatter_input_noalloc: bucket index out of range");
-    if (grads == nullptr) return fail(FSDPPACK_EINVAL, "pack_reduce_scatter_input_noalloc: grads is NULL");
-    const BucketPlan &b = plan->buckets[bucket];
-    const OpTable &op = b.pack;
-    const int64_t dsz = dtype_bytes(b.dtype);
-    if (b.S > 0 && (out == nullptr || !aligned(out, dsz)))
-        return fail(FSDPPACK_EINVAL, "pack_reduce_scatter_input_noalloc: out is NULL or not aligned to its element size");
-    for (int32_t t : b.members) {
-        if (plan->numel[t] == 0) continue;
-        const void *g = grads[t];
-        if (g == nullptr || !aligned(g, dtype_bytes(plan->params[t].grad_dtype)))
-            return fail(FSDPPACK_EINVAL, "pack_reduce_scatter_input_noalloc: grads[" + std::to_string(t) +
-                                             "] is NULL or not aligned to its element size");
-    }
+    const OpTable &op = plan->buckets[bucket].pack;
     if (op.table_params.size() > static_cast<size_t>(kInlineLarge))
         return fail(FSDPPACK_EINVAL, "pack_reduce_scatter_input_noalloc: the bucket has more than " +
                                          std::to_string(kInlineLarge) + " members");
@@ -488,7 +493,7 @@ int fsdppack_pack_reduce_scatter_input_noalloc(const fsdppack_plan *cplan, int32
     uint64_t key[kInlineLarge];
     const int32_t nk = static_cast<int32_t>(op.table_params.size());
     for (int32_t m = 0; m < nk; ++m) key[m] = reinterpret_cast<uint64_t>(grads[op.table_params[m]]);
-    const int le = launch_windows(args, key, nk, stream, ev0, ev1);
+    const int le = launch_windows(args, key, nk, stream, ev.start, ev.stop);
     if (le != 0) return hip_fail(static_cast<hipError_t>(le), "pack_reduce_scatter_input_noalloc");
     g_counters[0]++;
     g_counters[6]++;
@@ -498,6 +503,7 @@ int fsdppack_pack_reduce_scatter_input_noalloc(const fsdppack_plan *cplan, int32
 int fsdppack_all_gather_copy_in(const fsdppack_plan *cplan, int32_t rank, const void *const *shards, void *ag_out,
                                 void *stream)
 {
+    const ArmedEvents ev = take_armed_events();
     fsdppack_plan *plan = const_cast<fsdppack_plan *>(cplan);
     if (!plan_ok(plan)) return fail(FSDPPACK_ESTATE, "all_gather_copy_in: invalid plan handle");
     if (rank < 0 || rank >= plan->W) return fail(FSDPPACK_EINVAL, "all_gather_copy_in: rank out of range");
@@ -519,7 +525,7 @@ int fsdppack_all_gather_copy_in(const fsdppack_plan *cplan, int32_t rank, const 
         }
         char *row = static_cast<char *>(ag_out) + static_cast<int64_t>(rank) * plan->B;
         try {
-            return run_op(plan, op, plan->buckets.size(), key, row, stream, "all_gather_copy_in", rank);
+            return run_op(plan, op, plan->buckets.size(), key, row, stream, ev, "all_gather_copy_in", rank);
         } catch (const std::bad_alloc &) {
             return fail(FSDPPACK_ENOMEM, "all_gather_copy_in: out of host memory");
         }
@@ -539,7 +545,7 @@ int fsdppack_all_gather_copy_in(const fsdppack_plan *cplan, int32_t rank, const 
     }
     char *row = static_cast<char *>(ag_out) + static_cast<int64_t>(rank) * plan->B;
     try {
-        return run_op(plan, op, plan->buckets.size(), key, row, stream, "all_gather_copy_in");
+        return run_op(plan, op, plan->buckets.size(), key, row, stream, ev, "all_gather_copy_in");
     } catch (const std::bad_alloc &) {
         return fail(FSDPPACK_ENOMEM, "all_gather_copy_in: out of host memory");
     }
@@ -547,6 +553,7 @@ int fsdppack_all_gather_copy_in(const fsdppack_plan *cplan, int32_t rank, const 
 
 int fsdppack_all_gather_copy_out(const fsdppack_plan *cplan, const void *ag, void *const *params, void *stream)
 {
+    const ArmedEvents ev = take_armed_events();
     fsdppack_plan *plan = const_cast<fsdppack_plan *>(cplan);
     if (!plan_ok(plan)) return fail(FSDPPACK_ESTATE, "all_gather_copy_out: invalid plan handle");
     if (params == nullptr) return fail(FSDPPACK_EINVAL, "all_gather_copy_out: params is NULL");
@@ -564,14 +571,16 @@ int fsdppack_all_gather_copy_out(const fsdppack_plan *cplan, const void *ag, voi
     }
     try {
         return run_op(plan, plan->copy_out, plan->buckets.size() + 1, key,
-                        const_cast<char *>(static_cast<const char *>(ag)), stream, "all_gather_copy_out");
+                      const_cast<char *>(static_cast<const char *>(ag)), stream, ev, "all_gather_copy_out");
     } catch (const std::bad_alloc &) {
         return fail(FSDPPACK_ENOMEM, "all_gather_copy_out: out of host memory");
     }
 }
 
-int fsdppack_reduce_scatter_copy_out(const fsdppack_plan *cplan, int32_t bucket, int32_t rank, const void *rs_out,
-                                     float divide_factor, void *const *shard_grads, void *stream)
+namespace {
+// The per-bucket write-back, with the timing events its caller took.
+int reduce_scatter_copy_out(const fsdppack_plan *cplan, int32_t bucket, int32_t rank, const void *rs_out,
+                            float divide_factor, void *const *shard_grads, void *stream, const ArmedEvents &ev)
 {
     fsdppack_plan *plan = const_cast<fsdppack_plan *>(cplan);
     if (!plan_ok(plan)) return fail(FSDPPACK_ESTATE, "reduce_scatter_copy_out: invalid plan handle");
@@ -600,16 +609,25 @@ int fsdppack_reduce_scatter_copy_out(const fsdppack_plan *cplan, int32_t bucket,
     }
     try {
         return run_op(plan, b.write_back, plan->buckets.size() + 2 + static_cast<size_t>(bucket), key,
-                      const_cast<char *>(static_cast<const char *>(rs_out)), stream, "reduce_scatter_copy_out", rank,
-                      divide_factor);
+                      const_cast<char *>(static_cast<const char *>(rs_out)), stream, ev, "reduce_scatter_copy_out",
+                      rank, divide_factor);
     } catch (const std::bad_alloc &) {
         return fail(FSDPPACK_ENOMEM, "reduce_scatter_copy_out: out of host memory");
     }
+}
+}  // namespace
+
+int fsdppack_reduce_scatter_copy_out(const fsdppack_plan *cplan, int32_t bucket, int32_t rank, const void *rs_out,
+                                     float divide_factor, void *const *shard_grads, void *stream)
+{
+    const ArmedEvents ev = take_armed_events();
+    return reduce_scatter_copy_out(cplan, bucket, rank, rs_out, divide_factor, shard_grads, stream, ev);
 }
 
 int fsdppack_reduce_scatter_copy_out_all(const fsdppack_plan *cplan, int32_t rank, const void *const *rs_outs,
                                          float divide_factor, void *const *shard_grads, void *stream)
 {
+    const ArmedEvents ev = take_armed_events();
     fsdppack_plan *plan = const_cast<fsdppack_plan *>(cplan);
     if (!plan_ok(plan)) return fail(FSDPPACK_ESTATE, "reduce_scatter_copy_out_all: invalid plan handle");
     if (rs_outs == nullptr) return fail(FSDPPACK_EINVAL, "reduce_scatter_copy_out_all: rs_outs is NULL");
@@ -620,10 +638,9 @@ int fsdppack_reduce_scatter_copy_out_all(const fsdppack_plan *cplan, int32_t ran
             if (rank < 0 || rank >= plan->W) return fail(FSDPPACK_EINVAL, "reduce_scatter_copy_out_all: rank out of range");
             if (!(divide_factor > 0.0f) || divide_factor > 3.4028235e38f)
                 return fail(FSDPPACK_EINVAL, "reduce_scatter_copy_out_all: divide_factor must be finite and positive");
-            g_next_start = g_next_stop = nullptr;     // armed timing events are taken: nothing to launch
             return FSDPPACK_OK;
         }
-        return fsdppack_reduce_scatter_copy_out(cplan, 0, rank, rs_outs[0], divide_factor, shard_grads, stream);
+        return reduce_scatter_copy_out(cplan, 0, rank, rs_outs[0], divide_factor, shard_grads, stream, ev);
     }
     if (rank < 0 || rank >= plan->W) return fail(FSDPPACK_EINVAL, "reduce_scatter_copy_out_all: rank out of range");
     if (!(divide_factor > 0.0f) || divide_factor > 3.4028235e38f)
@@ -647,7 +664,7 @@ int fsdppack_reduce_scatter_copy_out_all(const fsdppack_plan *cplan, int32_t ran
         }
     }
     try {
-        return run_op(plan, plan->write_back_all, 2 * plan->buckets.size() + 2, key, nullptr, stream,
+        return run_op(plan, plan->write_back_all, 2 * plan->buckets.size() + 2, key, nullptr, stream, ev,
                       "reduce_scatter_copy_out_all", rank, divide_factor);
     } catch (const std::bad_alloc &) {
         return fail(FSDPPACK_ENOMEM, "reduce_scatter_copy_out_all: out of host memory");
@@ -701,13 +718,12 @@ int fsdppack_time_next_launch(void *start_event, void *stop_event)
 
 int fsdppack_empty_launch(int32_t workgroups, int32_t threads, void *stream)
 {
-    void *ev0 = g_next_start, *ev1 = g_next_stop;
-    g_next_start = g_next_stop = nullptr;
+    const ArmedEvents ev = take_armed_events();
     if (workgroups < 1 || threads < 64 || threads > 1024 || threads % 64 != 0 ||
         static_cast<int64_t>(workgroups) * threads >= (int64_t{1} << 32))
         return fail(FSDPPACK_EINVAL, "empty_launch: workgroups must be >= 1 and threads a multiple of 64 in [64, 1024], "
                                      "fewer than 2^32 work-items in all");
-    const int le = launch_empty(workgroups, threads, stream, ev0, ev1);
+    const int le = launch_empty(workgroups, threads, stream, ev.start, ev.stop);
     if (le != 0) return hip_fail(static_cast<hipError_t>(le), "empty_launch");
     return FSDPPACK_OK;
 }

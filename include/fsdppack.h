@@ -300,8 +300,8 @@ const char *fsdppack_last_error(void);
  * timing enabled; either may be NULL) at its kernel's start and end, so
  * hipEventElapsedTime gives that kernel's exact execution time.  The next
  * compute call takes the events whether it launches or not: a call with
- * nothing to write clears them without stamping them.  For benchmarks and
- * profilers. */
+ * nothing to write, or one rejected for its arguments, clears them without
+ * stamping them.  For benchmarks and profilers. */
 int fsdppack_time_next_launch(void *start_event, void *stop_event);
 
 /* Library-wide counters since load (for tests and tracing): counters[0] =

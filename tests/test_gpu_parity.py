@@ -434,10 +434,10 @@ def test_pointer_churn_on_two_streams():
     plan.destroy()
 
 
-def test_armed_timing_events_are_taken_by_a_call_with_nothing_to_launch():
+def test_armed_timing_events_are_taken_by_a_call_that_launches_nothing():
     """Events armed with time_next_launch belong to the next compute call even
-    when it has nothing to write: a later, unrelated kernel must not stamp
-    them."""
+    when it has nothing to write or is rejected for its arguments: a later,
+    unrelated kernel must not stamp them."""
     a = torch.randn(2048, 2048, device=DEV)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -457,6 +457,19 @@ def test_armed_timing_events_are_taken_by_a_call_with_nothing_to_launch():
     g_dev = [to_dev(g, t.grad_dtype) for g, t in zip(wl.make_grads(w), w.tensors)]
     gpu_pack(plan, 0, g_dev)                          # a real launch, after the empty call
     assert e0.elapsed_time(e1) == before               # not stamped by it
+    # a call rejected for its arguments takes them too (every compute entry point)
+    L = fp.lib()
+    rejected = [lambda: L.fsdppack_pack_reduce_scatter_input(plan.handle, 99, None, None, None),
+                lambda: L.fsdppack_pack_reduce_scatter_input_noalloc(plan.handle, 99, None, None, None),
+                lambda: L.fsdppack_all_gather_copy_in(plan.handle, -1, None, None, None),
+                lambda: L.fsdppack_all_gather_copy_out(plan.handle, None, None, None),
+                lambda: L.fsdppack_reduce_scatter_copy_out(plan.handle, 99, 0, None, 1.0, None, None),
+                lambda: L.fsdppack_reduce_scatter_copy_out_all(plan.handle, -1, None, 1.0, None, None)]
+    for call in rejected:
+        fp.time_next_launch(e0, e1)
+        assert call() == -1
+        gpu_pack(plan, 0, g_dev)
+        assert e0.elapsed_time(e1) == before
     fp.time_next_launch(e0, e1)
     gpu_pack(plan, 0, g_dev)
     assert e0.elapsed_time(e1) < before                # stamped when armed right before
