@@ -89,28 +89,27 @@ ArmedEvents take_armed_events()
     return ev;
 }
 
+// Copy one operation's tables to the device.  A table is kept only once its
+// copy has succeeded, so a call retried after a failed upload resumes it
+// without leaking or trusting a half-made table.
 int upload_table(OpTable &op)
 {
-    hipError_t e;
-    const size_t bytes = op.members.size();
-    if (bytes) {
-        if ((e = hipMalloc(&op.d_members, bytes)) != hipSuccess) return hip_fail(e, "hipMalloc(member table)");
-        if ((e = hipMemcpy(op.d_members, op.members.data(), bytes, hipMemcpyHostToDevice)) != hipSuccess)
-            return hip_fail(e, "hipMemcpy(member table)");
-    }
-    const size_t cbytes = op.columns.size() * sizeof(ColumnWindow);
-    if (cbytes) {
-        if ((e = hipMalloc(&op.d_columns, cbytes)) != hipSuccess) return hip_fail(e, "hipMalloc(column map)");
-        if ((e = hipMemcpy(op.d_columns, op.columns.data(), cbytes, hipMemcpyHostToDevice)) != hipSuccess)
-            return hip_fail(e, "hipMemcpy(column map)");
-    }
-    const size_t sbytes = op.stretches.size() * sizeof(PackStretch);
-    if (sbytes) {
-        if ((e = hipMalloc(&op.d_stretches, sbytes)) != hipSuccess) return hip_fail(e, "hipMalloc(stretch records)");
-        if ((e = hipMemcpy(op.d_stretches, op.stretches.data(), sbytes, hipMemcpyHostToDevice)) != hipSuccess)
-            return hip_fail(e, "hipMemcpy(stretch records)");
-    }
-    return FSDPPACK_OK;
+    auto put = [](void *&dst, const void *src, size_t bytes, const char *what) -> int {
+        if (bytes == 0 || dst != nullptr) return FSDPPACK_OK;
+        void *d = nullptr;
+        hipError_t e = hipMalloc(&d, bytes);
+        if (e != hipSuccess) return hip_fail(e, (std::string("hipMalloc(") + what + ")").c_str());
+        if ((e = hipMemcpy(d, src, bytes, hipMemcpyHostToDevice)) != hipSuccess) {
+            (void)hipFree(d);
+            return hip_fail(e, (std::string("hipMemcpy(") + what + ")").c_str());
+        }
+        dst = d;
+        return FSDPPACK_OK;
+    };
+    if (int rc = put(op.d_members, op.members.data(), op.members.size(), "member table")) return rc;
+    if (int rc = put(op.d_columns, op.columns.data(), op.columns.size() * sizeof(ColumnWindow), "column map"))
+        return rc;
+    return put(op.d_stretches, op.stretches.data(), op.stretches.size() * sizeof(PackStretch), "stretch records");
 }
 
 // Upload the plan's member tables once, on the current device; afterwards
@@ -222,10 +221,22 @@ int acquire_table(PtrCache &c, const std::vector<uint64_t> &key, hipStream_t str
     }
     const size_t bytes = key.size() * sizeof(uint64_t);
     if (victim->d_table == nullptr) {
-        if ((e = hipMalloc(reinterpret_cast<void **>(&victim->d_table), bytes)) != hipSuccess) return hip_fail(e, "hipMalloc(pointer table)");
-        if ((e = hipHostMalloc(reinterpret_cast<void **>(&victim->h_stage), bytes, hipHostMallocDefault)) != hipSuccess) return hip_fail(e, "hipHostMalloc(pointer table)");
-        hipEvent_t ev;
-        if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+        // the slot's device table, pinned staging and event, kept only together
+        uint64_t *d = nullptr, *h = nullptr;
+        hipEvent_t ev = nullptr;
+        if ((e = hipMalloc(reinterpret_cast<void **>(&d), bytes)) != hipSuccess)
+            return hip_fail(e, "hipMalloc(pointer table)");
+        if ((e = hipHostMalloc(reinterpret_cast<void **>(&h), bytes, hipHostMallocDefault)) != hipSuccess) {
+            (void)hipFree(d);
+            return hip_fail(e, "hipHostMalloc(pointer table)");
+        }
+        if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) {
+            (void)hipFree(d);
+            (void)hipHostFree(h);
+            return hip_fail(e, "hipEventCreate");
+        }
+        victim->d_table = d;
+        victim->h_stage = h;
         victim->ready = ev;
     }
     std::memcpy(victim->h_stage, key.data(), bytes);
