@@ -15,10 +15,13 @@ Functions (same names as the C ABI without the ``fsdppack_`` prefix):
   all_gather_copy_in(plan, rank, shards, ag_out, stream=None)
   all_gather_copy_out(plan, ag, params, stream=None)
   reduce_scatter_copy_out(plan, bucket, rank, rs_out, shard_grads, divide_factor=1.0, stream=None)
+  reduce_scatter_copy_out_all(plan, rank, rs_outs, shard_grads, divide_factor=1.0, stream=None)
+                                               (every bucket's write-back in one launch)
 
 The tensor lists may also be given as a PointerArray from prepare_grads /
-prepare_shards / prepare_params: validated once and reused across calls, the
-way a training loop reuses its gradient and shard buffers every step.
+prepare_shards / prepare_params / prepare_shard_grads: validated once and
+reused across calls, the way a training loop reuses its gradient and shard
+buffers every step.
 """
 from __future__ import annotations
 
