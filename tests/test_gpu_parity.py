@@ -355,6 +355,58 @@ def test_mid_size_pointer_churn_on_two_streams():
     plan.destroy()
 
 
+def test_one_plan_shared_by_threads_on_their_own_streams():
+    """One plan used by four host threads at once (the library's calls run
+    without the GIL), each on a stream of its own with its own rotation of
+    six gradient buffer sets, five rounds.  A 200-member bucket exercises
+    pointer sets passed in the launch arguments and uploaded behind the
+    launch, cached tables, and tables replaced while other streams read
+    them (24 sets, 16 tables); a 1000-member bucket, device tables staged
+    before the launch.  Every pack equals the oracle's."""
+    import threading
+    n_threads, n_sets, rounds = 4, 6, 5
+    for w in (_many_params(200, W=4, seed=6), _many_params(1000, W=4, seed=7)):
+        print(f"[threads] {len(w.tensors)} members", flush=True)
+        ref = oracle.plan(w.descs(), w.world)
+        plan = fp.plan_buckets(w.descs(), w.world)
+        b = plan.buckets[0]
+        sets = []
+        for th in range(n_threads):
+            mine = []
+            for k in range(n_sets):
+                grads = wl.make_grads(w, seed=1000 * (th + 1) + k)
+                g_dev = [to_dev(g, t.grad_dtype, k % 3) for g, t in zip(grads, w.tensors)]
+                mine.append((grads, fp.prepare_grads(plan, g_dev)))
+            sets.append(mine)
+        outs = [[torch.empty(w.world * b.S, dtype=fp.TORCH_DTYPE[b.dtype], device=DEV)
+                 for _ in range(rounds * n_sets)] for _ in range(n_threads)]
+        torch.cuda.synchronize()
+        errors = []
+
+        def work(th):
+            try:
+                stream = torch.cuda.Stream(device=DEV)
+                with torch.cuda.stream(stream):
+                    for i in range(rounds * n_sets):
+                        fp.pack_reduce_scatter_input(plan, 0, sets[th][i % n_sets][1], outs[th][i])
+                stream.synchronize()
+            except Exception as e:          # reported below, on the test's thread
+                errors.append((th, e))
+
+        threads = [threading.Thread(target=work, args=(th,)) for th in range(n_threads)]
+        for t in threads:
+            t.start()
+        for t in threads:
+            t.join()
+        assert not errors, errors
+        torch.cuda.synchronize()
+        for th in range(n_threads):
+            expect = [oracle.pack(ref, 0, sets[th][k][0]).view(np.uint8).reshape(-1) for k in range(n_sets)]
+            for i in range(rounds * n_sets):
+                assert np.array_equal(host_bytes(outs[th][i]), expect[i % n_sets]), (len(w.tensors), th, i)
+        plan.destroy()
+
+
 def _many_params(k=1000, W=4, seed=0):
     """A unit of more parameters than a launch's arguments carry (the pointer
     table goes through the device-table cache)."""
