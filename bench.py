@@ -78,6 +78,9 @@ def parse():
                     help="FSDP1 flat-parameter layout of the workload (reduce in fp32, compute in bf16)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run plain 256 MiB device copies (known size) to calibrate byte counters")
+    ap.add_argument("--mark-legs", action="store_true",
+                    help="launch an empty kernel of LEG workgroups (1, 2, ...) at the start of each leg, so that a "
+                         "profiler's kernel trace can be split by leg (LEGS lists them)")
     return ap.parse_args()
 
 
@@ -191,6 +194,12 @@ class Bench:
         self.torch.cuda.synchronize()
         return sum(a.elapsed_time(b) for a, b in ev) / K
 
+
+# The bench's legs, in launch order; with --mark-legs each starts with an
+# empty kernel of (its index + 1) workgroups
+LEGS = ["prime and warm-up", "timed steps", "stamped steps", "warm repeats", "isolated pack", "comparator",
+        "copy ceiling", "write-back", "launch floors", "pointer churn", "under load", "other target",
+        "calibration copy"]
 
 # Fewest stamped launches behind an isolated pack figure (each one of the
 # 50.3M-element layout is ~0.05 ms, so 100 cost a few milliseconds)
@@ -350,6 +359,10 @@ def main():
     nb = len(plan.buckets)
     new_event = B.new_event
 
+    def mark(leg):
+        if args.mark_legs:
+            fp.empty_launch(LEGS.index(leg) + 1, 64, stream)
+
     def timed(pair):
         # the library stamps these events at the kernel's own start and end
         if pair is not None:
@@ -369,6 +382,7 @@ def main():
 
     # prime: one pass over every buffer set (each set's first call uploads its
     # pointer tables), then the W warm-up steps
+    mark("prime and warm-up")
     for s_ in sets:
         step(s_)
     for i in range(args.warmup):
@@ -378,6 +392,7 @@ def main():
     K = args.steps
     # timed region: K steps exactly as a caller would issue them (no timing
     # events between kernels), bracketed by synchronisations
+    mark("timed steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -394,6 +409,7 @@ def main():
     evs = [[(new_event(), new_event()) for _ in range(nb + 2)] for _ in range(K)]
     loop0, loop1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    mark("stamped steps")
     step(sets[(K + R - 1) % R])
     loop0.record(stream)
     for i in range(K):
@@ -411,6 +427,7 @@ def main():
     # 256 MB Infinity Cache between steps
     per_step = [sum(e[bi][0].elapsed_time(e[bi][1]) for bi in range(nb)) for e in evs]
     pack_in_step_ms = sum(pack_ms)
+    mark("warm repeats")
     warm = [sum(x) for x in B.time_packs(plan, [sets[0][:2] + (None,)], K, args.warmup)]
     copy_in_ms = None if args.pack_only else mean_ms(nb)
     copy_out_ms = None if args.pack_only else mean_ms(nb + 1)
@@ -420,6 +437,7 @@ def main():
     # is reported beside it
     isolated = None
     if not args.flat and not args.pack_only:
+        mark("isolated pack")
         isolated = pack_target(B, args.workload, K, args.warmup, args.rotate_bytes)
         pack_ms = isolated["bucket_ms"]
     pack_total_ms = sum(pack_ms)
@@ -428,6 +446,7 @@ def main():
 
     extra = {}
     if not args.pack_only:
+        mark("comparator")
         # ---- pre-cast then homogeneous pack (the pages' comparator), our kernels, 2 launches;
         # its output must equal the fused pack's, byte for byte
         bf_idx = [i for i, t in enumerate(w.tensors) if t.grad_dtype == fp.BF16]
@@ -471,6 +490,7 @@ def main():
             del csets
 
         # ---- plain-copy ceiling: device-to-device copy moving the pack's byte count
+        mark("copy ceiling")
         nbytes = sum(pack_bytes) // 2
         src = [torch.empty(nbytes // 4, dtype=torch.float32, device=dev) for _ in range(R)]
         dst = [torch.empty_like(x) for x in src]
@@ -488,6 +508,7 @@ def main():
         extra["pack_frac_of_copy_ceiling"] = round(pack_gbps / extra["copy_ceiling_GBps"], 4)
         del src, dst
 
+        mark("write-back")
         # ---- reduce-scatter write-back of rank 0 (the step after the
         # reduce-scatter): row 0 of each bucket's packed buffer stands in for
         # the rank's reduced row, divided by W and cast to the storage dtypes
@@ -539,6 +560,7 @@ def main():
             del asets
         del wsets
 
+        mark("launch floors")
         # ---- launch floor: each launch of the step against an empty kernel
         # of the same number of 64-thread workgroups (the dispatch of its
         # workgroups and the launch's fixed cost)
@@ -578,6 +600,7 @@ def main():
                             "above_floor_us": round((kernel_ms[name] - f_ms) * 1e3, 2)}
         extra["launch_floor"] = floors
 
+        mark("pointer churn")
         # ---- pointer churn: every call brings a new set of gradient pointers
         # (as when gradients are allocated afresh each backward), cycling
         # through more sets than the library's 16-entry table cache (which
@@ -649,6 +672,7 @@ def main():
         }
         del churn, a_mm, b_mm
 
+        mark("under load")
         # ---- pack under concurrent load: packs on a side stream (default
         # priority) while a stream of bf16 GEMMs keeps the GPU busy, as FSDP
         # overlaps its gradient staging with the backward's compute
@@ -708,6 +732,7 @@ def main():
         del ma, mb, mc
 
     if args.calib_copy:
+        mark("calibration copy")
         # plain device-to-device copies of a known size: what a byte counter
         # reads for them calibrates the counter against real traffic
         n = 256 * 2**20 // 4
@@ -746,6 +771,7 @@ def main():
             if name == args.workload and isolated is not None:
                 targets[name] = isolated
             else:
+                mark("other target")
                 targets[name] = pack_target(B, name, K, args.warmup, args.rotate_bytes)
             targets[name]["meets_80pct"] = targets[name]["frac_of_peak"] >= 0.80
 
