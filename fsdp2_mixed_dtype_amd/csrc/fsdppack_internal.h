@@ -155,28 +155,37 @@ struct FlatMember {
 };
 static_assert(sizeof(FlatMember) == 32, "shared with the device");
 
-// One candidate member of a pack stretch.  Column offsets and counts are
-// 32-bit: stretch records are only built for buckets whose rows hold fewer
-// than 2^31 bytes and whose members' rank chunks hold fewer than 2^32 source
-// bytes (pack_narrow).
-//   source of row r, column c (O <= c < OP):  table[m] + r*Pss + (c - O)*size(dt)
-//   row r's real columns: [O, OP) for r < full, [O, OT) for r == full, none after
+// One candidate member of a pack stretch, in bytes of the destination row
+// (column c of the row is bytes [c*dsz, (c+1)*dsz), dsz the reduction
+// dtype's size), laid out so that the kernel's direct test is a handful of
+// scalar instructions: a whole window starting at row byte y0 lies in the
+// member's columns iff y0 - lo <= span (unsigned), and has no padding in row
+// r iff (r, y0 + window) <= (full, end) in lexicographic order.  Stretch
+// records are only built for buckets whose rows hold fewer than 2^31 bytes
+// and whose members' rank chunks hold fewer than 2^32 source bytes
+// (pack_narrow).
+//   source of row r, row byte y (lo <= y < lo + P*dsz):
+//       table[m] + r*Pss + (((y - lo) << 1) >> sh)
 struct PackCand {
-    uint32_t m;              // the member (its entry of the pointer table)
-    uint32_t Pss;            // P*size(dt): source bytes between consecutive rank chunks
-    uint32_t O;              // first column
-    uint32_t OP;             // O + P
+    uint32_t lo;             // O*dsz, the member's first row byte
+    uint32_t span;           // P*dsz - window bytes (0 with full = end = 0 when no window fits)
+    uint32_t end;            // row `full`'s first byte past its real columns: (O + numel - full*P)*dsz
     uint32_t full;           // ranks whose chunk is all real: numel / P
-    uint32_t OT;             // O + numel - full*P
-    uint32_t dt;             // source dtype; 0 = no candidate
-    uint32_t reserved;
+    uint32_t Pss;            // P*size(src): source bytes between consecutive rank chunks
+    uint32_t moff;           // 8*m: the byte offset of the member's pointer-table entry
+    uint32_t sh;             // 1 + log2(dsz) - log2(size(src))
+    uint32_t code;           // src_dt*4 + dst_dt
 };
 static_assert(sizeof(PackCand) == 32, "shared with the device");
 
 // The members a pack window may lie in, for the windows whose last byte falls
 // in one stretch of 2^map_lg bytes of a row: the members overlapping the
 // stretch extended one window to the left (so the window's first byte is
-// covered too), in column order, when there are at most two of them.
+// covered too), in column order, when there are at most two of them.  A
+// window starting at or past c[1].lo lies in c[1] if anywhere.  A missing
+// candidate has full = end = 0 (no window passes) and, as c[1], lo = ~0u.
+// The records run past the row's end, to the stretch of the last byte of the
+// grid's last window, so that the record of any window of the grid exists.
 struct PackStretch {
     PackCand c[2];
 };
@@ -418,54 +427,60 @@ FSDPPACK_HD inline bool pack_direct(const WindowArgs &a, int32_t w, DirectWindow
 // whole window inside one member's rank chunk, every element real.  One
 // scalar load of 64 bytes (the stretch record of the window's last byte),
 // then the member's pointer, stand between the launch arguments and the
-// data; the index arithmetic is 32-bit (rows of fewer than 2^31 bytes).  Fills `d`
-// as pack_direct does; the window then equals the single range
-// pack_window_rk produces for it.
+// data, with few scalar instructions around them: the record holds each
+// candidate's bounds in row bytes, so the test is two unsigned compares.
+// The index arithmetic is 32-bit (rows of fewer than 2^31 bytes).  Fills `d`
+// as pack_direct does; the window then equals the single range pack_window_rk
+// produces for it.  Both ends are always aligned for whole 16-byte
+// destination vectors (a window starts k*2048 bytes past the line boundary
+// at or before the row's start) and for element loads of the source (the
+// caller's pointers are aligned to their element size).
 // (The launch's fields the test reads are passed one by one: the kernel takes
 // them as leading scalar arguments, which the hardware can place in scalar
 // registers before the wave starts.)  table: the pointer table; rb: row
-// bytes; lg: log2 of the reduction dtype's size.
+// bytes.
 FSDPPACK_HD inline bool pack_direct_stretch_s(const PackStretch *stretches, const uint64_t *table, uint32_t rb,
-                                              uint32_t shift, uint32_t map_lg, uint32_t lg, int32_t reduce_dt,
-                                              int32_t r, int32_t k, DirectWindow &d)
+                                              uint32_t shift, uint32_t map_lg, int32_t r, int32_t k, DirectWindow &d)
 {
-    const uint32_t s_r = (shift + static_cast<uint32_t>(r) * rb) & (kLineBytes - 1);
-    const uint32_t kb = static_cast<uint32_t>(k) << kWindowLog2;
-    if (kb < s_r) return false;                                         // the row's first, partial window
-    const uint32_t y0 = kb - s_r, y1 = y0 + kWindowBytes;
-    if (y1 > rb) return false;                                          // the row's last, partial window
-    const uint32_t c0 = y0 >> lg, c1 = y1 >> lg;
-#if defined(__HIP_DEVICE_COMPILE__)
-    typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
-    const u32x16 v = ((const FSDPPACK_TABLE u32x16 *)stretches)[(y1 - 1) >> map_lg];
-    PackStretch e;
-    __builtin_memcpy(&e, &v, sizeof e);
-#else
-    const PackStretch e = stretches[(y1 - 1) >> map_lg];
-#endif
-    const PackCand &c = (e.c[1].dt != 0 && c0 >= e.c[1].O) ? e.c[1] : e.c[0];
-    if (c.dt == 0 || c0 < c.O || c1 > c.OP) return false;
+    constexpr uint32_t kWin = static_cast<uint32_t>(kWindowBytes);
     const uint32_t ur = static_cast<uint32_t>(r);
-    if (ur > c.full || (ur == c.full && c1 > c.OT)) return false;       // padding in the window
-    const uint32_t ssz = c.dt == kBF16 ? 2u : 4u;
+    const uint32_t s_r = (shift + ur * rb) & static_cast<uint32_t>(kLineBytes - 1);
+    // the row's first window wraps y0 below 0 (mod 2^32) when the row starts
+    // off a line; y0 + kWin - 1 wraps back, so its record is still in range,
+    // and it fails the range test
+    const uint32_t y0 = (static_cast<uint32_t>(k) << kWindowLog2) - s_r, y1 = y0 + kWin;
+    const uint32_t rec = ((y0 + (kWin - 1u)) >> map_lg) * static_cast<uint32_t>(sizeof(PackStretch));
 #if defined(__HIP_DEVICE_COMPILE__)
-    const uint64_t ptr = ((const FSDPPACK_TABLE uint64_t *)table)[c.m];
+    // the second candidate's first byte decides which of the two 32-byte
+    // candidates to load, so that no field needs a select
+    const FSDPPACK_TABLE char *R = (const FSDPPACK_TABLE char *)stretches;
+    const uint32_t split = *(const FSDPPACK_TABLE uint32_t *)(R + rec + sizeof(PackCand));
+    typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+    const u32x8 v = *(const FSDPPACK_TABLE u32x8 *)(R + (rec | (y0 >= split ? static_cast<uint32_t>(sizeof(PackCand)) : 0u)));
+    const uint32_t lo = v[0], span = v[1], end = v[2], full = v[3], Pss = v[4], moff = v[5], sh = v[6], code = v[7];
+    const uint64_t ptr = *(const FSDPPACK_TABLE uint64_t *)((const FSDPPACK_TABLE char *)table + moff);
 #else
-    const uint64_t ptr = table ? table[c.m] : 0;
+    const PackStretch &e = *reinterpret_cast<const PackStretch *>(reinterpret_cast<const char *>(stretches) + rec);
+    const PackCand &c = y0 >= e.c[1].lo ? e.c[1] : e.c[0];
+    const uint32_t lo = c.lo, span = c.span, end = c.end, full = c.full, Pss = c.Pss, sh = c.sh, code = c.code;
+    const uint64_t ptr = table ? table[c.moff / 8] : 0;
 #endif
-    d.src = ptr + static_cast<uint64_t>(ur) * c.Pss + static_cast<uint64_t>((c0 - c.O) * ssz);
+    // inside the member's columns, and no padding: r < full, or r == full
+    // and y1 <= end, which is r < full + (y1 <= end) (full < 2^31)
+    const uint32_t t = y0 - lo;
+    if (!((t <= span) & (ur < full + (y1 <= end ? 1u : 0u)))) return false;
+    d.src = ptr + static_cast<uint64_t>(ur) * Pss + ((t << 1) >> sh);
     d.dst_off = static_cast<int64_t>(static_cast<uint64_t>(ur) * rb + y0);
-    d.src_dt = static_cast<int32_t>(c.dt);
-    d.dst_dt = reduce_dt;
-    // a bf16 source may start 2 bytes past a dword (the kernel then shifts)
-    return (d.src & (ssz - 1)) == 0 && ((shift + d.dst_off) & 15) == 0;
+    d.src_dt = static_cast<int32_t>(code >> 2);
+    d.dst_dt = static_cast<int32_t>(code & 3u);
+    return true;
 }
 
 FSDPPACK_HD inline bool pack_direct_stretch(const WindowArgs &a, int32_t r, int32_t k, DirectWindow &d)
 {
     const uint32_t lg = a.reduce_dt == kBF16 ? 1u : 2u;
     return pack_direct_stretch_s(a.stretches, a.table, static_cast<uint32_t>(a.S) << lg, static_cast<uint32_t>(a.shift),
-                                 static_cast<uint32_t>(a.map_lg), lg, a.reduce_dt, r, k, d);
+                                 static_cast<uint32_t>(a.map_lg), r, k, d);
 }
 
 // The record of the window-indexed table `T` (records sorted by win0)

@@ -530,19 +530,18 @@ __device__ __forceinline__ void use_inline_table(WindowArgs &a, const PtrTab<N> 
 }
 
 // The direct test's inputs come first, as scalar arguments (st: the stretch
-// records; rb: row bytes; meta: reduction dtype | log2 of its size << 8 |
-// group_lg << 16), so that they can be preloaded into scalar registers.
+// records; rb: row bytes; glg: group_lg, log2 of the rows per row group), so
+// that they can be preloaded into scalar registers.
 template <int N>
 __global__ void __launch_bounds__(kPackBlock) pack_kernel(const PackStretch *st, uint32_t rb, uint32_t shift,
-                                                          uint32_t map_lg, uint32_t meta, WindowArgs a, PtrTab<N> t)
+                                                          uint32_t map_lg, uint32_t glg, WindowArgs a, PtrTab<N> t)
 {
     use_inline_table(a, t);
-    const uint32_t glg = meta >> 16, lg = (meta >> 8) & 0xFFu;
     const int32_t k = static_cast<int32_t>(blockIdx.x >> glg);
-    const int32_t r = static_cast<int32_t>((blockIdx.y << glg) + (blockIdx.x & ((1u << glg) - 1)));
+    const int32_t r = static_cast<int32_t>((blockIdx.y << glg) | (blockIdx.x & ((1u << glg) - 1)));
     DirectWindow d;
     if (st != nullptr) {
-        if (pack_direct_stretch_s(st, a.table, rb, shift, map_lg, lg, static_cast<int32_t>(meta & 0xFFu), r, k, d)) {
+        if (pack_direct_stretch_s(st, a.table, rb, shift, map_lg, r, k, d)) {
             run_direct<false, kPackBlock, kPackUnroll>(d, a.base);
             return;
         }
@@ -652,9 +651,9 @@ int launch_sized(const WindowArgs &args, const uint64_t *inline_ptrs, int32_t n,
                          static_cast<uint32_t>(args.W >> args.group_lg));
         const uint32_t lg = args.reduce_dt == kBF16 ? 1u : 2u;
         const uint32_t rb = args.stretches ? static_cast<uint32_t>(args.S) << lg : 0u;
-        const uint32_t meta = static_cast<uint32_t>(args.reduce_dt) | (lg << 8) | (static_cast<uint32_t>(args.group_lg) << 16);
         hipExtLaunchKernelGGL(pack_kernel<N>, grid2, dim3(kPackBlock), 0, st, e0, e1, 0, args.stretches, rb,
-                              static_cast<uint32_t>(args.shift), static_cast<uint32_t>(args.map_lg), meta, args, t);
+                              static_cast<uint32_t>(args.shift), static_cast<uint32_t>(args.map_lg),
+                              static_cast<uint32_t>(args.group_lg), args, t);
     } else if (args.op == kOpCopyIn) {
         hipExtLaunchKernelGGL(copy_in_kernel<N>, grid, block, 0, st, e0, e1, 0,
                               static_cast<const ColumnWindow *>(args.columns), static_cast<const CopyInSeg *>(args.members),

@@ -282,8 +282,7 @@ int build_plan(const fsdppack_param_desc *params, int32_t n, int32_t world, fsdp
         });
         op.narrow = pack_narrow(op, mem);
         if (op.narrow) {
-            op.stretches.resize(op.columns.size());
-            build_pack_stretches(op, op.stretches.data());
+            build_pack_stretches(op);
         }
     }
 
@@ -424,12 +423,18 @@ void build_scratch_images(fsdppack_plan *plan)
     }
 }
 
-void build_pack_stretches(const OpTable &op, PackStretch *out)
+void build_pack_stretches(OpTable &op)
 {
     const PackMember *M = reinterpret_cast<const PackMember *>(op.members.data());
     const int lg = op.reduce_dt == kBF16 ? 1 : 2;
     const int64_t rb = op.S << lg, E = int64_t{1} << op.map_lg;
     const int64_t nx = static_cast<int64_t>(op.columns.size());
+    // the grid's windows k = 0 .. gx of a row start at most at byte k*2048:
+    // records up to the stretch of the last byte of window gx
+    const int64_t n_rec = ((op.gx * kWindowBytes + kWindowBytes - 1) >> op.map_lg) + 1;
+    PackStretch none{};                                    // full = end = 0: no window passes
+    none.c[1].lo = ~0u;
+    op.stretches.assign(static_cast<size_t>(std::max(n_rec, nx)), none);
     int32_t first = 0;
     for (int64_t x = 0; x < nx; ++x) {
         // the columns of row bytes [x*E - window, (x+1)*E), clipped to the row:
@@ -439,22 +444,23 @@ void build_pack_stretches(const OpTable &op, PackStretch *out)
         while (first < op.n && M[first].O + M[first].P <= c0) ++first;
         int32_t last = first;
         while (last < op.n && M[last].O < c1) ++last;
-        PackStretch s{};                                   // dt 0: no candidate
-        if (last - first >= 1 && last - first <= 2) {
-            for (int32_t i = first; i < last; ++i) {
-                const PackMember &m = M[i];
-                const int64_t ssz = dtype_bytes(m.src_dt), full = m.numel / m.P;
-                PackCand &c = s.c[i - first];
-                c.m = static_cast<uint32_t>(i);
-                c.Pss = static_cast<uint32_t>(m.P * ssz);
-                c.O = static_cast<uint32_t>(m.O);
-                c.OP = static_cast<uint32_t>(m.O + m.P);
+        if (last - first < 1 || last - first > 2) continue;
+        PackStretch &s = op.stretches[static_cast<size_t>(x)];
+        for (int32_t i = first; i < last; ++i) {
+            const PackMember &m = M[i];
+            const int64_t ssz = dtype_bytes(m.src_dt), full = m.numel / m.P, Pb = m.P << lg;
+            PackCand &c = s.c[i - first];
+            c.lo = static_cast<uint32_t>(m.O << lg);
+            if (Pb >= kWindowBytes) {
+                c.span = static_cast<uint32_t>(Pb - kWindowBytes);
                 c.full = static_cast<uint32_t>(full);
-                c.OT = static_cast<uint32_t>(m.O + m.numel - full * m.P);
-                c.dt = static_cast<uint32_t>(m.src_dt);
-            }
+                c.end = static_cast<uint32_t>((m.O + m.numel - full * m.P) << lg);
+            }                                              // else full = end = 0: no whole window fits
+            c.Pss = static_cast<uint32_t>(m.P * ssz);
+            c.moff = static_cast<uint32_t>(i) * 8u;
+            c.sh = static_cast<uint32_t>(1 + lg - (ssz == 2 ? 1 : 2));
+            c.code = static_cast<uint32_t>(m.src_dt * 4 + op.reduce_dt);
         }
-        out[x] = s;
     }
 }
 
@@ -552,8 +558,7 @@ int build_plan_flat(const fsdppack_param_desc *params, int32_t n, int32_t world,
         });
         op.narrow = pack_narrow(op, mem);
         if (op.narrow) {
-            op.stretches.resize(op.columns.size());
-            build_pack_stretches(op, op.stretches.data());
+            build_pack_stretches(op);
         }
     }
 

@@ -142,11 +142,21 @@ static bool check_op(const char *name, const OpTable &op, int32_t W, int32_t shi
         const PackMember *M = reinterpret_cast<const PackMember *>(op.members.data());
         for (int32_t m = 0; m < op.n; ++m)
             ptrs[m] = (static_cast<uint64_t>(m + 1) << 32) + ((m & 1) ? dtype_bytes(M[m].src_dt) : 0);
-        CHECK(op.stretches.size() == (op.narrow ? op.columns.size() : 0) && (a.stretches != nullptr) == op.narrow,
+        // every window of the grid (k = 0 .. gx) finds its record
+        const size_t n_rec = op.narrow ? static_cast<size_t>(((op.gx + 1) * kWindowBytes - 1) >> op.map_lg) + 1 : 0;
+        CHECK(op.stretches.size() >= n_rec && op.stretches.size() >= (op.narrow ? op.columns.size() : 0) &&
+                  (!op.narrow || op.stretches.size() <= std::max(n_rec, op.columns.size())) &&
+                  (a.stretches != nullptr) == op.narrow,
               "%s: stretch records", name);
+        const int64_t rb = op.S * dtype_bytes(op.reduce_dt);
         for (const PackStretch &e : op.stretches)
-            for (const PackCand &c : e.c)
-                CHECK(c.dt == 0 || (c.m < static_cast<uint32_t>(op.n) && c.O < c.OP), "%s: stretch record", name);
+            for (int i = 0; i < 2; ++i) {
+                const PackCand &c = e.c[i];
+                const bool none = c.full == 0 && c.end == 0;
+                CHECK(none || (c.moff % 8 == 0 && c.moff / 8 < static_cast<uint32_t>(op.n) &&
+                               int64_t{c.lo} + c.span + kWindowBytes <= rb && c.sh <= 2 && (c.code & 3u) == static_cast<uint32_t>(op.reduce_dt)),
+                      "%s: stretch record", name);
+            }
     }
     for (int32_t w = 0; w < a.n_windows; ++w) {
         int ranges = 0;
