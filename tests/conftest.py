@@ -40,6 +40,17 @@ def direct_window_layout():
     return shapes, gdt, rdt, 4
 
 
+def single_pair_layouts():
+    """The shapes of direct_window_layout with every gradient in one dtype and
+    every reduction in one dtype, once per (gradient, reduction) dtype pair:
+    each is one bucket whose direct windows all have that pair.  Returns a
+    list of (shapes, grad dtypes, reduce dtypes, W, pair)."""
+    BF16, FP32 = 1, 2
+    shapes, _, _, W = direct_window_layout()
+    return [(shapes, [g] * len(shapes), [r] * len(shapes), W, g * 4 + r)
+            for g, r in ((BF16, FP32), (FP32, FP32), (FP32, BF16), (BF16, BF16))]
+
+
 def gathered_copy_out_layout():
     """Layouts whose copy-out windows span many small rank chunks (the
     kernel's element-by-element gather): parameters with fewer rows than

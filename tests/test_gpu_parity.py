@@ -133,6 +133,20 @@ def test_pack_direct_windows_every_dtype_pair_and_shift():
         check_pack(w, grads, [src_shift] * len(grads), out_off)
 
 
+def test_pack_direct_windows_single_pair_buckets():
+    """One bucket per dtype pair, every gradient of one dtype: the direct
+    copy of each pair on its own, with bf16 chunks at odd elements, shifted
+    sources and outputs off a 16-byte boundary."""
+    from conftest import single_pair_layouts
+    for shapes, gdt, rdt, W, pair in single_pair_layouts():
+        w = wl.custom(shapes, gdt, rdt, W, seed=13)
+        grads = wl.make_grads(w)
+        wl.inject_specials(grads, gdt, seed=13)
+        for src_shift, out_off in ((0, 0), (1, 0), (0, 6), (1, 2)):
+            print(f"[pack pair] pair={pair} src_shift={src_shift} out_off={out_off}", flush=True)
+            check_pack(w, grads, [src_shift] * len(grads), out_off)
+
+
 def _random_workload(rng, seed):
     W = rng.choice([1, 2, 3, 4, 5, 8, 16, 33, 128])
     n = rng.randint(1, 9)
