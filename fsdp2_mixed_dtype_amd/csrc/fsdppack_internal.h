@@ -168,7 +168,7 @@ static_assert(sizeof(FlatMember) == 32, "shared with the device");
 //       table[m] + r*Pss + (((y - lo) << 1) >> sh)
 struct PackCand {
     uint32_t lo;             // O*dsz, the member's first row byte
-    uint32_t span;           // P*dsz - window bytes (0 with full = end = 0 when no window fits)
+    uint32_t span;           // P*dsz - window bytes (listed members hold at least one window)
     uint32_t end;            // row `full`'s first byte past its real columns: (O + numel - full*P)*dsz
     uint32_t full;           // ranks whose chunk is all real: numel / P
     uint32_t Pss;            // P*size(src): source bytes between consecutive rank chunks
@@ -179,9 +179,10 @@ struct PackCand {
 static_assert(sizeof(PackCand) == 32, "shared with the device");
 
 // The members a pack window may lie in, for the windows whose last byte falls
-// in one stretch of 2^map_lg bytes of a row: the members overlapping the
-// stretch extended one window to the left (so the window's first byte is
-// covered too), in column order, when there are at most two of them.  A
+// in one stretch of 2^map_lg bytes of a row: the members of at least one
+// window's length overlapping the stretch extended one window to the left
+// (so the window's first byte is covered too), in column order, when there
+// are at most two of them.  A
 // window starting at or past c[1].lo lies in c[1] if anywhere.  A missing
 // candidate has full = end = 0 (no window passes) and, as c[1], lo = ~0u.
 // The records run past the row's end, to the stretch of the last byte of the

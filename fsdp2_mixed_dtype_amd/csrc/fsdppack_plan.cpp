@@ -435,27 +435,35 @@ void build_pack_stretches(OpTable &op)
     PackStretch none{};                                    // full = end = 0: no window passes
     none.c[1].lo = ~0u;
     op.stretches.assign(static_cast<size_t>(std::max(n_rec, nx)), none);
+    // Members whose rank chunk is shorter than a window can hold no direct
+    // window, so they take no candidate place: a stretch of large chunks with
+    // a few norms or biases between them still lists its large members
+    // (a window that touches a small member lies in no large one's columns
+    // and fails the range test).
+    std::vector<int32_t> big;
+    for (int32_t i = 0; i < op.n; ++i)
+        if ((M[i].P << lg) >= kWindowBytes) big.push_back(i);
+    const int32_t nbig = static_cast<int32_t>(big.size());
     int32_t first = 0;
     for (int64_t x = 0; x < nx; ++x) {
         // the columns of row bytes [x*E - window, (x+1)*E), clipped to the row:
         // every window whose last byte lies in stretch x starts in there
         const int64_t b0 = std::max<int64_t>(0, x * E - kWindowBytes), b1 = std::min(rb, (x + 1) * E);
         const int64_t c0 = b0 >> lg, c1 = (b1 + (int64_t{1} << lg) - 1) >> lg;
-        while (first < op.n && M[first].O + M[first].P <= c0) ++first;
+        while (first < nbig && M[big[first]].O + M[big[first]].P <= c0) ++first;
         int32_t last = first;
-        while (last < op.n && M[last].O < c1) ++last;
+        while (last < nbig && M[big[last]].O < c1) ++last;
         if (last - first < 1 || last - first > 2) continue;
         PackStretch &s = op.stretches[static_cast<size_t>(x)];
-        for (int32_t i = first; i < last; ++i) {
+        for (int32_t j = first; j < last; ++j) {
+            const int32_t i = big[j];
             const PackMember &m = M[i];
             const int64_t ssz = dtype_bytes(m.src_dt), full = m.numel / m.P, Pb = m.P << lg;
-            PackCand &c = s.c[i - first];
+            PackCand &c = s.c[j - first];
             c.lo = static_cast<uint32_t>(m.O << lg);
-            if (Pb >= kWindowBytes) {
-                c.span = static_cast<uint32_t>(Pb - kWindowBytes);
-                c.full = static_cast<uint32_t>(full);
-                c.end = static_cast<uint32_t>((m.O + m.numel - full * m.P) << lg);
-            }                                              // else full = end = 0: no whole window fits
+            c.span = static_cast<uint32_t>(Pb - kWindowBytes);
+            c.full = static_cast<uint32_t>(full);
+            c.end = static_cast<uint32_t>((m.O + m.numel - full * m.P) << lg);
             c.Pss = static_cast<uint32_t>(m.P * ssz);
             c.moff = static_cast<uint32_t>(i) * 8u;
             c.sh = static_cast<uint32_t>(1 + lg - (ssz == 2 ? 1 : 2));

@@ -196,8 +196,9 @@ int64_t shard_elements(const fsdppack_plan &plan, int32_t t, int32_t r);
 void build_scratch_images(fsdppack_plan *plan);
 
 // The stretch records of a narrow pack table (op.stretches): for each
-// column-map stretch, the members overlapping its bytes extended one window
-// to the left, when there are one or two of them (else none); then records
+// column-map stretch, the members of at least one window's length
+// overlapping its bytes extended one window to the left, when there are one
+// or two of them (else none); then records
 // with no candidate up to the stretch of the last byte of the grid's last
 // window of a row.
 void build_pack_stretches(OpTable &op);
