@@ -425,10 +425,11 @@ FSDPPACK_HD inline bool pack_direct(const WindowArgs &a, int32_t w, DirectWindow
 
 // Whether window k of row r is a direct window according to the stretch
 // records (a.stretches, built with the plan by build_pack_stretches): one
-// whole window inside one member's rank chunk, every element real.  One
-// scalar load of 64 bytes (the stretch record of the window's last byte),
-// then the member's pointer, stand between the launch arguments and the
-// data, with few scalar instructions around them: the record holds each
+// whole window inside one member's rank chunk, every element real.  Three
+// short scalar loads (the second candidate's first byte in the stretch
+// record of the window's last byte, then the one candidate the window can
+// lie in, then the member's pointer) stand between the launch arguments and
+// the data, with few scalar instructions around them: the record holds each
 // candidate's bounds in row bytes, so the test is two unsigned compares.
 // The index arithmetic is 32-bit (rows of fewer than 2^31 bytes).  Fills `d`
 // as pack_direct does; the window then equals the single range pack_window_rk
