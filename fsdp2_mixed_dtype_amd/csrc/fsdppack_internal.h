@@ -182,11 +182,11 @@ static_assert(sizeof(PackCand) == 32, "shared with the device");
 // in one stretch of 2^map_lg bytes of a row: the members of at least one
 // window's length overlapping the stretch extended one window to the left
 // (so the window's first byte is covered too), in column order, when there
-// are at most two of them.  A
-// window starting at or past c[1].lo lies in c[1] if anywhere.  A missing
-// candidate has full = end = 0 (no window passes) and, as c[1], lo = ~0u.
-// The records run past the row's end, to the stretch of the last byte of the
-// grid's last window, so that the record of any window of the grid exists.
+// are at most two of them.  A window starting at or past c[1].lo lies in
+// c[1] if anywhere.  A missing candidate has full = end = 0 (no window
+// passes) and, as c[1], lo = ~0u.  The records run past the row's end, to
+// the stretch of the last byte of the grid's last window, so that the record
+// of any window of the grid exists.
 struct PackStretch {
     PackCand c[2];
 };
