@@ -140,6 +140,12 @@ class Plan:
         self.P = tuple(P[i] for i in range(self.n))
         self.A = tuple(A[i] for i in range(self.n))
         self.numel = tuple(d.dim0 * d.inner for d in self.descs)
+        self.grad_dtypes = tuple(d.grad_dtype for d in self.descs)
+        self.storage_dtypes = tuple(d.storage_dtype for d in self.descs)
+        self.param_dtypes = tuple(d.param_dtype for d in self.descs)
+        # per bucket: its members, their gradient dtypes and element counts
+        self.member_specs = tuple((tuple(b.members), tuple(self.grad_dtypes[i] for i in b.members),
+                                   tuple(self.numel[i] for i in b.members)) for b in self.buckets)
         # flat layout: c per rank, parameter t at flat offset O_t of the one bucket
         self.c = self.buckets[0].S if flat and self.buckets else 0
 
@@ -213,6 +219,38 @@ def _ptr(t, dtype: int | None, numel: int | None, what: str):
     return t.data_ptr()
 
 
+def _ptrs(tensors, dtypes, numels, what: str, index=None):
+    """_ptr over a list (dtype codes and element counts by position; `index`:
+    the positions' indices for error messages, default 0, 1, ...): a plain
+    tensor that passes every check costs one condition; anything else (a
+    subclass, a wrong property) goes through _ptr, which accepts it or raises
+    the same error it would raise on its own."""
+    out = []
+    app = out.append
+    Tensor = torch.Tensor
+    for i, (t, dt, n) in enumerate(zip(tensors, dtypes, numels)):
+        if t is None:
+            app(0)
+        elif (type(t) is Tensor and t.is_cuda and t.dtype is TORCH_DTYPE[dt] and t.is_contiguous()
+              and t.numel() == n):
+            app(t.data_ptr())
+        else:
+            app(_ptr(t, dt, n, f"{what}[{i if index is None else index[i]}]"))
+    return out
+
+
+def _member_grads(plan, bucket: int, grads):
+    """The pointer array of a gradient list for one bucket's pack: its
+    members' pointers, validated, and 0 for every other parameter."""
+    if len(grads) != plan.n:
+        raise ValueError(f"grads: expected {plan.n} entries, got {len(grads)}")
+    mem, dts, ns = plan.member_specs[bucket]
+    ptrs = [0] * max(1, plan.n)
+    for i, p in zip(mem, _ptrs([grads[i] for i in mem], dts, ns, "grads", mem)):
+        ptrs[i] = p
+    return (ctypes.c_void_p * len(ptrs))(*ptrs)
+
+
 def _ptr_array(ptrs):
     return (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
 
@@ -234,7 +272,7 @@ def prepare_grads(plan: Plan, grads) -> PointerArray:
     for parameters that are never packed."""
     if len(grads) != plan.n:
         raise ValueError(f"grads: expected {plan.n} entries, got {len(grads)}")
-    ptrs = [_ptr(g, plan.descs[i].grad_dtype, plan.numel[i], f"grads[{i}]") for i, g in enumerate(grads)]
+    ptrs = _ptrs(grads, plan.grad_dtypes, plan.numel, "grads")
     return PointerArray(plan, "grads", grads, ptrs)
 
 
@@ -250,7 +288,7 @@ def prepare_shards(plan: Plan, shards, rank: int | None = None) -> PointerArray:
         ptrs = [_ptr(s, plan.descs[i].storage_dtype, valid_in_chunk(plan, i, rank), f"shards[{i}]")
                 if valid_in_chunk(plan, i, rank) else 0 for i, s in enumerate(shards)]
     else:
-        ptrs = [_ptr(s, plan.descs[i].storage_dtype, plan.P[i], f"shards[{i}]") for i, s in enumerate(shards)]
+        ptrs = _ptrs(shards, plan.storage_dtypes, plan.P, "shards")
     arr = PointerArray(plan, "shards", shards, ptrs)
     arr.rank = rank if plan.flat else None
     return arr
@@ -260,7 +298,7 @@ def prepare_params(plan: Plan, params) -> PointerArray:
     """Full parameters by index (param dtype, numel elements)."""
     if len(params) != plan.n:
         raise ValueError(f"params: expected {plan.n} entries, got {len(params)}")
-    ptrs = [_ptr(p, plan.descs[i].param_dtype, plan.numel[i], f"params[{i}]") for i, p in enumerate(params)]
+    ptrs = _ptrs(params, plan.param_dtypes, plan.numel, "params")
     return PointerArray(plan, "params", params, ptrs)
 
 
@@ -280,11 +318,7 @@ def pack_reduce_scatter_input(plan: Plan, bucket: int, grads, out, stream=None):
     if isinstance(grads, PointerArray):
         arr = _prepared(plan, grads, "grads", prepare_grads)
     else:
-        members = set(b.members)
-        if len(grads) != plan.n:
-            raise ValueError(f"grads: expected {plan.n} entries, got {len(grads)}")
-        arr = _ptr_array([_ptr(g, plan.descs[i].grad_dtype, plan.numel[i], f"grads[{i}]") if i in members else 0
-                          for i, g in enumerate(grads)])
+        arr = _member_grads(plan, bucket, grads)
     optr = _ptr(out, b.dtype, plan.world * b.S, "out")
     _check(lib().fsdppack_pack_reduce_scatter_input(plan.handle, bucket, arr, optr, _stream(stream)))
     return out
@@ -298,11 +332,7 @@ def pack_reduce_scatter_input_noalloc(plan: Plan, bucket: int, grads, out, strea
     if isinstance(grads, PointerArray):
         arr = _prepared(plan, grads, "grads", prepare_grads)
     else:
-        members = set(b.members)
-        if len(grads) != plan.n:
-            raise ValueError(f"grads: expected {plan.n} entries, got {len(grads)}")
-        arr = _ptr_array([_ptr(g, plan.descs[i].grad_dtype, plan.numel[i], f"grads[{i}]") if i in members else 0
-                          for i, g in enumerate(grads)])
+        arr = _member_grads(plan, bucket, grads)
     optr = _ptr(out, b.dtype, plan.world * b.S, "out")
     _check(lib().fsdppack_pack_reduce_scatter_input_noalloc(plan.handle, bucket, arr, optr, _stream(stream)))
     return out
