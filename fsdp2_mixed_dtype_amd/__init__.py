@@ -146,6 +146,7 @@ class Plan:
         # per bucket: its members, their gradient dtypes and element counts
         self.member_specs = tuple((tuple(b.members), tuple(self.grad_dtypes[i] for i in b.members),
                                    tuple(self.numel[i] for i in b.members)) for b in self.buckets)
+        self.shard_grad_specs = {}   # (bucket or None, rank) -> the write-back's members on that rank
         # flat layout: c per rank, parameter t at flat offset O_t of the one bucket
         self.c = self.buckets[0].S if flat and self.buckets else 0
 
@@ -388,17 +389,20 @@ def prepare_shard_grads(plan: Plan, bucket: int | None, rank: int, grads) -> Poi
     None."""
     if len(grads) != plan.n:
         raise ValueError(f"shard_grads: expected {plan.n} entries, got {len(grads)}")
-    if bucket is None:
-        members = {i for b in plan.buckets for i in b.members}
-    else:
-        members = set(plan.buckets[bucket].members)
-    ptrs = []
-    for i, g in enumerate(grads):
-        v = valid_in_chunk(plan, i, rank)
-        if i in members and v:
-            ptrs.append(_ptr(g, plan.descs[i].storage_dtype, v, f"shard_grads[{i}]"))
-        else:
-            ptrs.append(0)
+    key = (bucket, rank)
+    spec = plan.shard_grad_specs.get(key)
+    if spec is None:
+        # the members with real elements on this rank, their storage dtypes
+        # and element counts (the layout is fixed, so once per bucket and rank)
+        members = sorted({i for b in plan.buckets for i in b.members} if bucket is None
+                         else plan.buckets[bucket].members)
+        mem = tuple(i for i in members if valid_in_chunk(plan, i, rank))
+        spec = (mem, tuple(plan.storage_dtypes[i] for i in mem), tuple(valid_in_chunk(plan, i, rank) for i in mem))
+        plan.shard_grad_specs[key] = spec
+    mem, dts, ns = spec
+    ptrs = [0] * plan.n
+    for i, p in zip(mem, _ptrs([grads[i] for i in mem], dts, ns, "shard_grads", mem)):
+        ptrs[i] = p
     arr = PointerArray(plan, "shard_grads", grads, ptrs)
     arr.bucket, arr.rank = bucket, rank
     return arr
