@@ -628,6 +628,16 @@ def main():
         torch.cuda.synchronize()
         churn_wall = (time.perf_counter() - t_ch) * 1e3 / K
         cnt1 = fp.counters()
+        # the same packs with tensor lists, validated on every call: the host
+        # time per step of a caller whose gradients are new tensors each step
+        host_lists = []
+        for i in range(K):
+            gl = churn[(i + 2 * n_churn) % n_churn].tensors
+            h0 = time.perf_counter()
+            for bi in range(nb):
+                fp.pack_reduce_scatter_input(plan, bi, gl, outs0[bi], stream)
+            host_lists.append(time.perf_counter() - h0)
+        torch.cuda.synchronize()
         churn_pack = sum(a.elapsed_time(b) for e in e_ch for a, b in e) / K
         # the same loop without kernel-stamped events (whose dispatch adds a
         # few microseconds per launch): the wall time per pack a caller sees
@@ -663,6 +673,7 @@ def main():
             "wall_ms_per_pack": round(churn_plain, 5),
             "wall_ms_per_pack_stamped": round(churn_wall, 5),
             "host_us_per_call_p50": round(median(host) * 1e6, 1),
+            "host_us_per_step_tensor_lists_p50": round(median(host_lists) * 1e6, 1),
             "inline_pointer_launches": cnt1[6] - cnt0[6],
             "table_uploads": cnt1[1] - cnt0[1], "table_replacements": cnt1[4] - cnt0[4],
             "cross_stream_waits": cnt1[5] - cnt0[5],
